@@ -1,0 +1,261 @@
+"""CPU oracle for the fused MoE expert forward -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP library never loads it, and it
+never loads the HIP library. The arithmetic lives in ``moe_oracle.c`` (plain
+per-token loops, fp64 accumulation, bf16 rounding at h, z, o and y); this file
+only marshals numpy arrays.
+
+Functions with no independent pin would say "parity unpinned" here; every
+function below is pinned by the CPU tests (``tests/test_oracle_*.py``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_SO = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-o", _SO + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_SO + ".tmp", _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        sig = {
+            "oracle_bf16_to_f64_n": [_P, _I64, _P],
+            "oracle_f64_to_bf16_n": [_P, _I64, _P],
+            "oracle_e4m3_to_f64_n": [_P, _I64, _P],
+            "oracle_f32_to_e4m3_n": [_P, _I64, _P],
+            "oracle_quant_groups_fp8": [_P, _I64, _P, _P],
+            "oracle_topk": [_P, _I64, _I32, _I32, _I32, _P, _P],
+            "oracle_align_capacity": [_I64, _I32, _I32, _I32],
+            "oracle_align": [_P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P],
+            "oracle_gemm1_bf16": [_P, _P, _I32, _I32, _P],
+            "oracle_act_bf16": [_P, _I32, ctypes.c_double, _P],
+            "oracle_gemm2_bf16": [_P, _P, _I32, _I32, _P],
+            "oracle_gemm_fp8": [_P, _P, _P, _P, _I32, _I32, _P],
+            "oracle_act_fp8": [_P, _I32, ctypes.c_double, _P, _P],
+            "oracle_fused_experts_bf16": [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                          _I32, _I64, _I64, _P, _P],
+            "oracle_fused_experts_fp8": [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                         _P, _P, _I32, _I64, _I64, _P, _P],
+            "oracle_dense_experts_bf16": [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                          _P, _P],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+        L.oracle_align_capacity.restype = _I64
+        _lib = L
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------- codecs ---
+
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    b = _c(b, np.uint16)
+    out = np.empty(b.shape, np.float64)
+    lib().oracle_bf16_to_f64_n(_p(b), b.size, _p(out))
+    return out
+
+
+def f64_to_bf16(v: np.ndarray) -> np.ndarray:
+    v = _c(np.asarray(v, np.float64), np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_f64_to_bf16_n(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_to_f64(c: np.ndarray) -> np.ndarray:
+    c = _c(c, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().oracle_e4m3_to_f64_n(_p(c), c.size, _p(out))
+    return out
+
+
+def f32_to_e4m3(v: np.ndarray) -> np.ndarray:
+    v = _c(np.asarray(v, np.float32), np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_f32_to_e4m3_n(_p(v), v.size, _p(out))
+    return out
+
+
+def quant_groups_fp8(v: np.ndarray):
+    """Per-row, per-128-column dynamic fp8 quantisation of a [rows, n] fp32 array."""
+    v = _c(np.asarray(v, np.float32), np.float32)
+    rows, n = v.shape
+    assert n % 128 == 0
+    q = np.empty((rows, n), np.uint8)
+    s = np.empty((rows, n // 128), np.float32)
+    for r in range(rows):
+        lib().oracle_quant_groups_fp8(_p(v[r]), n, _p(q[r]), _p(s[r]))
+    return q, s
+
+
+# ---------------------------------------------------------------- router ---
+
+def topk(logits: np.ndarray, k: int, renormalize: bool = True):
+    logits = _c(logits, np.float32)
+    M, E = logits.shape
+    ids = np.empty((M, k), np.int32)
+    w = np.empty((M, k), np.float32)
+    rc = lib().oracle_topk(_p(logits), M, E, k, int(renormalize), _p(ids), _p(w))
+    if rc:
+        raise ValueError("oracle_topk: invalid arguments")
+    return ids, w
+
+
+# ----------------------------------------------------------------- align ---
+
+def align_capacity(M: int, k: int, E: int, B: int) -> int:
+    return int(lib().oracle_align_capacity(M, k, E, B))
+
+
+def align(ids: np.ndarray, E: int, B: int, cap: int | None = None):
+    ids = _c(ids, np.int32)
+    M, k = ids.shape
+    if cap is None:
+        cap = align_capacity(M, k, E, B)
+    sorted_ids = np.empty(cap, np.int32)
+    expert_ids = np.empty(cap // B, np.int32)
+    npp = np.zeros(1, np.int32)
+    inv = np.empty((M, k), np.int32)
+    rc = lib().oracle_align(_p(ids), M, k, E, B, cap, _p(sorted_ids), _p(expert_ids), _p(npp),
+                            _p(inv))
+    if rc:
+        raise ValueError(f"oracle_align failed ({rc})")
+    return sorted_ids, expert_ids, int(npp[0]), inv
+
+
+# ------------------------------------------------------------ expert steps ---
+
+def gemm1_bf16(x_row: np.ndarray, w13e: np.ndarray) -> np.ndarray:
+    x_row = _c(x_row, np.uint16)
+    w13e = _c(w13e, np.uint16)
+    N2, H = w13e.shape
+    h = np.empty(N2, np.uint16)
+    lib().oracle_gemm1_bf16(_p(x_row), _p(w13e), H, N2 // 2, _p(h))
+    return h
+
+
+def act_bf16(h: np.ndarray, alpha: float = 1.0) -> np.ndarray:
+    h = _c(h, np.uint16)
+    I = h.size // 2
+    z = np.empty(I, np.uint16)
+    lib().oracle_act_bf16(_p(h), I, float(alpha), _p(z))
+    return z
+
+
+def gemm2_bf16(z: np.ndarray, w2e: np.ndarray) -> np.ndarray:
+    z = _c(z, np.uint16)
+    w2e = _c(w2e, np.uint16)
+    H, I = w2e.shape
+    o = np.empty(H, np.uint16)
+    lib().oracle_gemm2_bf16(_p(z), _p(w2e), H, I, _p(o))
+    return o
+
+
+def gemm_fp8(qa: np.ndarray, sa: np.ndarray, qw: np.ndarray, sw: np.ndarray) -> np.ndarray:
+    qa, sa = _c(qa, np.uint8), _c(sa, np.float32)
+    qw, sw = _c(qw, np.uint8), _c(sw, np.float32)
+    N, K = qw.shape
+    out = np.empty(N, np.uint16)
+    lib().oracle_gemm_fp8(_p(qa), _p(sa), _p(qw), _p(sw), N, K, _p(out))
+    return out
+
+
+def act_fp8(h: np.ndarray, alpha: float = 1.0):
+    h = _c(h, np.uint16)
+    I = h.size // 2
+    zq = np.empty(I, np.uint8)
+    zs = np.empty(I // 128, np.float32)
+    lib().oracle_act_fp8(_p(h), I, float(alpha), _p(zq), _p(zs))
+    return zq, zs
+
+
+# ----------------------------------------------------------------- layer ---
+
+def fused_experts_bf16(x, w13, w2, ids, weights, on_input=False, t0=0, t1=None,
+                       return_acc=False):
+    """y rows [t0, t1) of the layer with bf16 weights (uint16 bit patterns)."""
+    x, w13, w2 = _c(x, np.uint16), _c(w13, np.uint16), _c(w2, np.uint16)
+    ids, weights = _c(ids, np.int32), _c(weights, np.float32)
+    M, H = x.shape
+    E, N2, _ = w13.shape
+    k = ids.shape[1]
+    t1 = M if t1 is None else t1
+    y = np.zeros((M, H), np.uint16)
+    acc = np.zeros((M, H), np.float64) if return_acc else None
+    rc = lib().oracle_fused_experts_bf16(M, H, N2 // 2, E, k, _p(x), _p(w13), _p(w2), _p(ids),
+                                         _p(weights), int(on_input), t0, t1, _p(y),
+                                         _p(acc) if acc is not None else None)
+    if rc:
+        raise ValueError("oracle_fused_experts_bf16: expert id out of range")
+    return (y[t0:t1], acc[t0:t1]) if return_acc else y[t0:t1]
+
+
+def fused_experts_fp8(x, w13q, w13s, w2q, w2s, ids, weights, on_input=False, t0=0, t1=None,
+                      return_acc=False):
+    """y rows [t0, t1) of the layer with e4m3 weights and 128x128 block scales."""
+    x = _c(x, np.uint16)
+    w13q, w2q = _c(w13q, np.uint8), _c(w2q, np.uint8)
+    w13s, w2s = _c(w13s, np.float32), _c(w2s, np.float32)
+    ids, weights = _c(ids, np.int32), _c(weights, np.float32)
+    M, H = x.shape
+    E, N2, _ = w13q.shape
+    k = ids.shape[1]
+    t1 = M if t1 is None else t1
+    y = np.zeros((M, H), np.uint16)
+    acc = np.zeros((M, H), np.float64) if return_acc else None
+    rc = lib().oracle_fused_experts_fp8(M, H, N2 // 2, E, k, _p(x), _p(w13q), _p(w13s),
+                                        _p(w2q), _p(w2s), _p(ids), _p(weights), int(on_input),
+                                        t0, t1, _p(y), _p(acc) if acc is not None else None)
+    if rc:
+        raise ValueError("oracle_fused_experts_fp8: expert id out of range")
+    return (y[t0:t1], acc[t0:t1]) if return_acc else y[t0:t1]
+
+
+def dense_experts_bf16(x, w13, w2, ids, weights, return_acc=False):
+    """Every expert evaluated for every token, weighted 0 outside the top-k."""
+    x, w13, w2 = _c(x, np.uint16), _c(w13, np.uint16), _c(w2, np.uint16)
+    ids, weights = _c(ids, np.int32), _c(weights, np.float32)
+    M, H = x.shape
+    E, N2, _ = w13.shape
+    k = ids.shape[1]
+    y = np.zeros((M, H), np.uint16)
+    acc = np.zeros((M, H), np.float64)
+    lib().oracle_dense_experts_bf16(M, H, N2 // 2, E, k, _p(x), _p(w13), _p(w2), _p(ids),
+                                    _p(weights), _p(y), _p(acc))
+    return (y, acc) if return_acc else y

@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs for the fused MoE expert forward.
+
+This module is shared by the CPU oracle (``oracle/``) and the HIP path
+(``mixture_experts_ffn_block_amd``). It only draws random numbers and stores
+them in the dtypes the path consumes; it computes none of the layer's
+arithmetic (no routing, no GEMM, no activation, no reduction).
+
+The one encoding it performs is the offline 128x128 block quantisation of the
+fp8 weights. On the pages this happens when the checkpoint is loaded, before
+any forward runs ("DeepGEMM FusedMoE on Blackwell", section 2.8(c), weight
+pre-processing). It is done here with torch's own float8_e4m3fn cast, so both
+sides receive the same weight bytes and scales.
+
+Recipe (every tensor is drawn from its own generator, seeded by
+``(seed, tensor id, expert)``, so the values do not depend on how the
+generation is chunked):
+
+* ``x``       [M, H]  ~ N(0, 1) in fp32, rounded to bf16 (round-to-nearest-even).
+* ``logits``  [M, E]  ~ N(0, 1) fp32, plus a per-expert bias ~ N(0, bias_std)
+  when the workload asks for skewed routing.
+* ``w13``     [E, 2I, H] ~ N(0, 1/sqrt(H)) -> bf16; rows [0, I) are the gate
+  projection, rows [I, 2I) the up projection.
+* ``w2``      [E, H, I]  ~ N(0, 1/sqrt(I)) -> bf16.
+* fp8 workloads: ``w13q``/``w2q`` float8_e4m3fn with fp32 scales per 128x128
+  block, ``scale = amax(block) / 448``, ``q = e4m3(w / scale)``.
+
+The second argument of N(.,.) is the standard deviation.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+
+import torch
+
+# Named workloads. Sizes and routing statistics follow the pages' usual model
+# shapes; block_m is the row-block size shared by the align step and the GEMMs.
+WORKLOADS = {
+    "tiny": dict(M=64, H=256, I=512, E=8, topk=2, wdtype="bf16", block_m=16, bias_std=0.0),
+    "mixtral_prefill_m4096": dict(M=4096, H=4096, I=14336, E=8, topk=2, wdtype="bf16",
+                                  block_m=128, bias_std=0.0),
+    "dsv3_skewed_prefill_m8192": dict(M=8192, H=7168, I=2048, E=256, topk=8, wdtype="bf16",
+                                      block_m=128, bias_std=1.5),
+    "decode_m32": dict(M=32, H=2048, I=768, E=128, topk=8, wdtype="bf16", block_m=16,
+                       bias_std=0.0),
+    "fp8_block_m4096": dict(M=4096, H=7168, I=2048, E=256, topk=8, wdtype="fp8",
+                            block_m=128, bias_std=0.0),
+}
+
+_T_X, _T_LOGITS, _T_BIAS, _T_W13, _T_W2 = 1, 2, 3, 4, 5
+
+
+@dataclasses.dataclass
+class Problem:
+    """Sizes and options of one fused MoE call."""
+
+    M: int
+    H: int
+    I: int
+    E: int
+    topk: int
+    wdtype: str = "bf16"          # "bf16" or "fp8" (e4m3 weights + 128x128 fp32 scales)
+    block_m: int = 16
+    bias_std: float = 0.0
+    seed: int = 0
+    apply_router_weight_on_input: bool = False
+
+    @staticmethod
+    def named(name: str, **overrides) -> "Problem":
+        d = dict(WORKLOADS[name])
+        d.update(overrides)
+        return Problem(**d)
+
+
+def _gen(device, seed: int, tensor_id: int, expert: int = 0) -> torch.Generator:
+    # torch's CPU generator keeps only the low 32 bits of a seed, so the tuple
+    # is hashed down to 32 bits rather than packed into a wider integer
+    h = hashlib.blake2b(f"{seed}/{tensor_id}/{expert}".encode(), digest_size=4).digest()
+    g = torch.Generator(device=device)
+    g.manual_seed(int.from_bytes(h, "little"))
+    return g
+
+
+def _randn(shape, device, seed, tensor_id, expert=0, std=1.0) -> torch.Tensor:
+    t = torch.randn(shape, generator=_gen(device, seed, tensor_id, expert),
+                    dtype=torch.float32, device=device)
+    if std != 1.0:
+        t.mul_(std)
+    return t
+
+
+def block_quant_fp8(w: torch.Tensor):
+    """128x128 block quantisation of a bf16 [N, K] matrix (offline weight prep).
+
+    Returns (q float8_e4m3fn [N, K], scale fp32 [N/128, K/128]).
+    """
+    N, K = w.shape
+    assert N % 128 == 0 and K % 128 == 0
+    wf = w.float().view(N // 128, 128, K // 128, 128)
+    amax = wf.abs().amax(dim=(1, 3))                       # [N/128, K/128]
+    scale = amax / 448.0
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    # an all-zero block keeps scale 0 and divides by 1, giving zero codes
+    q = (wf / safe[:, None, :, None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(N, K), scale
+
+
+@dataclasses.dataclass
+class Inputs:
+    x: torch.Tensor                   # [M, H] bf16
+    logits: torch.Tensor              # [M, E] fp32
+    w13: torch.Tensor | None          # [E, 2I, H] bf16 (bf16 workloads)
+    w2: torch.Tensor | None           # [E, H, I] bf16
+    w13q: torch.Tensor | None = None  # [E, 2I, H] float8_e4m3fn (fp8 workloads)
+    w13s: torch.Tensor | None = None  # [E, 2I/128, H/128] fp32
+    w2q: torch.Tensor | None = None   # [E, H, I] float8_e4m3fn
+    w2s: torch.Tensor | None = None   # [E, H/128, I/128] fp32
+
+
+def make_inputs(p: Problem, device="cpu") -> Inputs:
+    """Draw the seeded synthetic inputs of problem ``p`` on ``device``."""
+    M, H, I, E = p.M, p.H, p.I, p.E
+    x = _randn((M, H), device, p.seed, _T_X).to(torch.bfloat16)
+    logits = _randn((M, E), device, p.seed, _T_LOGITS)
+    if p.bias_std:
+        logits += _randn((E,), device, p.seed, _T_BIAS, std=p.bias_std)[None, :]
+    if p.wdtype == "bf16":
+        w13 = torch.empty((E, 2 * I, H), dtype=torch.bfloat16, device=device)
+        w2 = torch.empty((E, H, I), dtype=torch.bfloat16, device=device)
+        for e in range(E):
+            w13[e] = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H))
+            w2[e] = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I))
+        return Inputs(x, logits, w13, w2)
+    if p.wdtype == "fp8":
+        w13q = torch.empty((E, 2 * I, H), dtype=torch.float8_e4m3fn, device=device)
+        w2q = torch.empty((E, H, I), dtype=torch.float8_e4m3fn, device=device)
+        w13s = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
+        w2s = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=device)
+        for e in range(E):
+            m13 = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H)).to(torch.bfloat16)
+            w13q[e], w13s[e] = block_quant_fp8(m13)
+            m2 = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I)).to(torch.bfloat16)
+            w2q[e], w2s[e] = block_quant_fp8(m2)
+        return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s)
+    raise ValueError(f"unknown weight dtype {p.wdtype!r}")
+
