@@ -1,0 +1,156 @@
+/*
+ * moe.h -- C ABI of the gfx950 (MI355X) fused MoE expert forward.
+ *
+ * The layer computes, for every token t with hidden state x_t,
+ *     y_t = sum over the token's top-k experts e of
+ *           alpha_{t,e} * W2_e ( SiLU(G_e x_t) * (U_e x_t) )
+ * where G_e and U_e are rows [0, I) and [I, 2I) of w13[e]
+ * ("fused_moe.py analysis" (FlagDoc), sections 1.1-1.4;
+ *  "DeepGEMM FusedMoE on Blackwell (vLLM)", section 1.1, steps 2-8).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless marked "host".
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
+ *     stream-ordered, never synchronises the host, and reads no device data
+ *     on the host.
+ *   - The library allocates nothing and keeps no global state: scratch space
+ *     comes from the caller's workspace. Calls are thread-safe.
+ *   - Arguments are validated on the host before any launch; a failing check
+ *     returns its status and launches nothing.
+ *   - Tensors are dense, row-major and contiguous. bf16 is stored as its
+ *     16-bit pattern, e4m3 as OCP float8_e4m3fn bytes.
+ */
+#ifndef MOE_GFX950_H
+#define MOE_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_INVALID = 1,     /* null pointer, negative size, topk outside [1, min(E, 32)] */
+    MOE_E_UNSUPPORTED = 2, /* E > 256, H or I not a multiple of 128, unknown block_m or
+                              dtype, fp8 with block_m 16, more than 2^31 routed rows */
+    MOE_E_WORKSPACE = 3,   /* workspace_bytes < moe_workspace_bytes(p) */
+    MOE_E_HIP = 4          /* a kernel launch failed (hipGetLastError) */
+} moe_status_t;
+
+typedef enum {
+    MOE_W_BF16 = 0,              /* bf16 weights, bf16 activations, fp32 accumulate */
+    MOE_W_FP8_E4M3_BLOCK128 = 1  /* e4m3 weights with one fp32 scale per 128x128 block;
+                                    activations quantised per token per 128 columns */
+} moe_wdtype_t;
+
+/* Sizes and options of one fused_experts call. */
+typedef struct {
+    int64_t M;         /* tokens */
+    int32_t H;         /* hidden size (K of GEMM1, N of GEMM2) */
+    int32_t I;         /* intermediate size per expert (w13 has 2I rows) */
+    int32_t E;         /* experts */
+    int32_t topk;      /* experts per token */
+    int32_t block_m;   /* rows per expert block: 16 (bf16 only), 32, 64 or 128 */
+    int32_t wdtype;    /* moe_wdtype_t */
+    int32_t apply_router_weight_on_input; /* 0: weight the expert outputs in the final sum;
+                                             1: weight the SiLU-and-mul output instead */
+} moe_problem_t;
+
+/*
+ * Router: softmax over the E logits of each token, then the top-k experts
+ * ("vLLM modular_kernel.py notes", section 3, fused_topk with
+ *  scoring_func="softmax"; "fused_moe.py analysis", section 1.1).
+ *
+ *   logits        [M, E] fp32
+ *   topk_ids      [M, topk] int32 out: slot j holds the j-th largest logit; equal
+ *                 logits go to the lower expert index
+ *   topk_weights  [M, topk] fp32 out: softmax probability of the chosen expert;
+ *                 when `renormalize` != 0, divided by the sum over the k chosen
+ * Limits: 1 <= E <= 256, 1 <= topk <= min(E, 32). M == 0 launches nothing.
+ */
+moe_status_t moe_topk(const float *logits, int64_t M, int32_t E, int32_t topk,
+                      int32_t renormalize, int32_t *topk_ids, float *topk_weights,
+                      void *stream);
+
+/*
+ * Host-only, pure: the number of rows the expert-sorted layout may need,
+ * roundup(R + min(R, E) * (block_m - 1), block_m) with R = M * topk
+ * ("DeepGEMM FusedMoE on Blackwell", section 2.6.1, the bound used when the
+ * per-expert counts are not known on the host). Returns -1 on bad arguments.
+ */
+int64_t moe_align_capacity(int64_t M, int32_t topk, int32_t E, int32_t block_m);
+
+/*
+ * Align / permute ("fused_moe.py analysis", "moe_align_block_size";
+ * "DeepGEMM FusedMoE on Blackwell", section 2.6.2). Routed item r = t*topk + j.
+ *
+ *   topk_ids               [M, topk] int32, values in [0, E); other values are
+ *                          skipped (not placed, inv_perm = -1)
+ *   sorted_token_ids       [cap] int32 out: items grouped by expert (ascending),
+ *                          ascending r inside a group, each group padded to a
+ *                          multiple of block_m with the sentinel R; the tail
+ *                          [num_tokens_post_padded, cap) also holds R
+ *   expert_ids             [cap / block_m] int32 out: expert of each block, -1
+ *                          for blocks past the padded total
+ *   num_tokens_post_padded [1] int32 out: sum over experts of roundup(n_e, block_m)
+ *   inv_perm               [M, topk] int32 out: the row of sorted_token_ids that
+ *                          holds item r
+ * cap = moe_align_capacity(M, topk, E, block_m). The layout is deterministic.
+ * With M == 0 only num_tokens_post_padded is written (0); the other pointers
+ * may then be NULL.
+ */
+moe_status_t moe_align_block_size(const int32_t *topk_ids, int64_t M, int32_t topk, int32_t E,
+                                  int32_t block_m, int32_t *sorted_token_ids,
+                                  int32_t *expert_ids, int32_t *num_tokens_post_padded,
+                                  int32_t *inv_perm, void *stream);
+
+/*
+ * Dynamic fp8 quantisation of activations, per row and per 128 columns
+ * ("DeepGEMM FusedMoE on Blackwell", section 2.5 / 1.1 step 4;
+ *  "fused_moe.py analysis", "FP8 W8A8").
+ *
+ *   x      [rows, cols] bf16, cols a multiple of 128
+ *   q      [rows, cols] e4m3 out: RNE(clamp(x / scale, -448, 448))
+ *   scale  [rows, cols / 128] fp32 out: amax of the group / 448 (0 for an
+ *          all-zero group, whose codes are then 0)
+ */
+moe_status_t moe_quant_fp8_groups(const void *x, int64_t rows, int32_t cols, void *q,
+                                  float *scale, void *stream);
+
+/* Host-only, pure: bytes of device workspace fused_experts needs for `p`
+ * (0 when M == 0). */
+size_t moe_workspace_bytes(const moe_problem_t *p);
+
+/*
+ * The fused expert forward: align, GEMM1 (gathered token rows x w13[e]),
+ * SiLU-and-mul, GEMM2 (x w2[e]), then the top-k weighted sum in fp32, cast
+ * to bf16 ("fused_moe.py analysis", sections 1.2-1.3 and "fused_moe_kernel";
+ * "DeepGEMM FusedMoE on Blackwell", sections 2.6.1-2.6.5).
+ *
+ *   x             [M, H] bf16
+ *   w13           [E, 2I, H] bf16 or e4m3 (per p->wdtype); rows [0, I) gate,
+ *                 [I, 2I) up
+ *   w13_scale     [E, 2I/128, H/128] fp32 for fp8 (NULL is MOE_E_INVALID), ignored for bf16
+ *   w2            [E, H, I] bf16 or e4m3
+ *   w2_scale      [E, H/128, I/128] fp32 for fp8 (NULL is MOE_E_INVALID), ignored for bf16
+ *   topk_ids      [M, topk] int32, topk_weights [M, topk] fp32 (as from moe_topk)
+ *   y             [M, H] bf16 out; may be the same buffer as x (in place)
+ *   workspace     device scratch of at least moe_workspace_bytes(p) bytes,
+ *                 256-byte aligned; its contents on entry do not matter
+ * M == 0 returns MOE_OK and launches nothing.
+ */
+moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w13,
+                           const float *w13_scale, const void *w2, const float *w2_scale,
+                           const int32_t *topk_ids, const float *topk_weights, void *y,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only: a static, human-readable name of a status code. */
+const char *moe_status_string(moe_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GFX950_H */

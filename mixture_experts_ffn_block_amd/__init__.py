@@ -1,0 +1,184 @@
+"""Python binding of libmoe.so, the gfx950 fused MoE expert forward.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/moe.h``. torch supplies device memory
+and the current HIP stream. If the library is not built this module raises
+at import of the first call; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
+MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
+
+EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_quant_fp8_groups",
+           "moe_workspace_bytes", "fused_experts", "moe_status_string")
+
+
+class MoeProblem(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("wdtype", ctypes.c_int32), ("apply_router_weight_on_input", ctypes.c_int32)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+_P, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_topk.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P]
+        L.moe_align_capacity.argtypes = [_I64, _I32, _I32, _I32]
+        L.moe_align_capacity.restype = _I64
+        L.moe_align_block_size.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P]
+        L.moe_quant_fp8_groups.argtypes = [_P, _I64, _I32, _P, _P, _P]
+        L.moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeProblem)]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.fused_experts.argtypes = [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]
+        L.moe_status_string.argtypes = [_I32]
+        L.moe_status_string.restype = ctypes.c_char_p
+        for name in ("moe_topk", "moe_align_block_size", "moe_quant_fp8_groups", "fused_experts"):
+            getattr(L, name).restype = _I32
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().moe_status_string(s).decode()
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected a contiguous {dtype} device tensor, "
+                         f"got {t.dtype} (contiguous={t.is_contiguous()}, device={t.device})")
+
+
+# ----------------------------------------------------------------- entries ---
+
+def moe_topk(logits: torch.Tensor, topk: int, renormalize: bool = True, stream=None,
+             out: tuple[torch.Tensor, torch.Tensor] | None = None):
+    """softmax + top-k router -> (topk_ids int32 [M, k], topk_weights fp32 [M, k])."""
+    _need(logits, torch.float32, "logits")
+    M, E = logits.shape
+    if out is None:
+        ids = torch.empty((M, topk), dtype=torch.int32, device=logits.device)
+        w = torch.empty((M, topk), dtype=torch.float32, device=logits.device)
+    else:
+        ids, w = out
+    _check(lib().moe_topk(_ptr(logits), M, E, topk, int(renormalize), _ptr(ids), _ptr(w),
+                          _stream(stream)), "moe_topk")
+    return ids, w
+
+
+def moe_align_capacity(M: int, topk: int, E: int, block_m: int) -> int:
+    return int(lib().moe_align_capacity(M, topk, E, block_m))
+
+
+def moe_align_block_size(topk_ids: torch.Tensor, E: int, block_m: int, stream=None):
+    """-> (sorted_token_ids [cap], expert_ids [cap/block_m], num_tokens_post_padded [1],
+    inv_perm [M, topk]), all int32 on the device."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    M, k = topk_ids.shape
+    cap = moe_align_capacity(M, k, E, block_m)
+    dev = topk_ids.device
+    sorted_ids = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(max(cap, 0) // block_m, dtype=torch.int32, device=dev)
+    npp = torch.zeros(1, dtype=torch.int32, device=dev)
+    inv = torch.empty((M, k), dtype=torch.int32, device=dev)
+    _check(lib().moe_align_block_size(_ptr(topk_ids), M, k, E, block_m, _ptr(sorted_ids),
+                                      _ptr(expert_ids), _ptr(npp), _ptr(inv), _stream(stream)),
+           "moe_align_block_size")
+    return sorted_ids, expert_ids, npp, inv
+
+
+def moe_quant_fp8_groups(x: torch.Tensor, stream=None):
+    """Per-row, per-128-column dynamic e4m3 quantisation -> (q, scale)."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=x.device)
+    s = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    _check(lib().moe_quant_fp8_groups(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream(stream)),
+           "moe_quant_fp8_groups")
+    return q, s
+
+
+def make_problem(M, H, I, E, topk, block_m, wdtype=MOE_W_BF16, on_input=False) -> MoeProblem:
+    return MoeProblem(M, H, I, E, topk, block_m, wdtype, int(on_input))
+
+
+def moe_workspace_bytes(p: MoeProblem) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(p)))
+
+
+def workspace_for(p: MoeProblem, device="cuda") -> torch.Tensor:
+    n = moe_workspace_bytes(p)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids: torch.Tensor,
+                  topk_weights: torch.Tensor, block_m: int, w13_scale: torch.Tensor | None = None,
+                  w2_scale: torch.Tensor | None = None, apply_router_weight_on_input=False,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """y = fused MoE expert forward (bf16 [M, H]). `out` may be `x` (in place)."""
+    _need(x, torch.bfloat16, "x")
+    fp8 = w13.dtype == torch.float8_e4m3fn
+    wdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    _need(w13, wdt, "w13")
+    _need(w2, wdt, "w2")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_weights, torch.float32, "topk_weights")
+    if fp8:
+        _need(w13_scale, torch.float32, "w13_scale")
+        _need(w2_scale, torch.float32, "w2_scale")
+    M, H = x.shape
+    E, N2, H2 = w13.shape
+    if H2 != H or tuple(w2.shape) != (E, H, N2 // 2) or topk_ids.shape != topk_weights.shape \
+            or topk_ids.shape[0] != M:
+        raise ValueError("fused_experts: inconsistent shapes")
+    p = make_problem(M, H, N2 // 2, E, topk_ids.shape[1], block_m,
+                     MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16, apply_router_weight_on_input)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = workspace_for(p, x.device)
+    _check(lib().fused_experts(ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                               _ptr(w2_scale), _ptr(topk_ids), _ptr(topk_weights), _ptr(out),
+                               _ptr(workspace), workspace.numel(), _stream(stream)),
+           "fused_experts")
+    return out

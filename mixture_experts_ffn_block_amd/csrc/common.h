@@ -1,0 +1,62 @@
+// common.h -- device types and helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_WAVE 64
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 has a native converter; the
+// compiler emits it for this cast).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(bf16_t, h);
+}
+
+// two fp32 -> packed pair of bf16 (low half = a)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// SiLU(g) = g / (1 + exp(-g)), fp32
+__device__ __forceinline__ float silu_f32(float g) {
+    return g / (1.0f + __expf(-g));
+}
+
+// fp32 -> OCP e4m3 byte, round to nearest even; the caller clamps to +-448.
+// gfx950's v_cvt_pk_fp8_f32 converts to the OCP float8_e4m3fn format.
+__device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float d) {
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int both = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+    return static_cast<uint32_t>(both);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

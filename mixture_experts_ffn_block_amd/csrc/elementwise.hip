@@ -1,0 +1,177 @@
+// elementwise.hip -- SiLU-and-mul (+ fp8 group quant), activation quant,
+// and the top-k weighted unpermute-reduce.
+//
+// * SiLU-and-mul: "fused_moe.py analysis", apply_moe_activation /
+//   _silu_and_mul_kernel; "DeepGEMM FusedMoE on Blackwell", 2.6.4 (SwiGLU and
+//   the dynamic per-128 quantisation in one pass): z = SiLU(gate) * up over
+//   the first and second halves of each GEMM1 row.
+// * Dynamic quantisation: "DeepGEMM FusedMoE on Blackwell", 2.5
+//   (per_token_group_quant_fp8, fp32 scale per 128 columns of a row).
+// * Reduce: "DeepGEMM FusedMoE on Blackwell", 2.6.5 (ep_gather: per token,
+//   the k expert rows are fetched through inv_perm and summed with their
+//   weights in fp32, then cast to bf16); "vLLM modular_kernel.py notes" 7.3.3
+//   (multiply by topk_weights, then sum over the top-k dimension).
+//
+// All three are HBM-bound; every thread moves 16-byte vectors.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+// ---------------------------------------------------------------- bf16 act --
+// One thread per 8 output elements. Rows >= num_tokens_post_padded are not
+// touched; padding rows (sentinel item) are written as zeros.
+__global__ __launch_bounds__(256) void silu_mul_bf16_kernel(
+    const bf16_t* __restrict__ h, bf16_t* __restrict__ z, const int32_t* __restrict__ sorted,
+    const float* __restrict__ weights, int R, int I, const int32_t* __restrict__ npp_ptr,
+    int on_input) {
+    const int64_t pos = blockIdx.y;
+    if (pos >= *npp_ptr) return;
+    const int i0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i0 >= I) return;
+    const int r = sorted[pos];
+    u32x4_t out{0, 0, 0, 0};
+    if (r < R) {
+        const float alpha = on_input ? weights[r] : 1.0f;
+        const u32x4_t g = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + i0);
+        const u32x4_t u = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + I + i0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float g0 = __uint_as_float(g[j] << 16), g1 = __uint_as_float(g[j] & 0xffff0000u);
+            const float u0 = __uint_as_float(u[j] << 16), u1 = __uint_as_float(u[j] & 0xffff0000u);
+            out[j] = pack_bf16x2(alpha * silu_f32(g0) * u0, alpha * silu_f32(g1) * u1);
+        }
+    }
+    *reinterpret_cast<u32x4_t*>(z + pos * I + i0) = out;
+}
+
+// ------------------------------------------------------ fp8 group quantiser --
+// Quantises 8 fp32 values per lane; the 16 lanes of a quarter-wave form one
+// 128-value group. Returns 8 e4m3 codes packed into 2 words and writes the
+// group scale from the group's first lane.
+__device__ __forceinline__ u32x2_t quant_group8(const float (&v)[8], float* scale_out, bool writer) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float s = amax / 448.0f;
+    if (writer) *scale_out = s;
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = amax == 0.0f ? 0.0f : fminf(fmaxf(v[j] / s, -448.0f), 448.0f);
+    return u32x2_t{cvt_e4m3x4(q[0], q[1], q[2], q[3]), cvt_e4m3x4(q[4], q[5], q[6], q[7])};
+}
+
+// SiLU-and-mul, then per-row per-128 fp8 quantisation of the fp32 result.
+// One wavefront per (row, 4 groups).
+__global__ __launch_bounds__(256) void silu_mul_fp8_kernel(
+    const bf16_t* __restrict__ h, uint8_t* __restrict__ zq, float* __restrict__ zs,
+    const int32_t* __restrict__ sorted, const float* __restrict__ weights, int R, int I,
+    const int32_t* __restrict__ npp_ptr, int on_input) {
+    const int64_t pos = blockIdx.y;
+    if (pos >= *npp_ptr) return;
+    const int lane = threadIdx.x & 63;
+    const int i0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512 + lane * 8;
+    if (i0 >= I) return;
+    const int r = sorted[pos];
+    float v[8];
+    if (r < R) {
+        const float alpha = on_input ? weights[r] : 1.0f;
+        const u32x4_t g = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + i0);
+        const u32x4_t u = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + I + i0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = alpha * silu_f32(__uint_as_float(g[j] << 16)) * __uint_as_float(u[j] << 16);
+            v[2 * j + 1] = alpha * silu_f32(__uint_as_float(g[j] & 0xffff0000u)) *
+                           __uint_as_float(u[j] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+    const u32x2_t q = quant_group8(v, zs + pos * (I / 128) + i0 / 128, (lane & 15) == 0);
+    *reinterpret_cast<u32x2_t*>(zq + pos * I + i0) = q;
+}
+
+// Per-row, per-128-column quantisation of a bf16 matrix [rows, cols].
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict__ x,
+                                                        uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale, int cols) {
+    const int64_t row = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512 + lane * 8;
+    if (c0 >= cols) return;
+    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + row * cols + c0);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(xv[j] << 16);
+        v[2 * j + 1] = __uint_as_float(xv[j] & 0xffff0000u);
+    }
+    const u32x2_t qq = quant_group8(v, scale + row * (cols / 128) + c0 / 128, (lane & 15) == 0);
+    *reinterpret_cast<u32x2_t*>(q + row * cols + c0) = qq;
+}
+
+// ------------------------------------------------------------------ reduce --
+// y[t, n] = bf16( sum_j alpha_j * o[inv_perm[t, j], n] ), fp32, slot order.
+__global__ __launch_bounds__(256) void reduce_kernel(const bf16_t* __restrict__ o,
+                                                     const int32_t* __restrict__ inv_perm,
+                                                     const float* __restrict__ weights, int k,
+                                                     int H, int use_weights,
+                                                     bf16_t* __restrict__ y) {
+    const int64_t t = blockIdx.y;
+    const int n0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (n0 >= H) return;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+        const int pos = inv_perm[t * k + j];
+        if (pos < 0) continue;
+        const float a = use_weights ? weights[t * k + j] : 1.0f;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o + static_cast<int64_t>(pos) * H + n0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += a * __uint_as_float(v[i] << 16);
+            acc[2 * i + 1] += a * __uint_as_float(v[i] & 0xffff0000u);
+        }
+    }
+    u32x4_t out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    *reinterpret_cast<u32x4_t*>(y + t * H + n0) = out;
+}
+
+}  // namespace
+
+hipError_t launch_silu_mul_bf16(const bf16_t* h, bf16_t* z, const int32_t* sorted,
+                                const float* weights, int R, int I, int64_t cap,
+                                const int32_t* npp, int on_input, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(I / 8, 256)), static_cast<unsigned>(cap));
+    hipLaunchKernelGGL(silu_mul_bf16_kernel, grid, dim3(256), 0, stream, h, z, sorted, weights, R,
+                       I, npp, on_input);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_fp8(const bf16_t* h, uint8_t* zq, float* zs, const int32_t* sorted,
+                               const float* weights, int R, int I, int64_t cap,
+                               const int32_t* npp, int on_input, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(I, 2048)), static_cast<unsigned>(cap));
+    hipLaunchKernelGGL(silu_mul_fp8_kernel, grid, dim3(256), 0, stream, h, zq, zs, sorted,
+                       weights, R, I, npp, on_input);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q, float* scale,
+                            hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(cols, 2048)), static_cast<unsigned>(rows));
+    hipLaunchKernelGGL(quant_fp8_kernel, grid, dim3(256), 0, stream, x, q, scale, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const bf16_t* o, const int32_t* inv_perm, const float* weights, int64_t M,
+                         int k, int H, int use_weights, bf16_t* y, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(H / 8, 256)), static_cast<unsigned>(M));
+    hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, o, inv_perm, weights, k, H,
+                       use_weights, y);
+    return hipGetLastError();
+}

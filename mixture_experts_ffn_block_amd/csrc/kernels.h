@@ -1,0 +1,50 @@
+// kernels.h -- launch entry points of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;
+
+// Arguments of one grouped expert GEMM: C[pos, n] = sum_k A[row(pos), k] * W[e(pos), n, k]
+// over the expert-sorted rows pos < num_tokens_post_padded.
+struct GemmArgs {
+    const void* A;             // activation rows (bf16 or e4m3)
+    int64_t lda_bytes;         // row stride of A
+    const int32_t* sorted;     // non-null: row(pos) = sorted[pos] / topk (gather); null: row = pos
+    int topk;
+    int R;                     // M * topk; sorted entries >= R are padding
+    const void* W;             // [E, N, K] weights
+    int64_t w_expert_bytes;    // bytes per expert of W
+    int64_t ldw_bytes;         // row stride of W
+    const int32_t* expert_ids; // [m_blocks]
+    const int32_t* npp;        // [1] num_tokens_post_padded (device)
+    void* C;                   // [m_blocks * BM, N] bf16
+    int64_t ldc_bytes;
+    int N, K;
+    int m_blocks;              // row blocks in the grid (capacity / block_m)
+    int group_m;               // row blocks per scheduling group
+    // fp8 only
+    const float* a_scale;      // per row of A, K/128 groups
+    const float* w_scale;      // [E, N/128, K/128]
+    int64_t w_scale_expert;    // floats per expert of w_scale
+    int scale_groups;          // K / 128
+};
+
+hipError_t launch_topk_softmax(const float* logits, int64_t M, int E, int k, int renormalize,
+                               int32_t* ids, float* weights, hipStream_t stream);
+hipError_t launch_align(const int32_t* ids, int64_t R, int E, int B, int64_t cap, int32_t* sorted,
+                        int32_t* expert_ids, int32_t* npp, int32_t* inv_perm, hipStream_t stream);
+int gemm_supported_block_m(int bm);
+hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStream_t stream);
+hipError_t launch_stream_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_silu_mul_bf16(const bf16_t* h, bf16_t* z, const int32_t* sorted,
+                                const float* weights, int R, int I, int64_t cap,
+                                const int32_t* npp, int on_input, hipStream_t stream);
+hipError_t launch_silu_mul_fp8(const bf16_t* h, uint8_t* zq, float* zs, const int32_t* sorted,
+                               const float* weights, int R, int I, int64_t cap,
+                               const int32_t* npp, int on_input, hipStream_t stream);
+hipError_t launch_quant_fp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q, float* scale,
+                            hipStream_t stream);
+hipError_t launch_reduce(const bf16_t* o, const int32_t* inv_perm, const float* weights, int64_t M,
+                         int k, int H, int use_weights, bf16_t* y, hipStream_t stream);

@@ -1,0 +1,106 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+every host-side check returns its status before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_block_amd as moe
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"if", "defined"})
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS), names
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_capacity_matches_oracle():
+    for args in [(64, 2, 8, 16), (4096, 2, 8, 128), (8192, 8, 256, 128), (32, 8, 128, 16),
+                 (1, 1, 1, 16), (0, 2, 8, 16), (7, 3, 5, 64)]:
+        assert moe.moe_align_capacity(*args) == oracle.align_capacity(*args)
+    assert moe.moe_align_capacity(-1, 2, 8, 16) == -1
+
+
+def P(**kw):
+    d = dict(M=64, H=256, I=512, E=8, topk=2, block_m=16, wdtype=moe.MOE_W_BF16, on_input=False)
+    d.update(kw)
+    return moe.make_problem(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), moe.MOE_E_INVALID),
+    (dict(topk=0), moe.MOE_E_INVALID),
+    (dict(topk=9), moe.MOE_E_INVALID),
+    (dict(E=300, topk=2), moe.MOE_E_UNSUPPORTED),
+    (dict(H=200), moe.MOE_E_UNSUPPORTED),
+    (dict(I=96), moe.MOE_E_UNSUPPORTED),
+    (dict(block_m=48), moe.MOE_E_UNSUPPORTED),
+    (dict(wdtype=7), moe.MOE_E_UNSUPPORTED),
+    (dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=16), moe.MOE_E_UNSUPPORTED),
+])
+def test_fused_experts_validation(kw, status):
+    p = P(**kw)
+    assert moe.moe_workspace_bytes(p) == 0
+    dummy = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    rc = moe.lib().fused_experts(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                 dummy, dummy, 1 << 40, None)
+    assert rc == status
+
+
+def test_fused_experts_pointer_and_workspace_checks():
+    p = P()
+    need = moe.moe_workspace_bytes(p)
+    assert need > 0
+    d = ctypes.c_void_p(1 << 20)
+    L = moe.lib()
+    assert L.fused_experts(ctypes.byref(p), None, d, None, d, None, d, d, d, d, need, None) \
+        == moe.MOE_E_INVALID
+    assert L.fused_experts(ctypes.byref(p), d, d, None, d, None, d, d, d, d, need - 1, None) \
+        == moe.MOE_E_WORKSPACE
+    assert L.fused_experts(ctypes.byref(p), d, d, None, d, None, d, d, d, None, need, None) \
+        == moe.MOE_E_WORKSPACE
+    misaligned = ctypes.c_void_p((1 << 20) + 64)
+    assert L.fused_experts(ctypes.byref(p), d, d, None, d, None, d, d, d, misaligned, need, None) \
+        == moe.MOE_E_INVALID
+    pf = P(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=64)
+    needf = moe.moe_workspace_bytes(pf)
+    assert L.fused_experts(ctypes.byref(pf), d, d, None, d, d, d, d, d, d, needf, None) \
+        == moe.MOE_E_INVALID
+    assert L.fused_experts(ctypes.byref(P(M=0)), None, None, None, None, None, None, None, None,
+                           None, 0, None) == moe.MOE_OK
+
+
+def test_workspace_grows_with_problem():
+    a = moe.moe_workspace_bytes(P(M=64))
+    b = moe.moe_workspace_bytes(P(M=128))
+    c = moe.moe_workspace_bytes(P(M=64, wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=32))
+    assert 0 < a < b and c > 0 and a % 256 == 0
+
+
+def test_router_align_quant_validation():
+    L = moe.lib()
+    d = ctypes.c_void_p(1 << 20)
+    assert L.moe_topk(d, 4, 8, 9, 1, d, d, None) == moe.MOE_E_INVALID
+    assert L.moe_topk(d, 4, 300, 2, 1, d, d, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_topk(None, 4, 8, 2, 1, d, d, None) == moe.MOE_E_INVALID
+    assert L.moe_topk(None, 0, 8, 2, 1, None, None, None) == moe.MOE_OK
+    assert L.moe_align_block_size(d, 4, 2, 8, 24, d, d, d, d, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_align_block_size(d, 4, 2, 8, 16, d, d, None, d, None) == moe.MOE_E_INVALID
+    assert L.moe_align_block_size(None, 4, 2, 8, 16, d, d, d, d, None) == moe.MOE_E_INVALID
+    assert L.moe_quant_fp8_groups(d, 4, 100, d, d, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_quant_fp8_groups(None, 4, 128, d, d, None) == moe.MOE_E_INVALID
+    assert L.moe_quant_fp8_groups(None, 0, 128, None, None, None) == moe.MOE_OK
+    for s in range(5):
+        assert moe.status_string(s)

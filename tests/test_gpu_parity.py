@@ -1,0 +1,263 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+* Router ids, the aligned layout and the fp8 activation codes are compared
+  bit for bit; router weights within 1e-6 (fp32 exp and division of k <= 32
+  terms: a few ulp of a value <= 1).
+* y is compared element by element: |y - y_ref| <= tol * max(1, |y_ref|) with
+  tol = 2e-2 for bf16 and 6e-2 for fp8.
+* Full-size workloads are checked on sampled tokens, which the oracle computes
+  one by one from host copies of the inputs those tokens touch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_block_amd as moe
+import oracle
+import synth
+from hostutil import bf16_f64, bits16, bits8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = {"bf16": 2e-2, "fp8": 6e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def to_dev(inp: synth.Inputs) -> synth.Inputs:
+    return synth.Inputs(*[None if t is None else t.to(DEV) for t in (
+        inp.x, inp.logits, inp.w13, inp.w2, inp.w13q, inp.w13s, inp.w2q, inp.w2s)])
+
+
+def run_layer(p: synth.Problem, d: synth.Inputs, ids, w, out=None):
+    if p.wdtype == "fp8":
+        return moe.fused_experts(d.x, d.w13q, d.w2q, ids, w, p.block_m, d.w13s, d.w2s,
+                                 apply_router_weight_on_input=p.apply_router_weight_on_input,
+                                 out=out)
+    return moe.fused_experts(d.x, d.w13, d.w2, ids, w, p.block_m,
+                             apply_router_weight_on_input=p.apply_router_weight_on_input, out=out)
+
+
+def oracle_layer(p, inp_cpu, ids, w, t0=0, t1=None):
+    on = p.apply_router_weight_on_input
+    if p.wdtype == "fp8":
+        return oracle.fused_experts_fp8(bits16(inp_cpu.x), bits8(inp_cpu.w13q),
+                                        inp_cpu.w13s.numpy(), bits8(inp_cpu.w2q),
+                                        inp_cpu.w2s.numpy(), ids, w, on_input=on, t0=t0, t1=t1)
+    return oracle.fused_experts_bf16(bits16(inp_cpu.x), bits16(inp_cpu.w13), bits16(inp_cpu.w2),
+                                     ids, w, on_input=on, t0=t0, t1=t1)
+
+
+def assert_close(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float, what: str):
+    a, b = bf16_f64(y_gpu), bf16_f64(y_ref)
+    assert np.all(np.isfinite(a)), f"{what}: non-finite output"
+    err = np.abs(a - b)
+    lim = tol * np.maximum(1.0, np.abs(b))
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, (f"{what}: {len(bad)} elements out of tolerance, first {bad[:4].tolist()}, "
+                           f"max err {err.max():.4g}")
+
+
+# ------------------------------------------------------------------ router ---
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_router_bit_exact(name):
+    p = synth.Problem.named(name)
+    log(f"router {name}")
+    logits = synth.make_inputs(synth.Problem(M=p.M, H=128, I=128, E=p.E, topk=p.topk,
+                                             bias_std=p.bias_std, seed=p.seed), "cpu").logits
+    ids, w = moe.moe_topk(logits.to(DEV), p.topk)
+    ids_ref, w_ref = oracle.topk(logits.numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
+
+
+def test_router_ties_and_unnormalised():
+    logits = torch.zeros((8, 16), dtype=torch.float32)
+    logits[:, 3] = 1.0
+    logits[:, 7] = 1.0
+    logits[4:, :] = torch.randn(4, 16, generator=torch.Generator().manual_seed(3))
+    for renorm in (True, False):
+        ids, w = moe.moe_topk(logits.to(DEV), 4, renormalize=renorm)
+        ids_ref, w_ref = oracle.topk(logits.numpy(), 4, renormalize=renorm)
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
+
+
+# ------------------------------------------------------------------- align ---
+
+def check_align(ids_np: np.ndarray, E: int, B: int):
+    ids = torch.from_numpy(ids_np).to(DEV)
+    s, x, npp, inv = moe.moe_align_block_size(ids, E, B)
+    rs, rx, rnpp, rinv = oracle.align(ids_np, E, B)
+    assert int(npp.item()) == rnpp
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(x.cpu().numpy(), rx)
+    assert np.array_equal(inv.cpu().numpy(), rinv)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_align_bit_exact_workloads(name):
+    p = synth.Problem.named(name)
+    log(f"align {name}")
+    logits = synth.make_inputs(synth.Problem(M=p.M, H=128, I=128, E=p.E, topk=p.topk,
+                                             bias_std=p.bias_std, seed=p.seed), "cpu").logits
+    ids, _ = oracle.topk(logits.numpy(), p.topk)
+    for B in sorted({p.block_m, 16, 64, 128}):
+        check_align(ids, p.E, B)
+
+
+def test_align_edge_cases():
+    g = np.random.default_rng(0)
+    check_align(np.zeros((300, 1), np.int32), 4, 16)                     # all to one expert
+    check_align(np.tile(np.arange(8, dtype=np.int32), (5, 1)), 8, 32)     # E == topk
+    check_align(np.array([[3, 1]], np.int32), 8, 128)                     # M = 1
+    ids = np.stack([g.choice(256, 8, replace=False) for _ in range(3000)]).astype(np.int32)
+    check_align(ids, 256, 64)
+    skew = np.minimum(g.geometric(0.05, (5000, 4)), 255).astype(np.int32)  # heavy skew, dupes ok
+    check_align(skew, 256, 16)
+
+
+# ------------------------------------------------------------------- quant ---
+
+def test_quant_fp8_bit_exact():
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(515, 7168, generator=g) * torch.exp2(torch.randint(-8, 8, (515, 1), generator=g))
+    x[3, 128:256] = 0.0
+    x[4, :5] = -0.0
+    xb = x.to(torch.bfloat16)
+    q, s = moe.moe_quant_fp8_groups(xb.to(DEV))
+    q_ref, s_ref = oracle.quant_groups_fp8(xb.float().numpy())
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(bits8(q), q_ref)
+
+
+# ------------------------------------------------------------- full layer ---
+
+SMALL = [
+    dict(M=64, H=256, I=512, E=8, topk=2, block_m=16),                 # tiny workload
+    dict(M=64, H=256, I=512, E=8, topk=2, block_m=32),
+    dict(M=64, H=256, I=512, E=8, topk=2, block_m=64),
+    dict(M=64, H=256, I=512, E=8, topk=2, block_m=128),
+    dict(M=37, H=384, I=256, E=6, topk=3, block_m=32),                 # ragged tails
+    dict(M=37, H=384, I=256, E=6, topk=3, block_m=64),
+    dict(M=130, H=640, I=384, E=5, topk=2, block_m=128),
+    dict(M=130, H=640, I=384, E=5, topk=2, block_m=16),
+    dict(M=1, H=256, I=256, E=4, topk=2, block_m=16),                  # a single token
+    dict(M=1, H=256, I=256, E=4, topk=2, block_m=128),
+    dict(M=24, H=256, I=256, E=4, topk=4, block_m=32),                 # E == topk
+    dict(M=64, H=256, I=512, E=8, topk=2, block_m=64, apply_router_weight_on_input=True),
+    dict(M=32, H=2048, I=768, E=128, topk=8, block_m=16),              # decode workload
+]
+FP8_SMALL = [
+    dict(M=40, H=256, I=384, E=5, topk=2, block_m=32, wdtype="fp8"),
+    dict(M=40, H=256, I=384, E=5, topk=2, block_m=64, wdtype="fp8"),
+    dict(M=150, H=512, I=256, E=7, topk=3, block_m=128, wdtype="fp8"),
+    dict(M=40, H=256, I=384, E=5, topk=2, block_m=64, wdtype="fp8",
+         apply_router_weight_on_input=True),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL + FP8_SMALL, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_layer_small_elementwise(cfg):
+    p = synth.Problem(**cfg)
+    log(f"layer {cfg}")
+    inp = synth.make_inputs(p, "cpu")
+    ids_ref, w_ref = oracle.topk(inp.logits.numpy(), p.topk)
+    d = to_dev(inp)
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    y = run_layer(p, d, ids, w)
+    torch.cuda.synchronize()
+    y_ref = oracle_layer(p, inp, ids_ref, w.cpu().numpy())
+    assert_close(bits16(y), y_ref, TOL[p.wdtype], str(cfg))
+
+
+def test_layer_all_tokens_one_expert_and_in_place():
+    p = synth.Problem(M=200, H=256, I=256, E=8, topk=2, block_m=64)
+    inp = synth.make_inputs(p, "cpu")
+    ids_np = np.tile(np.array([[5, 2]], np.int32), (p.M, 1))
+    w_np = np.tile(np.array([[0.75, 0.25]], np.float32), (p.M, 1))
+    d = to_dev(inp)
+    x_copy = d.x.clone()
+    y = run_layer(p, d, torch.from_numpy(ids_np).to(DEV), torch.from_numpy(w_np).to(DEV), out=d.x)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == d.x.data_ptr()
+    assert not torch.equal(x_copy, d.x)
+    y_ref = oracle_layer(p, inp, ids_np, w_np)
+    assert_close(bits16(y), y_ref, TOL["bf16"], "one expert, in place")
+
+
+def test_layer_deterministic():
+    p = synth.Problem(M=300, H=512, I=384, E=16, topk=4, block_m=64)
+    d = to_dev(synth.make_inputs(p, "cpu"))
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    a = run_layer(p, d, ids, w)
+    b = run_layer(p, d, ids, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_token_permutation_equivariance():
+    # permuting tokens permutes y rows; routing and tiles change, so compare
+    # to tolerance rather than bits
+    p = synth.Problem(M=96, H=256, I=256, E=6, topk=2, block_m=32)
+    d = to_dev(synth.make_inputs(p, "cpu"))
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    y = run_layer(p, d, ids, w)
+    perm = torch.randperm(p.M, generator=torch.Generator().manual_seed(1)).to(DEV)
+    dp = synth.Inputs(d.x[perm].contiguous(), d.logits[perm].contiguous(), d.w13, d.w2)
+    yp = run_layer(p, dp, ids[perm].contiguous(), w[perm].contiguous())
+    torch.cuda.synchronize()
+    assert_close(bits16(yp), bits16(y[perm]), 1e-2, "permuted tokens")
+
+
+# --------------------------------------------------- full-size, sampled ---
+
+def sampled_check(name, n_samples=6):
+    p = synth.Problem.named(name)
+    log(f"full-size {name}: generating inputs on the device")
+    d = synth.make_inputs(p, DEV)
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    y = run_layer(p, d, ids, w)
+    torch.cuda.synchronize()
+    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    ids_ref, _ = oracle.topk(d.logits.cpu().numpy(), p.topk)
+    assert np.array_equal(ids_np, ids_ref)
+    # samples: first, last, and tokens routed to the busiest expert
+    counts = np.bincount(ids_np.reshape(-1), minlength=p.E)
+    busiest = np.nonzero((ids_np == counts.argmax()).any(1))[0]
+    rng = np.random.default_rng(0)
+    toks = sorted(set([0, p.M - 1] + list(rng.choice(busiest, 2, replace=False)) +
+                      list(rng.choice(p.M, n_samples - 4, replace=False))))
+    experts = sorted(set(ids_np[toks].reshape(-1).tolist()))
+    remap = {e: i for i, e in enumerate(experts)}
+    sub_ids = np.vectorize(remap.get)(ids_np[toks]).astype(np.int32)
+    sel = torch.tensor(experts, device=DEV)
+    log(f"full-size {name}: oracle on tokens {toks} ({len(experts)} experts)")
+    sub = synth.Inputs(d.x[toks].cpu(), None,
+                       None if d.w13 is None else d.w13[sel].cpu(),
+                       None if d.w2 is None else d.w2[sel].cpu(),
+                       None if d.w13q is None else d.w13q[sel].cpu(),
+                       None if d.w13s is None else d.w13s[sel].cpu(),
+                       None if d.w2q is None else d.w2q[sel].cpu(),
+                       None if d.w2s is None else d.w2s[sel].cpu())
+    y_ref = oracle_layer(p, sub, sub_ids, w_np[toks])
+    assert_close(bits16(y[toks]), y_ref, TOL[p.wdtype], name)
+    assert bool(torch.isfinite(y.float()).all())
+
+
+@pytest.mark.parametrize("name", ["mixtral_prefill_m4096", "dsv3_skewed_prefill_m8192",
+                                  "fp8_block_m4096"])
+def test_layer_full_size_sampled(name):
+    sampled_check(name)
