@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Throughput of the fused MoE expert forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the router
+(moe_topk) and fused_experts (align, GEMM1, SiLU-and-mul, GEMM2, weighted
+unpermute-reduce; fp8 adds the activation quantisation). Inputs are seeded,
+synthetic and resident in HBM before the timed region starts.
+
+Printed JSON line (rank 0):
+  value        whole-job algorithmic TFLOP/s (6*M*topk*H*I per step); tokens/s beside it
+  roofline     the dominant kernel (GEMM1): algorithmic FLOP or bytes per launch divided
+               by its average duration, from HIP events recorded on its stream over a
+               second timed region that launches the same kernels stage by stage
+  cpu_baseline the CPU oracle timed on a bounded sample of tokens of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "fused-MoE layer TFLOP/s and tokens/s at 1 MI355X; % of MFMA or HBM roofline"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill_m4096", choices=list(synth.WORKLOADS))
+    ap.add_argument("--block-m", type=int, default=None, help="override the workload's block_m")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    return ap.parse_args()
+
+
+class Step:
+    """Device buffers and the two ways of running one step."""
+
+    def __init__(self, p: synth.Problem, d: synth.Inputs):
+        import mixture_experts_ffn_block_amd as moe
+        self.moe, self.p, self.d = moe, p, d
+        self.fp8 = p.wdtype == "fp8"
+        dev = d.x.device
+        M, H, I, E, k, B = p.M, p.H, p.I, p.E, p.topk, p.block_m
+        self.prob = moe.make_problem(M, H, I, E, k, B,
+                                     moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16,
+                                     p.apply_router_weight_on_input)
+        self.ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((M, k), dtype=torch.float32, device=dev)
+        self.y = torch.empty_like(d.x)
+        self.ws = moe.workspace_for(self.prob, dev)
+        cap = moe.moe_align_capacity(M, k, E, B)
+        self.cap = cap
+        # buffers of the staged run
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.sorted = torch.empty(cap, **i32)
+        self.expert_ids = torch.empty(cap // B, **i32)
+        self.npp = torch.zeros(1, **i32)
+        self.inv = torch.empty((M, k), **i32)
+        self.h = torch.empty((cap, 2 * I), dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        adt = torch.float8_e4m3fn if self.fp8 else torch.bfloat16
+        self.z = torch.empty((cap, I), dtype=adt, device=dev)
+        self.zs = torch.empty((cap, I // 128), dtype=torch.float32, device=dev) if self.fp8 else None
+        if self.fp8:
+            self.xq = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
+            self.xs = torch.empty((M, H // 128), dtype=torch.float32, device=dev)
+        self.w13 = d.w13q if self.fp8 else d.w13
+        self.w2 = d.w2q if self.fp8 else d.w2
+
+    def fused(self):
+        m, d = self.moe, self.d
+        m.moe_topk(d.logits, self.p.topk, out=(self.ids, self.w))
+        m.fused_experts(d.x, self.w13, self.w2, self.ids, self.w, self.p.block_m,
+                        d.w13s, d.w2s, self.p.apply_router_weight_on_input, out=self.y,
+                        workspace=self.ws)
+
+    STAGES = ("router", "quant", "align", "gemm1", "act", "gemm2", "reduce")
+
+    def staged(self, ev):
+        """The same kernels, launched stage by stage; ev[i] is recorded after stage i."""
+        m, d, p = self.moe, self.d, self.prob
+        lib = m.lib()
+        s = m._stream()
+        ev[0].record()
+        m.moe_topk(d.logits, self.p.topk, out=(self.ids, self.w))
+        ev[1].record()
+        a1, a1s = d.x, None
+        if self.fp8:
+            lib.moe_quant_fp8_groups(m._ptr(d.x), self.p.M, self.p.H, m._ptr(self.xq),
+                                     m._ptr(self.xs), s)
+            a1, a1s = self.xq, self.xs
+        ev[2].record()
+        lib.moe_align_block_size(m._ptr(self.ids), self.p.M, self.p.topk, self.p.E,
+                                 self.p.block_m, m._ptr(self.sorted), m._ptr(self.expert_ids),
+                                 m._ptr(self.npp), m._ptr(self.inv), s)
+        ev[3].record()
+        m.moe_expert_gemm(p, 1, a1, self.w13, self.sorted, self.expert_ids, self.npp, self.h,
+                          a1s, d.w13s)
+        ev[4].record()
+        m.moe_silu_and_mul(p, self.h, self.sorted, self.w, self.npp, self.z, self.zs)
+        ev[5].record()
+        m.moe_expert_gemm(p, 2, self.z, self.w2, None, self.expert_ids, self.npp, self.o,
+                          self.zs, d.w2s)
+        ev[6].record()
+        m.moe_unpermute_reduce(p, self.o, self.inv, self.w, self.y)
+        ev[7].record()
+
+
+def algorithmic(p: synth.Problem, touched: int):
+    """Algorithmic FLOP and HBM bytes of the step and of GEMM1 (padding excluded)."""
+    R = p.M * p.topk
+    wb = 1 if p.wdtype == "fp8" else 2
+    flops_g1 = 4.0 * R * p.H * p.I
+    flops = 6.0 * R * p.H * p.I
+    w13_b = touched * 2 * p.I * p.H * wb
+    w2_b = touched * p.H * p.I * wb
+    if p.wdtype == "fp8":
+        w13_b += touched * (2 * p.I // 128) * (p.H // 128) * 4
+        w2_b += touched * (p.H // 128) * (p.I // 128) * 4
+    x_b = p.M * p.H * 2
+    y_b = p.M * p.H * 2
+    logits_b = p.M * p.E * 4
+    xin_g1 = p.M * p.H * wb + (p.M * (p.H // 128) * 4 if p.wdtype == "fp8" else 0)
+    h_b = R * 2 * p.I * 2
+    return dict(flops=flops, bytes=w13_b + w2_b + x_b + y_b + logits_b,
+                flops_g1=flops_g1, bytes_g1=w13_b + xin_g1 + h_b)
+
+
+def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.Tensor,
+                 target_s: float):
+    """The CPU oracle on a bounded sample of tokens (test infrastructure, timed as a baseline)."""
+    import oracle
+    threads = oracle.threads()
+
+    def bits16(t):
+        return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def bits8(t):
+        return t.cpu().contiguous().view(torch.uint8).numpy()
+
+    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+
+    def run(T):
+        toks = np.arange(T)
+        experts = sorted(set(ids_np[toks].reshape(-1).tolist()))
+        remap = np.full(p.E, -1, np.int32)
+        remap[experts] = np.arange(len(experts), dtype=np.int32)
+        sub_ids = remap[ids_np[toks]]
+        sel = torch.tensor(experts, device=d.x.device)
+        x = bits16(d.x[:T])
+        if p.wdtype == "fp8":
+            args = (x, bits8(d.w13q[sel]), d.w13s[sel].cpu().numpy(), bits8(d.w2q[sel]),
+                    d.w2s[sel].cpu().numpy(), sub_ids, w_np[toks])
+            fn = oracle.fused_experts_fp8
+        else:
+            args = (x, bits16(d.w13[sel]), bits16(d.w2[sel]), sub_ids, w_np[toks])
+            fn = oracle.fused_experts_bf16
+        t0 = time.perf_counter()
+        fn(*args, on_input=p.apply_router_weight_on_input)
+        return time.perf_counter() - t0
+
+    T = min(p.M, threads)
+    dt = run(T)
+    if dt < target_s / 2 and T < p.M:
+        T = int(min(p.M, max(T, round(T * target_s / dt / threads) * threads)))
+        dt = run(T)
+    flops = 6.0 * T * p.topk * p.H * p.I
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "tokens_per_s": round(T / dt, 3), "seconds": round(dt, 3),
+            "sample": f"first {T} of {p.M} tokens of the same workload (all their top-{p.topk} "
+                      f"experts), plain C oracle, fp64 accumulation, {threads} OpenMP threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "gpus_requested": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    import mixture_experts_ffn_block_amd as moe
+    moe.lib()  # fails loudly if the HIP library is missing
+
+    over = {} if args.block_m is None else {"block_m": args.block_m}
+    p = synth.Problem.named(args.workload, **over)
+    print(f"# workload {args.workload}: {p}", file=sys.stderr, flush=True)
+    d = synth.make_inputs(p, "cuda")
+    st = Step(p, d)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        st.fused()
+    torch.cuda.synchronize()
+    ids_host = st.ids.cpu().numpy()
+    touched = int(np.unique(ids_host).size)
+
+    # timed region: K steps through the product entry points
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        st.fused()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+
+    # stage breakdown: the same kernels stage by stage, HIP events on the same stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    for _ in range(2):
+        st.staged([torch.cuda.Event(enable_timing=True) for _ in range(8)])
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        st.staged(evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+                for j, name in enumerate(Step.STAGES)}
+    staged_total = float(np.mean([e[0].elapsed_time(e[7]) for e in evs]))
+
+    alg = algorithmic(p, touched)
+    tflops = alg["flops"] / (ms * 1e-3) / 1e12
+    tok_s = p.M / (ms * 1e-3)
+    dt = "fp8" if p.wdtype == "fp8" else "bf16"
+    g1_s = stage_ms["gemm1"] * 1e-3
+    t_mfma = alg["flops_g1"] / (PEAK_TFLOPS[dt] * 1e12)
+    t_hbm = alg["bytes_g1"] / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(alg["flops_g1"] / g1_s / 1e12, 2),
+                "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(alg["bytes_g1"] / g1_s / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "gemm1 (grouped expert GEMM, gathered token rows x w13)"
+    roof["avg_ms"] = round(stage_ms["gemm1"], 4)
+    t_star = max(alg["flops"] / (PEAK_TFLOPS[dt] * 1e12), alg["bytes"] / (PEAK_HBM_GBS * 1e9))
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s",
+        "tokens_per_s": round(tok_s, 1), "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": args.workload, "M": p.M, "H": p.H, "I": p.I, "E": p.E,
+                   "topk": p.topk, "block_m": p.block_m, "weights": p.wdtype,
+                   "experts_touched": touched, "seed": p.seed},
+        "step_roofline_frac": round(t_star / (ms * 1e-3), 4),
+        "roofline": roof,
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "staged_ms_per_step": round(staged_total, 4),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+    }
+    if args.cpu_seconds > 0:
+        print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(p, d, st.ids, st.w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,7 +34,8 @@ typedef enum {
     MOE_OK = 0,
     MOE_E_INVALID = 1,     /* null pointer, negative size, topk outside [1, min(E, 32)] */
     MOE_E_UNSUPPORTED = 2, /* E > 256, H or I not a multiple of 128, unknown block_m or
-                              dtype, fp8 with block_m 16, more than 2^31 routed rows */
+                              dtype, fp8 with block_m 16 or 256, more than 2^31 routed rows,
+                              one expert's w13 of 2 GiB or more */
     MOE_E_WORKSPACE = 3,   /* workspace_bytes < moe_workspace_bytes(p) */
     MOE_E_HIP = 4          /* a kernel launch failed (hipGetLastError) */
 } moe_status_t;
@@ -52,7 +53,7 @@ typedef struct {
     int32_t I;         /* intermediate size per expert (w13 has 2I rows) */
     int32_t E;         /* experts */
     int32_t topk;      /* experts per token */
-    int32_t block_m;   /* rows per expert block: 16 (bf16 only), 32, 64 or 128 */
+    int32_t block_m;   /* rows per expert block: 16 or 256 (bf16 only), 32, 64 or 128 */
     int32_t wdtype;    /* moe_wdtype_t */
     int32_t apply_router_weight_on_input; /* 0: weight the expert outputs in the final sum;
                                              1: weight the SiLU-and-mul output instead */
@@ -145,6 +146,56 @@ moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w1
                            const float *w13_scale, const void *w2, const float *w2_scale,
                            const int32_t *topk_ids, const float *topk_weights, void *y,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The stages of fused_experts, for callers that build their own pipeline or
+ * time the stages one by one. fused_experts launches exactly these kernels.
+ * `p` has the same meaning as for fused_experts; cap is
+ * moe_align_capacity(M, topk, E, block_m); the layout arrays are those of
+ * moe_align_block_size. Rows at or past num_tokens_post_padded are skipped.
+ */
+
+/*
+ * Grouped expert GEMM over the expert-sorted layout ("fused_moe.py
+ * analysis", 1.3 and "fused_moe_kernel"; "DeepGEMM FusedMoE on Blackwell",
+ * 2.6.3 and 2.6.5): every block b of block_m rows uses expert expert_ids[b].
+ *   which = 1: c[pos, 0:2I] = a[sorted_token_ids[pos] / topk, :] . w13[e]^T,
+ *              a = x [M, H] (bf16, or e4m3 with a_scale [M, H/128]);
+ *              padding rows (sorted id >= M*topk) read token 0 and are never
+ *              consumed
+ *   which = 2: c[pos, 0:H] = a[pos, :] . w2[e]^T, a = z [cap, I] (bf16, or
+ *              e4m3 with a_scale [cap, I/128]); sorted_token_ids may be NULL
+ *   c [cap, N] bf16 out (fp32 accumulation, one rounding at the end).
+ *   fp8: w_scale is [E, N/128, K/128]; every 128-wide K block's partial sum
+ *   is multiplied by a_scale[row, block] * w_scale[e, n/128, block].
+ */
+moe_status_t moe_expert_gemm(const moe_problem_t *p, int32_t which, const void *a,
+                             const float *a_scale, const void *w, const float *w_scale,
+                             const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                             const int32_t *num_tokens_post_padded, void *c, void *stream);
+
+/*
+ * SiLU-and-mul ("DeepGEMM FusedMoE on Blackwell", 2.6.4; "fused_moe.py
+ * analysis", apply_moe_activation): z[pos, i] = SiLU(h[pos, i]) * h[pos, I+i]
+ * in fp32 (times topk_weights[item] when apply_router_weight_on_input),
+ * padding rows set to 0.
+ *   h [cap, 2I] bf16; z [cap, I] bf16 out, or for fp8 z [cap, I] e4m3 plus
+ *   z_scale [cap, I/128] fp32 out (per-row, per-128 dynamic quantisation).
+ */
+moe_status_t moe_silu_and_mul(const moe_problem_t *p, const void *h,
+                              const int32_t *sorted_token_ids, const float *topk_weights,
+                              const int32_t *num_tokens_post_padded, void *z, float *z_scale,
+                              void *stream);
+
+/*
+ * Weighted unpermute-reduce ("DeepGEMM FusedMoE on Blackwell", 2.6.5,
+ * ep_gather; "vLLM modular_kernel.py notes", 7.3.3):
+ *   y[t, :] = bf16( sum_j a_j * o[inv_perm[t, j], :] ), fp32, slots in order,
+ *   a_j = topk_weights[t, j] (1 when apply_router_weight_on_input);
+ *   slots with inv_perm < 0 are skipped. o [cap, H] bf16, y [M, H] bf16 out.
+ */
+moe_status_t moe_unpermute_reduce(const moe_problem_t *p, const void *o, const int32_t *inv_perm,
+                                  const float *topk_weights, void *y, void *stream);
 
 /* Host-only: a static, human-readable name of a status code. */
 const char *moe_status_string(moe_status_t s);

@@ -20,7 +20,8 @@ MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
 
 EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_quant_fp8_groups",
-           "moe_workspace_bytes", "fused_experts", "moe_status_string")
+           "moe_workspace_bytes", "fused_experts", "moe_expert_gemm", "moe_silu_and_mul",
+           "moe_unpermute_reduce", "moe_status_string")
 
 
 class MoeProblem(ctypes.Structure):
@@ -55,9 +56,14 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.fused_experts.argtypes = [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]
+        PP = ctypes.POINTER(MoeProblem)
+        L.moe_expert_gemm.argtypes = [PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_silu_and_mul.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_unpermute_reduce.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_status_string.argtypes = [_I32]
         L.moe_status_string.restype = ctypes.c_char_p
-        for name in ("moe_topk", "moe_align_block_size", "moe_quant_fp8_groups", "fused_experts"):
+        for name in ("moe_topk", "moe_align_block_size", "moe_quant_fp8_groups", "fused_experts",
+                     "moe_expert_gemm", "moe_silu_and_mul", "moe_unpermute_reduce"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -182,3 +188,35 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
                                _ptr(workspace), workspace.numel(), _stream(stream)),
            "fused_experts")
     return out
+
+
+# ------------------------------------------------------------------ stages ---
+
+def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
+                    sorted_token_ids: torch.Tensor | None, expert_ids: torch.Tensor,
+                    num_tokens_post_padded: torch.Tensor, c: torch.Tensor,
+                    a_scale: torch.Tensor | None = None, w_scale: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Grouped expert GEMM over the aligned layout (which = 1: x.w13^T, 2: z.w2^T)."""
+    _check(lib().moe_expert_gemm(ctypes.byref(p), which, _ptr(a), _ptr(a_scale), _ptr(w),
+                                 _ptr(w_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
+                                 _ptr(num_tokens_post_padded), _ptr(c), _stream(stream)),
+           "moe_expert_gemm")
+    return c
+
+
+def moe_silu_and_mul(p: MoeProblem, h: torch.Tensor, sorted_token_ids: torch.Tensor,
+                     topk_weights: torch.Tensor, num_tokens_post_padded: torch.Tensor,
+                     z: torch.Tensor, z_scale: torch.Tensor | None = None, stream=None):
+    _check(lib().moe_silu_and_mul(ctypes.byref(p), _ptr(h), _ptr(sorted_token_ids),
+                                  _ptr(topk_weights), _ptr(num_tokens_post_padded), _ptr(z),
+                                  _ptr(z_scale), _stream(stream)), "moe_silu_and_mul")
+    return z, z_scale
+
+
+def moe_unpermute_reduce(p: MoeProblem, o: torch.Tensor, inv_perm: torch.Tensor,
+                         topk_weights: torch.Tensor, y: torch.Tensor, stream=None):
+    _check(lib().moe_unpermute_reduce(ctypes.byref(p), _ptr(o), _ptr(inv_perm),
+                                      _ptr(topk_weights), _ptr(y), _stream(stream)),
+           "moe_unpermute_reduce")
+    return y

@@ -57,7 +57,11 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->E > kMaxE || p->H % 128 || p->I % 128) return MOE_E_UNSUPPORTED;
     if (!block_m_ok(p->block_m)) return MOE_E_UNSUPPORTED;
     if (p->wdtype != MOE_W_BF16 && p->wdtype != MOE_W_FP8_E4M3_BLOCK128) return MOE_E_UNSUPPORTED;
-    if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && p->block_m == 16) return MOE_E_UNSUPPORTED;
+    if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && (p->block_m == 16 || p->block_m == 256))
+        return MOE_E_UNSUPPORTED;
+    // one expert's weight matrix is addressed with 32-bit byte offsets
+    const int64_t esz = p->wdtype == MOE_W_FP8_E4M3_BLOCK128 ? 1 : 2;
+    if (int64_t(2) * p->I * p->H * esz >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
     // positions and routed items are int32 on the device
     if (p->M * p->topk >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
     if (moe_align_capacity(p->M, p->topk, p->E, p->block_m) >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
@@ -65,6 +69,64 @@ moe_status_t check_problem(const moe_problem_t* p) {
 }
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+
+// ---- the stages of fused_experts, shared with their exported entry points --
+
+// which == 1: C[pos, :2I] = A[token(pos)] w13[e]^T, A rows gathered through sorted
+// which == 2: C[pos, :H]  = A[pos] w2[e]^T
+hipError_t gemm_stage(const moe_problem_t& p, int which, const void* a, const float* a_scale,
+                      const void* w, const float* w_scale, const int32_t* sorted,
+                      const int32_t* expert_ids, const int32_t* npp, void* c, hipStream_t s) {
+    const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    const int esz = fp8 ? 1 : 2;  // bytes per weight / activation element
+    const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
+    const int N = which == 1 ? 2 * p.I : p.H;
+    const int K = which == 1 ? p.H : p.I;
+    GemmArgs g{};
+    g.A = a;
+    g.lda_bytes = static_cast<int64_t>(K) * esz;
+    g.sorted = which == 1 ? sorted : nullptr;
+    g.topk = p.topk;
+    g.R = static_cast<int>(p.M * p.topk);
+    g.W = w;
+    g.w_expert_bytes = static_cast<int64_t>(N) * K * esz;
+    g.ldw_bytes = static_cast<int64_t>(K) * esz;
+    g.expert_ids = expert_ids;
+    g.npp = npp;
+    g.C = c;
+    g.ldc_bytes = static_cast<int64_t>(N) * 2;
+    g.N = N;
+    g.K = K;
+    g.m_blocks = static_cast<int>(cap / p.block_m);
+    g.group_m = kGroupM;
+    if (fp8) {
+        g.a_scale = a_scale;
+        g.w_scale = w_scale;
+        g.w_scale_expert = static_cast<int64_t>(N / 128) * (K / 128);
+        g.scale_groups = K / 128;
+    }
+    return p.block_m == 16 ? launch_stream_gemm(g, s) : launch_grouped_gemm(g, p.block_m, fp8, s);
+}
+
+hipError_t act_stage(const moe_problem_t& p, const void* h, const int32_t* sorted,
+                     const float* weights, const int32_t* npp, void* z, float* z_scale,
+                     hipStream_t s) {
+    const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
+    const int R = static_cast<int>(p.M * p.topk);
+    const int on_input = p.apply_router_weight_on_input ? 1 : 0;
+    if (p.wdtype == MOE_W_FP8_E4M3_BLOCK128)
+        return launch_silu_mul_fp8(static_cast<const bf16_t*>(h), static_cast<uint8_t*>(z),
+                                   z_scale, sorted, weights, R, p.I, cap, npp, on_input, s);
+    return launch_silu_mul_bf16(static_cast<const bf16_t*>(h), static_cast<bf16_t*>(z), sorted,
+                                weights, R, p.I, cap, npp, on_input, s);
+}
+
+hipError_t reduce_stage(const moe_problem_t& p, const void* o, const int32_t* inv_perm,
+                        const float* weights, void* y, hipStream_t s) {
+    return launch_reduce(static_cast<const bf16_t*>(o), inv_perm, weights, p.M, p.topk, p.H,
+                         p.apply_router_weight_on_input ? 0 : 1, static_cast<bf16_t*>(y), s);
+}
 
 }  // namespace
 
@@ -153,81 +215,69 @@ moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w1
     int32_t* inv_perm = reinterpret_cast<int32_t*>(ws + L.inv_perm);
     void* ho = ws + L.ho;
     void* z = ws + L.z;
-    const int M = static_cast<int>(p->M), H = p->H, I = p->I, k = p->topk, B = p->block_m;
-    const int R = static_cast<int>(L.R);
-    const int m_blocks = static_cast<int>(L.cap / B);
+    const int M = static_cast<int>(p->M), H = p->H;
 
     hipError_t err = hipSuccess;
     const void* a1 = x;
+    const float* a1_scale = nullptr;
     if (fp8) {
         err = launch_quant_fp8(static_cast<const bf16_t*>(x), M, H, ws + L.xq,
                                reinterpret_cast<float*>(ws + L.xs), s);
         if (err != hipSuccess) return MOE_E_HIP;
         a1 = ws + L.xq;
+        a1_scale = reinterpret_cast<const float*>(ws + L.xs);
     }
-    err = launch_align(topk_ids, R, p->E, B, L.cap, sorted, expert_ids, npp, inv_perm, s);
+    err = launch_align(topk_ids, M * p->topk, p->E, p->block_m, L.cap, sorted, expert_ids, npp,
+                       inv_perm, s);
     if (err != hipSuccess) return MOE_E_HIP;
-
-    const int esz = fp8 ? 1 : 2;  // bytes per weight / activation element
-    GemmArgs g1{};
-    g1.A = a1;
-    g1.lda_bytes = static_cast<int64_t>(H) * esz;
-    g1.sorted = sorted;
-    g1.topk = k;
-    g1.R = R;
-    g1.W = w13;
-    g1.w_expert_bytes = static_cast<int64_t>(2 * I) * H * esz;
-    g1.ldw_bytes = static_cast<int64_t>(H) * esz;
-    g1.expert_ids = expert_ids;
-    g1.npp = npp;
-    g1.C = ho;
-    g1.ldc_bytes = static_cast<int64_t>(2 * I) * 2;
-    g1.N = 2 * I;
-    g1.K = H;
-    g1.m_blocks = m_blocks;
-    g1.group_m = kGroupM;
-    if (fp8) {
-        g1.a_scale = reinterpret_cast<const float*>(ws + L.xs);
-        g1.w_scale = w13_scale;
-        g1.w_scale_expert = static_cast<int64_t>(2 * I / 128) * (H / 128);
-        g1.scale_groups = H / 128;
-    }
-    err = B == 16 ? launch_stream_gemm(g1, s) : launch_grouped_gemm(g1, B, fp8, s);
+    err = gemm_stage(*p, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, s);
     if (err != hipSuccess) return MOE_E_HIP;
-
-    const int on_input = p->apply_router_weight_on_input ? 1 : 0;
-    if (fp8)
-        err = launch_silu_mul_fp8(static_cast<const bf16_t*>(ho), static_cast<uint8_t*>(z),
-                                  reinterpret_cast<float*>(ws + L.zs), sorted, topk_weights, R, I,
-                                  L.cap, npp, on_input, s);
-    else
-        err = launch_silu_mul_bf16(static_cast<const bf16_t*>(ho), static_cast<bf16_t*>(z), sorted,
-                                   topk_weights, R, I, L.cap, npp, on_input, s);
+    err = act_stage(*p, ho, sorted, topk_weights, npp, z, reinterpret_cast<float*>(ws + L.zs), s);
     if (err != hipSuccess) return MOE_E_HIP;
-
-    GemmArgs g2 = g1;
-    g2.A = z;
-    g2.lda_bytes = static_cast<int64_t>(I) * esz;
-    g2.sorted = nullptr;
-    g2.W = w2;
-    g2.w_expert_bytes = static_cast<int64_t>(H) * I * esz;
-    g2.ldw_bytes = static_cast<int64_t>(I) * esz;
-    g2.C = ho;
-    g2.ldc_bytes = static_cast<int64_t>(H) * 2;
-    g2.N = H;
-    g2.K = I;
-    if (fp8) {
-        g2.a_scale = reinterpret_cast<const float*>(ws + L.zs);
-        g2.w_scale = w2_scale;
-        g2.w_scale_expert = static_cast<int64_t>(H / 128) * (I / 128);
-        g2.scale_groups = I / 128;
-    }
-    err = B == 16 ? launch_stream_gemm(g2, s) : launch_grouped_gemm(g2, B, fp8, s);
+    err = gemm_stage(*p, 2, z, reinterpret_cast<const float*>(ws + L.zs), w2, w2_scale, sorted,
+                     expert_ids, npp, ho, s);
     if (err != hipSuccess) return MOE_E_HIP;
+    return hip_status(reduce_stage(*p, ho, inv_perm, topk_weights, y, s));
+}
 
-    err = launch_reduce(static_cast<const bf16_t*>(ho), inv_perm, topk_weights, M, k, H,
-                        on_input ? 0 : 1, static_cast<bf16_t*>(y), s);
-    return hip_status(err);
+moe_status_t moe_expert_gemm(const moe_problem_t* p, int32_t which, const void* a,
+                             const float* a_scale, const void* w, const float* w_scale,
+                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                             const int32_t* num_tokens_post_padded, void* c, void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (which != 1 && which != 2) return MOE_E_INVALID;
+    if (p->M == 0) return MOE_OK;
+    const bool fp8 = p->wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    if (!a || !w || !expert_ids || !num_tokens_post_padded || !c) return MOE_E_INVALID;
+    if (which == 1 && !sorted_token_ids) return MOE_E_INVALID;
+    if (fp8 && (!a_scale || !w_scale)) return MOE_E_INVALID;
+    return hip_status(gemm_stage(*p, which, a, a_scale, w, w_scale, sorted_token_ids, expert_ids,
+                                 num_tokens_post_padded, c, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_silu_and_mul(const moe_problem_t* p, const void* h,
+                              const int32_t* sorted_token_ids, const float* topk_weights,
+                              const int32_t* num_tokens_post_padded, void* z, float* z_scale,
+                              void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->M == 0) return MOE_OK;
+    if (!h || !sorted_token_ids || !topk_weights || !num_tokens_post_padded || !z)
+        return MOE_E_INVALID;
+    if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && !z_scale) return MOE_E_INVALID;
+    return hip_status(act_stage(*p, h, sorted_token_ids, topk_weights, num_tokens_post_padded, z,
+                                z_scale, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_unpermute_reduce(const moe_problem_t* p, const void* o, const int32_t* inv_perm,
+                                  const float* topk_weights, void* y, void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->M == 0) return MOE_OK;
+    if (!o || !inv_perm || !topk_weights || !y) return MOE_E_INVALID;
+    return hip_status(reduce_stage(*p, o, inv_perm, topk_weights, y,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

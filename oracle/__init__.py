@@ -68,6 +68,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
         L.oracle_align_capacity.restype = _I64
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = _I32
         _lib = L
     return _lib
 
@@ -80,6 +82,11 @@ def _c(a: np.ndarray, dtype) -> np.ndarray:
 
 def _p(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oracle_threads())
 
 
 # ---------------------------------------------------------------- codecs ---

@@ -34,9 +34,13 @@
  *     RNE(clamp(v/scale)), an all-zero group gives scale 0 and code 0.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the parallel loops below use (reported beside CPU timings). */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 stored mantissa bits. */

@@ -113,7 +113,7 @@ def test_align_bit_exact_workloads(name):
     logits = synth.make_inputs(synth.Problem(M=p.M, H=128, I=128, E=p.E, topk=p.topk,
                                              bias_std=p.bias_std, seed=p.seed), "cpu").logits
     ids, _ = oracle.topk(logits.numpy(), p.topk)
-    for B in sorted({p.block_m, 16, 64, 128}):
+    for B in sorted({p.block_m, 16, 64, 128, 256}):
         check_align(ids, p.E, B)
 
 
@@ -158,6 +158,8 @@ SMALL = [
     dict(M=24, H=256, I=256, E=4, topk=4, block_m=32),                 # E == topk
     dict(M=64, H=256, I=512, E=8, topk=2, block_m=64, apply_router_weight_on_input=True),
     dict(M=32, H=2048, I=768, E=128, topk=8, block_m=16),              # decode workload
+    dict(M=300, H=512, I=384, E=3, topk=2, block_m=256),               # 256-row blocks
+    dict(M=64, H=256, I=512, E=8, topk=2, block_m=256),
 ]
 FP8_SMALL = [
     dict(M=40, H=256, I=384, E=5, topk=2, block_m=32, wdtype="fp8"),

@@ -42,7 +42,7 @@ def check_invariants(ids, E, B, sorted_ids, expert_ids, npp, inv):
 
 
 @pytest.mark.parametrize("M,k,E,B", [(64, 2, 8, 16), (32, 8, 128, 16), (100, 4, 16, 32),
-                                     (7, 3, 5, 64), (300, 8, 256, 128)])
+                                     (7, 3, 5, 64), (300, 8, 256, 128), (500, 2, 6, 256)])
 def test_align_random(M, k, E, B):
     g = np.random.default_rng(M + k + E + B)
     ids = np.stack([g.choice(E, k, replace=False) for _ in range(M)]).astype(np.int32)
