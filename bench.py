@@ -33,6 +33,36 @@ import synth  # noqa: E402
 METRIC = "fused-MoE layer TFLOP/s and tokens/s at 1 MI355X; % of MFMA or HBM roofline"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("gemm.hip", "gemm_stream.hip", "common.h", "kernels.h", "api.hip")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the GEMM sources; a traffic measurement is only reported for the
+    kernel it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_ffn_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM1 launch from the committed counter profile of this workload
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel of known size), or None if
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"gemm1_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return float(kv["hbm_bytes_per_launch"])
 
 
 def parse():
@@ -44,6 +74,10 @@ def parse():
     ap.add_argument("--block-m", type=int, default=None, help="override the workload's block_m")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before the timed region, so "
+                         "that a counter profile of this command can scale FETCH_SIZE and "
+                         "WRITE_SIZE by a kernel whose traffic is known")
     return ap.parse_args()
 
 
@@ -203,6 +237,13 @@ def main():
     print(f"# workload {args.workload}: {p}", file=sys.stderr, flush=True)
     d = synth.make_inputs(p, "cuda")
     st = Step(p, d)
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -249,7 +290,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(alg["bytes_g1"] / g1_s / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.workload)
     roof["kernel"] = "gemm1 (grouped expert GEMM, gathered token rows x w13)"
     roof["avg_ms"] = round(stage_ms["gemm1"], 4)
     t_star = max(alg["flops"] / (PEAK_TFLOPS[dt] * 1e12), alg["bytes"] / (PEAK_HBM_GBS * 1e9))

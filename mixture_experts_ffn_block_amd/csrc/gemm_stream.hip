@@ -27,6 +27,7 @@ constexpr int kTilesPerWave = 4;                 // 16-column MFMA tiles per wav
 constexpr int kColsPerWave = 16 * kTilesPerWave;  // 64
 constexpr int kColsPerWG = kWavesPerWG * kColsPerWave;
 
+template <bool GATHER>
 __global__ __launch_bounds__(kWavesPerWG * 64) void stream_gemm_bf16_kernel(GemmArgs p) {
     const int n_wg = (p.N + kColsPerWG - 1) / kColsPerWG;
     const int mb = blockIdx.x / n_wg, nb = blockIdx.x % n_wg;
@@ -42,9 +43,9 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void stream_gemm_bf16_kernel(Gemm
     if (nw0 >= p.N) return;
 
     int64_t src_row = m0 + row16;
-    if (p.sorted) {
+    if constexpr (GATHER) {
         const int r = p.sorted[m0 + row16];
-        src_row = r < p.R ? r / p.topk : 0;
+        src_row = r < p.R ? r / p.topk : 0;  // padding rows read token 0
     }
     const uint8_t* a_ptr = reinterpret_cast<const uint8_t*>(p.A) + src_row * p.lda_bytes + kq * 64;
     const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
@@ -109,6 +110,9 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void stream_gemm_bf16_kernel(Gemm
 hipError_t launch_stream_gemm(const GemmArgs& a, hipStream_t stream) {
     const int n_wg = (a.N + kColsPerWG - 1) / kColsPerWG;
     const dim3 grid(static_cast<unsigned>(a.m_blocks * n_wg));
-    hipLaunchKernelGGL(stream_gemm_bf16_kernel, grid, dim3(kWavesPerWG * 64), 0, stream, a);
+    if (a.sorted)
+        hipLaunchKernelGGL(stream_gemm_bf16_kernel<true>, grid, dim3(kWavesPerWG * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL(stream_gemm_bf16_kernel<false>, grid, dim3(kWavesPerWG * 64), 0, stream, a);
     return hipGetLastError();
 }
