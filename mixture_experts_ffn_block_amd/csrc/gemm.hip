@@ -33,6 +33,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef DMA128_WIDE
+#define DMA128_WIDE 0
+#endif
+
 namespace {
 
 constexpr int kRowBytes = 128;  // one tile row = 128 bytes of K
@@ -63,6 +67,35 @@ struct Tile {
     static_assert(kLdsBytes <= 160 * 1024, "fits gfx950 LDS");
 };
 
+// ---- tile scheduling, shared by the LDS-tiled kernels ---------------------
+// The grid is sized for the worst-case number of expert blocks; only the
+// first npp / BM blocks hold rows, so the logical tiles are those of the real
+// blocks and the rest of the grid exits at once (otherwise the empty tiles,
+// which come last in the logical order, would leave whole XCDs idle).
+// Hardware id h runs on XCD h % 8; XCD x receives the contiguous logical range
+// starting at x*q + min(x, rem), a bijection onto [0, total), so tiles that
+// share token rows or weight rows meet in one L2. The logical order walks
+// group_m expert blocks down one column of tiles before the next column.
+struct TilePos {
+    int mb, nb;
+};
+template <int BM, int BN>
+__device__ __forceinline__ bool tile_of(const GemmArgs& p, TilePos& t) {
+    const int n_tiles = (p.N + BN - 1) / BN;
+    const int m_real = min(p.m_blocks, (*p.npp + BM - 1) / BM);
+    const int total = m_real * n_tiles;
+    const int hw = blockIdx.x;
+    if (hw >= total) return false;
+    const int xcd = hw & 7, q8 = total >> 3, rem = total & 7;
+    const int tile = xcd * q8 + min(xcd, rem) + (hw >> 3);
+    const int per_group = p.group_m * n_tiles;
+    const int first_mb = (tile / per_group) * p.group_m;
+    const int rows_in_group = min(p.group_m, m_real - first_mb);
+    t.mb = first_mb + (tile % per_group) % rows_in_group;
+    t.nb = (tile % per_group) / rows_in_group;
+    return true;
+}
+
 // Both operands are staged through LDS: 8 consecutive lanes load one row's
 // 128-byte K slice, so every global load instruction reads whole cache lines.
 // The next K tile is loaded into registers while the current one is
@@ -73,23 +106,10 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) u32x4_t sA[2][BM * kChunks];
     __shared__ __attribute__((aligned(16))) u32x4_t sB[2][BN * kChunks];
 
-    // ---- tile scheduling: XCD-aware remap, then grouped ordering ----------
-    const int n_tiles = (p.N + BN - 1) / BN;
-    const int total = p.m_blocks * n_tiles;
-    // hardware id h runs on XCD h % 8; XCD x receives the contiguous logical
-    // range starting at x*q + min(x, rem) (a bijection onto [0, total))
-    const int hw = blockIdx.x, xcd = hw & 7;
-    const int q8 = total >> 3, rem = total & 7;
-    const int tile = xcd * q8 + min(xcd, rem) + (hw >> 3);
-    const int per_group = p.group_m * n_tiles;
-    const int first_mb = (tile / per_group) * p.group_m;
-    const int rows_in_group = min(p.group_m, p.m_blocks - first_mb);
-    const int mb = first_mb + (tile % per_group) % rows_in_group;
-    const int nb = (tile % per_group) / rows_in_group;
-
-    const int npp = *p.npp;
+    TilePos tp;
+    if (!tile_of<BM, BN>(p, tp)) return;
+    const int mb = tp.mb, nb = tp.nb;
     const int64_t m0 = static_cast<int64_t>(mb) * BM;
-    if (m0 >= npp) return;
     const int e = p.expert_ids[mb];
     if (e < 0) return;
     const int n0 = nb * BN;
@@ -123,10 +143,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs p) {
     if constexpr (FP8) {
 #pragma unroll
         for (int tm = 0; tm < T::TM; ++tm) xs_row[tm] = p.a_scale + src_row_of(tm * 32 + r32) * p.scale_groups;
-        // a wave's WN (<= 128, dividing 128) weight rows lie in one 128-row scale block
+        // a wave's WN (<= 128, dividing 128) weight rows lie in one 128-row scale
+        // block; waves wholly past N (tail tile) read the last block, unused
         static_assert(128 % T::WN == 0, "wave columns within one scale block");
         ws_row = p.w_scale + static_cast<int64_t>(e) * p.w_scale_expert +
-                 static_cast<int64_t>((n0 + wave * T::WN) / 128) * p.scale_groups;
+                 static_cast<int64_t>(min((n0 + wave * T::WN) / 128, p.N / 128 - 1)) * p.scale_groups;
     }
 
     const int KT = p.K / T::kElemsPerRow;
@@ -263,10 +284,6 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs p) {
 // groups of a 256-byte bank row.
 namespace dma {
 
-constexpr int ROWB = 64, CH = 4;  // tile rows are 32 bf16 = 64 bytes of K
-
-__device__ __forceinline__ int swz64(int row, int chunk) { return row * CH + (chunk ^ ((row >> 2) & 3)); }
-
 // Copies of 1 KB each into consecutive 1 KB LDS blocks starting at `lds`. M0
 // holds the LDS base; the instruction offset is added to both the LDS and the
 // global address, so copy i passes its global address minus i KB. One M0 write
@@ -301,6 +318,16 @@ __device__ __forceinline__ void copy_group(const uint8_t* const (&g)[N], uint32_
             : "memory");
 }
 
+// scheduling pattern: R LDS reads spread over Mf MFMAs, one read then its
+// share of the MFMAs
+template <int I, int R, int Mf>
+__device__ __forceinline__ void interleave_step() {
+    constexpr int n = (I + 1) * Mf / R - I * Mf / R;
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x008, n, 0);  // MFMA
+    if constexpr (I + 1 < R) interleave_step<I + 1, R, Mf>();
+}
+
 // wait until the copies of all but the newest `newer` K tiles of this wave have
 // landed (L copies per tile), then barrier
 template <int L>
@@ -315,19 +342,33 @@ __device__ __forceinline__ void wait_barrier(int newer) {
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Geometry: BM x BN tile, WM x WN waves (4 in total), each wave 128 x 128
-// (4 x 4 MFMA tiles), STAGES LDS stages of (BM + BN) x 64 bytes.
-template <int BM_, int BN_, int WM_, int STAGES_>
+// Geometry: BM x BN tile, WM x WN waves (4 in total), each wave TM x TN MFMA
+// tiles of 32 x 32; STAGES LDS stages of (BM + BN) rows of ROWB bytes (ROWB/2
+// bf16 of K, so ROWB/32 MFMA K steps per stage).
+//
+// LDS rows hold ROWB/16 chunks of 16 bytes; chunk c of row r sits at
+// r*CH + (c ^ key(r)). The key changes so that the 16 lanes one ds_read_b128
+// serves together (16 consecutive rows, one logical chunk) land in 16 distinct
+// 16-byte bank groups of a 256-byte bank row: (r >> 2) & 3 for 64-byte rows,
+// (r >> 1) & 7 for 128-byte rows.
+template <int BM_, int BN_, int WM_, int STAGES_, int ROWB_>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, STAGES = STAGES_;
+    static constexpr int ROWB = ROWB_, CH = ROWB / 16, KS = ROWB / 2, NKS = ROWB / 32;
+    static constexpr int ROWS_PER_COPY = 1024 / ROWB;
     static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 1 KB copies per wave
     static constexpr int B_INSTR = B_BYTES / 1024 / 4;
     static constexpr int L = A_INSTR + B_INSTR;
     static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    static_assert(TM == 4 && TN == 4, "128 x 128 per wave");
+    static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte rows");
+    static_assert(NKS % 2 == 0, "fragment sets alternate; the last K step uses set 1");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "fits gfx950 LDS");
-    static_assert(STAGES - 3 <= 3, "wait_barrier covers up to 3 newer tiles");
+    static_assert(STAGES >= 3 && STAGES - 3 <= 3, "pipeline depth");
+    __device__ static __forceinline__ int swz(int row, int chunk) {
+        const int key = ROWB == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+        return row * CH + (chunk ^ key);
+    }
 };
 
 }  // namespace dma
@@ -336,25 +377,15 @@ template <class C, bool GATHER>
 __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
     using namespace dma;
     constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES, TM = C::TM, TN = C::TN;
-    constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR;
+    constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR, NKS = C::NKS;
     extern __shared__ __attribute__((aligned(1024))) u32x4_t smem[];
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) u32x4_t*)smem));
 
-    const int n_tiles = (p.N + BN - 1) / BN;
-    const int total = p.m_blocks * n_tiles;
-    const int hw = blockIdx.x, xcd = hw & 7;
-    const int q8 = total >> 3, rem = total & 7;
-    const int tile = xcd * q8 + min(xcd, rem) + (hw >> 3);
-    const int per_group = p.group_m * n_tiles;
-    const int first_mb = (tile / per_group) * p.group_m;
-    const int rows_in_group = min(p.group_m, p.m_blocks - first_mb);
-    const int mb = first_mb + (tile % per_group) % rows_in_group;
-    const int nb = (tile % per_group) / rows_in_group;
-
-    const int npp = *p.npp;
+    TilePos tp;
+    if (!tile_of<BM, BN>(p, tp)) return;
+    const int mb = tp.mb, nb = tp.nb;
     const int64_t m0 = static_cast<int64_t>(mb) * BM;
-    if (m0 >= npp) return;
     const int e = p.expert_ids[mb];
     if (e < 0) return;
     const int n0 = nb * BN;
@@ -363,41 +394,41 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
     const int r32 = lane & 31, half = lane >> 5;
     const int wm = wave / C::WN, wn = wave % C::WN;
 
-    // copy sources: a wave's copy i covers 16 rows; lane l takes row +l/4 and the
-    // logical chunk stored in LDS slot l%4
-    const int cp_row = lane >> 2, cp_slot = lane & 3;
+    // copy sources: a wave's copy i covers ROWS_PER_COPY rows; lane l takes row
+    // +l/CH and the logical chunk stored in LDS slot l%CH
+    const int cp_row = lane / C::CH, cp_slot = lane % C::CH;
     const uint8_t* a_src[A_INSTR];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
-        const int row = (wave * A_INSTR + i) * 16 + cp_row;
+        const int row = (wave * A_INSTR + i) * C::ROWS_PER_COPY + cp_row;
         int64_t src = m0 + row;
         if constexpr (GATHER) {
             const int r = p.sorted[m0 + row];
             src = r < p.R ? r / p.topk : 0;  // padding rows read token 0
         }
-        const int chunk = cp_slot ^ ((row >> 2) & 3);
+        const int chunk = C::swz(row, cp_slot) - row * C::CH;  // XOR is its own inverse
         a_src[i] = reinterpret_cast<const uint8_t*>(p.A) + src * p.lda_bytes + chunk * 16;
     }
     const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
     int32_t b_off[B_INSTR];
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
-        const int row = (wave * B_INSTR + i) * 16 + cp_row;
-        const int chunk = cp_slot ^ ((row >> 2) & 3);
+        const int row = (wave * B_INSTR + i) * C::ROWS_PER_COPY + cp_row;
+        const int chunk = C::swz(row, cp_slot) - row * C::CH;
         b_off[i] = min(n0 + row, p.N - 1) * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
     }
     // LDS destinations are wave-uniform: keep them in scalar registers
     const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds_base + wave * A_INSTR * 1024);
     const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_base + C::A_BYTES + wave * B_INSTR * 1024);
 
-    const int KT = p.K / 32;
+    const int KT = p.K / C::KS;
     // copy group j of K tile kt: groups of 4 (or 2) consecutive 1 KB copies
-    constexpr int AG = A_INSTR >= 4 ? 4 : A_INSTR, BG = 4;
+    constexpr int AG = A_INSTR >= 4 ? 4 : A_INSTR, BG = B_INSTR >= 4 ? 4 : B_INSTR;
     static_assert(A_INSTR % AG == 0 && B_INSTR % BG == 0, "whole copy groups");
     constexpr int NGROUPS = A_INSTR / AG + B_INSTR / BG;
     auto copy = [&](int kt, int j) {
         const uint32_t st = static_cast<uint32_t>(kt % STAGES) * C::STAGE_BYTES;
-        const int64_t off = static_cast<int64_t>(kt) * ROWB;
+        const int64_t off = static_cast<int64_t>(kt) * C::ROWB;
         if (j < A_INSTR / AG) {
             const uint8_t* g[AG];
 #pragma unroll
@@ -426,14 +457,19 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
     struct Frag {
         bf16x8_t a[TM], b[TN];
     };
+    auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * (C::STAGE_BYTES / 16); };
+    auto read_a = [&](int kt, int ks, Frag& f, int i) {
+        f.a[i] = __builtin_bit_cast(bf16x8_t, stage_ptr(kt)[C::swz(arow + i * 32 + r32, 2 * ks + half)]);
+    };
+    auto read_b = [&](int kt, int ks, Frag& f, int i) {
+        f.b[i] = __builtin_bit_cast(bf16x8_t,
+                                    (stage_ptr(kt) + C::A_BYTES / 16)[C::swz(brow + i * 32 + r32, 2 * ks + half)]);
+    };
     auto read = [&](int kt, int ks, Frag& f) {
-        const u32x4_t* sa = smem + (kt % STAGES) * (C::STAGE_BYTES / 16);
-        const u32x4_t* sb = sa + C::A_BYTES / 16;
 #pragma unroll
-        for (int i = 0; i < TN; ++i) {
-            f.b[i] = __builtin_bit_cast(bf16x8_t, sb[swz64(brow + i * 32 + r32, 2 * ks + half)]);
-            f.a[i] = __builtin_bit_cast(bf16x8_t, sa[swz64(arow + i * 32 + r32, 2 * ks + half)]);
-        }
+        for (int i = 0; i < TN; ++i) read_b(kt, ks, f, i);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) read_a(kt, ks, f, i);
     };
     auto mma = [&](const Frag& f) {
 #pragma unroll
@@ -442,28 +478,16 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
             for (int tm = 0; tm < TM; ++tm)
                 acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
     };
-    // one LDS fragment read per two MFMAs, so LDS traffic is spread over the MFMA time
-    auto interleave = [&]() {
-#pragma unroll
-        for (int i = 0; i < TM + TN; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-        }
-    };
+    // spread the TM + TN fragment reads of the next K step over this step's
+    // TM * TN MFMAs
+    auto interleave = [&]() { dma::interleave_step<0, TM + TN, TM * TN>(); };
 
-    // Pipeline per K tile kt (two K steps, F0 and F1):
-    //   read F1(kt) | MFMA F0(kt) | wait tile kt+1, barrier, copy tile kt+S-1 into
-    //   the stage of tile kt-1 | read F0(kt+1) | MFMA F1(kt)
-    // LDS reads always overlap MFMAs of the other fragment set, and S-2 tiles are
-    // in flight while tile kt is multiplied.
     // MFMAs of fragment set f, one weight row (tn) at a time. Between the rows
     // go the LDS reads of the next K tile's first fragment set (into g) and the
     // copies of tile `ck`: no long run of VMEM or LDS issues holds back the
     // MFMAs queued behind it (a wave issues in order), and every MFMA only
     // depends on LDS reads issued long before it.
     auto mma_and_prefetch = [&](const Frag& f, int next_kt, Frag& g, int ck) {
-        const u32x4_t* sa = smem + (next_kt % STAGES) * (C::STAGE_BYTES / 16);
-        const u32x4_t* sb = sa + C::A_BYTES / 16;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
@@ -471,8 +495,9 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
                 acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (next_kt >= 0) {
-                g.b[tn] = __builtin_bit_cast(bf16x8_t, sb[swz64(brow + tn * 32 + r32, half)]);
-                g.a[tn] = __builtin_bit_cast(bf16x8_t, sa[swz64(arow + tn * 32 + r32, half)]);
+                read_b(next_kt, 0, g, tn);
+#pragma unroll
+                for (int i = tn * TM / TN; i < (tn + 1) * TM / TN; ++i) read_a(next_kt, 0, g, i);
             }
             if (ck >= 0) {
 #pragma unroll
@@ -482,19 +507,24 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
         }
     };
 
-    // Pipeline per K tile kt (two K steps, fragment sets F0 and F1):
-    //   read F1(kt) interleaved with MFMA F0(kt) | wait tile kt+1, barrier |
-    //   MFMA F1(kt) interleaved with reads of F0(kt+1) and the copies of tile
-    //   kt+S-1 into the stage of tile kt-1
+    // Pipeline per K tile kt (NKS K steps, fragment sets alternating 0, 1):
+    //   for each K step but the last: read the next step's set while the MFMAs
+    //   of this step run;
+    //   last step: wait for tile kt+1, barrier, then its MFMAs interleaved with
+    //   the reads of tile kt+1's first set and the copies of tile kt+S-1 into
+    //   the stage of tile kt-1.
     // S-2 tiles are in flight while tile kt is multiplied.
-    Frag f0, f1;
+    Frag fs[2];
     for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
     wait_barrier<C::L>(min(STAGES - 2, KT - 1));
-    read(0, 0, f0);
+    read(0, 0, fs[0]);
     for (int kt = 0; kt < KT; ++kt) {
-        read(kt, 1, f1);
-        mma(f0);
-        interleave();
+#pragma unroll
+        for (int ks = 0; ks + 1 < NKS; ++ks) {
+            read(kt, ks + 1, fs[(ks + 1) & 1]);
+            mma(fs[ks & 1]);
+            interleave();
+        }
         int next = -1, ck = -1;
         if (kt + 1 < KT) {
             // tile kt+1 landed (tiles kt+2 .. kt+S-2 may still be in flight);
@@ -503,7 +533,7 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
             next = kt + 1;
             if (kt + STAGES - 1 < KT) ck = kt + STAGES - 1;
         }
-        mma_and_prefetch(f1, next, f0, ck);
+        mma_and_prefetch(fs[1], next, fs[0], ck);
     }
 
     uint8_t* c_base = reinterpret_cast<uint8_t*>(p.C);
@@ -525,6 +555,234 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 W8A8 (128x128 weight blocks, per-row per-128 activation groups), same
+// DMA pipeline. One K stage is 128 e4m3 = one scale group, multiplied in two
+// v_mfma_scale_f32_32x32x64_f8f6f4 steps into a partial accumulator that is
+// then added to the fp32 accumulator times (token scale x weight-block scale)
+// ("fused_moe.py analysis", "FP8 W8A8", block-wise). The token scales of each
+// stage are copied into LDS next to the tiles (one 4-byte gather copy per
+// wave, so the copy count stays uniform); each wave's weight-block scale is a
+// scalar load. No other vector loads run in the loop, so the explicit vmcnt
+// counts stay exact.
+namespace dma {
+
+__device__ __forceinline__ void copy4(const float* g, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(g)
+        : "memory");
+}
+
+}  // namespace dma
+
+template <class C, bool GATHER>
+__global__ __launch_bounds__(256) void expert_gemm_dma_fp8_kernel(GemmArgs p) {
+    using namespace dma;
+    constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES, TM = C::TM, TN = C::TN;
+    constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR;
+    constexpr int SCALE_OFF = C::A_BYTES + C::B_BYTES;     // token scales after the tiles
+    constexpr int STAGE = C::STAGE_BYTES + 1024;           // 4 waves x 256 bytes of scales
+    constexpr int L = C::L + 1;                             // copies per wave per stage
+    static_assert(C::ROWB == 128 && C::WM == 1 && BM == 128, "one 128-wide scale group per stage");
+    static_assert(C::WN * 0 + BN / 4 <= 128 && 128 % (BN / 4) == 0, "wave rows in one scale block");
+    extern __shared__ __attribute__((aligned(1024))) u32x4_t smem[];
+    const uint32_t lds_base = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) u32x4_t*)smem));
+
+    TilePos tp;
+    if (!tile_of<BM, BN>(p, tp)) return;
+    const int mb = tp.mb, nb = tp.nb;
+    const int64_t m0 = static_cast<int64_t>(mb) * BM;
+    const int e = p.expert_ids[mb];
+    if (e < 0) return;
+    const int n0 = nb * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, half = lane >> 5;
+
+    auto src_row_of = [&](int row) -> int64_t {
+        if constexpr (GATHER) {
+            const int r = p.sorted[m0 + row];
+            return r < p.R ? r / p.topk : 0;  // padding rows read token 0
+        } else {
+            return m0 + row;
+        }
+    };
+    const int cp_row = lane / C::CH, cp_slot = lane % C::CH;
+    const uint8_t* a_src[A_INSTR];
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i) {
+        const int row = (wave * A_INSTR + i) * C::ROWS_PER_COPY + cp_row;
+        const int chunk = C::swz(row, cp_slot) - row * C::CH;
+        a_src[i] = reinterpret_cast<const uint8_t*>(p.A) + src_row_of(row) * p.lda_bytes + chunk * 16;
+    }
+    const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
+    int32_t b_off[B_INSTR];
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i) {
+        const int row = (wave * B_INSTR + i) * C::ROWS_PER_COPY + cp_row;
+        const int chunk = C::swz(row, cp_slot) - row * C::CH;
+        b_off[i] = min(n0 + row, p.N - 1) * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
+    }
+    // token scales: wave w copies rows 32w .. 32w+31 (both lane halves copy the same rows)
+    const float* xs_src = p.a_scale + src_row_of(wave * 32 + r32) * p.scale_groups;
+    // this wave's weight rows lie in one 128-row scale block: a scalar pointer
+    // (read through the constant address space so that it becomes a scalar
+    // load, which leaves the vector memory counter to the copies)
+    using cfloat = __attribute__((address_space(4))) const float;
+    cfloat* ws_row = (cfloat*)(p.w_scale) + static_cast<int64_t>(e) * p.w_scale_expert +
+                     static_cast<int64_t>(min((n0 + wave * (BN / 4)) / 128, p.N / 128 - 1)) * p.scale_groups;
+
+    const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds_base + wave * A_INSTR * 1024);
+    const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_base + C::A_BYTES + wave * B_INSTR * 1024);
+    const uint32_t s_dst = __builtin_amdgcn_readfirstlane(lds_base + SCALE_OFF + wave * 256);
+
+    const int KT = p.K / 128;
+    constexpr int AG = A_INSTR >= 4 ? 4 : A_INSTR, BG = B_INSTR >= 4 ? 4 : B_INSTR;
+    static_assert(A_INSTR % AG == 0 && B_INSTR % BG == 0, "whole copy groups");
+    constexpr int NGROUPS = A_INSTR / AG + B_INSTR / BG + 1;  // + the scale copy
+    auto copy = [&](int kt, int j) {
+        const uint32_t st = static_cast<uint32_t>(kt % STAGES) * STAGE;
+        const int64_t off = static_cast<int64_t>(kt) * C::ROWB;
+        if (j < A_INSTR / AG) {
+            const uint8_t* g[AG];
+#pragma unroll
+            for (int i = 0; i < AG; ++i) g[i] = a_src[j * AG + i] + off;
+            copy_group<AG>(g, a_dst + st + j * AG * 1024);
+        } else if (j < A_INSTR / AG + B_INSTR / BG) {
+            const int jb = j - A_INSTR / AG;
+            const uint8_t* g[BG];
+#pragma unroll
+            for (int i = 0; i < BG; ++i) g[i] = w_base + b_off[jb * BG + i] + off;
+            copy_group<BG>(g, b_dst + st + jb * BG * 1024);
+        } else {
+            copy4(xs_src + kt, s_dst + st);
+        }
+    };
+    auto issue = [&](int kt) {
+#pragma unroll
+        for (int j = 0; j < NGROUPS; ++j) copy(kt, j);
+    };
+
+    f32x16_t acc[TN][TM], part[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x16_t{};
+
+    const int brow = wave * (BN / 4);
+    struct Frag {
+        i32x8_t a[TM], b[TN];
+    };
+    auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * (STAGE / 16); };
+    auto frag = [&](const u32x4_t* base, int row, int ks) {
+        const u32x4_t lo = base[C::swz(row, 4 * ks + 2 * half)];
+        const u32x4_t hi = base[C::swz(row, 4 * ks + 2 * half + 1)];
+        return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    auto read_a = [&](int kt, int ks, Frag& f, int i) { f.a[i] = frag(stage_ptr(kt), i * 32 + r32, ks); };
+    auto read_b = [&](int kt, int ks, Frag& f, int i) {
+        f.b[i] = frag(stage_ptr(kt) + C::A_BYTES / 16, brow + i * 32 + r32, ks);
+    };
+    auto read = [&](int kt, int ks, Frag& f) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i) read_b(kt, ks, f, i);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) read_a(kt, ks, f, i);
+    };
+    // formats 0/0 = e4m3 x e4m3; E8M0 scale 127 = 1.0
+    auto mma = [&](const Frag& f, bool first) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+                part[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.b[tn], f.a[tm], first ? f32x16_t{} : part[tn][tm], 0, 0, 0, 127, 0, 127);
+    };
+    // add the stage's partial sums with their scales; the token scale of row
+    // tm*32 + r32 was copied by wave tm into lane slot r32
+    auto fold = [&](int kt) {
+        const float sw = ws_row[kt];
+        const float* sx = reinterpret_cast<const float*>(stage_ptr(kt) + SCALE_OFF / 16);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const float sc = sx[tm * 64 + r32] * sw;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[tn][tm][r] += part[tn][tm][r] * sc;
+        }
+    };
+
+    // Pipeline per K stage kt (two MFMA steps). This kernel is bound by HBM,
+    // so the copies of stage kt+S-1 go out right after the barrier that ends
+    // every wave's use of stage kt-1 (whose slot they fill), before this
+    // stage's MFMAs: S-1 stages are in flight whenever a wave waits.
+    Frag f0, f1;
+    for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
+    for (int kt = 0; kt < KT; ++kt) {
+        wait_barrier<L>(min(STAGES - 2, KT - 1 - kt));
+        const bool more = kt + STAGES - 1 < KT;
+        read(kt, 0, f0);
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < NGROUPS / 2; ++j) copy(kt + STAGES - 1, j);
+        }
+        read(kt, 1, f1);
+        mma(f0, true);
+        if (more) {
+#pragma unroll
+            for (int j = NGROUPS / 2; j < NGROUPS; ++j) copy(kt + STAGES - 1, j);
+        }
+        mma(f1, false);
+        fold(kt);
+    }
+
+    uint8_t* c_base = reinterpret_cast<uint8_t*>(p.C);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int64_t row = m0 + tm * 32 + r32;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + brow + tn * 32 + 8 * q + 4 * half;
+                if (n < p.N) {
+                    const f32x16_t& a = acc[tn][tm];
+                    u32x2_t v{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+                    *reinterpret_cast<u32x2_t*>(c_base + row * p.ldc_bytes + n * 2) = v;
+                }
+            }
+        }
+    }
+}
+
+template <class C>
+hipError_t launch_dma_fp8(const GemmArgs& a, hipStream_t stream) {
+    const int n_tiles = (a.N + C::BN - 1) / C::BN;
+    const dim3 grid(static_cast<unsigned>(a.m_blocks * n_tiles));
+    const size_t lds = C::STAGES * (C::STAGE_BYTES + 1024);
+    const void* fn = a.sorted ? reinterpret_cast<const void*>(expert_gemm_dma_fp8_kernel<C, true>)
+                              : reinterpret_cast<const void*>(expert_gemm_dma_fp8_kernel<C, false>);
+    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+    if (a.sorted)
+        hipLaunchKernelGGL((expert_gemm_dma_fp8_kernel<C, true>), grid, dim3(256), lds, stream, a);
+    else
+        hipLaunchKernelGGL((expert_gemm_dma_fp8_kernel<C, false>), grid, dim3(256), lds, stream, a);
+    return hipGetLastError();
+}
+
 template <class C>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
     const int n_tiles = (a.N + C::BN - 1) / C::BN;
@@ -542,8 +800,14 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-using Dma128 = dma::Cfg<128, 512, 1, 4>;  // 128 tokens x 512 weight rows, 1 x 4 waves
-using Dma256 = dma::Cfg<256, 256, 2, 5>;  // 256 tokens x 256 weight rows, 2 x 2 waves
+// 128 tokens x 512 weight rows, 64-byte rows, 1 x 4 waves of 128 x 128
+using Dma128 = dma::Cfg<128, 512, 1, 4, 64>;
+// 128 tokens x 256 weight rows, 128-byte rows, 1 x 4 waves of 128 x 64
+using Dma128w = dma::Cfg<128, 256, 1, 3, 128>;
+// 256 tokens x 256 weight rows, 64-byte rows, 2 x 2 waves of 128 x 128
+using Dma256 = dma::Cfg<256, 256, 2, 5, 64>;
+// fp8: 128 tokens x 256 weight rows, 128 e4m3 of K per stage (one scale group)
+using Dma128f8 = dma::Cfg<128, 256, 1, 3, 128>;
 
 template <int BM, int BN, bool FP8>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
@@ -565,14 +829,14 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStre
         switch (block_m) {
             case 32: return launch_tile<32, 256, false>(a, stream);
             case 64: return launch_tile<64, 512, false>(a, stream);
-            case 128: return launch_dma<Dma128>(a, stream);
+            case 128: return DMA128_WIDE ? launch_dma<Dma128w>(a, stream) : launch_dma<Dma128>(a, stream);
             case 256: return launch_dma<Dma256>(a, stream);
         }
     } else {
         switch (block_m) {
             case 32: return launch_tile<32, 256, true>(a, stream);
             case 64: return launch_tile<64, 256, true>(a, stream);
-            case 128: return launch_tile<128, 256, true>(a, stream);
+            case 128: return launch_dma_fp8<Dma128f8>(a, stream);
         }
     }
     return hipErrorInvalidValue;

@@ -167,6 +167,11 @@ FP8_SMALL = [
     dict(M=150, H=512, I=256, E=7, topk=3, block_m=128, wdtype="fp8"),
     dict(M=40, H=256, I=384, E=5, topk=2, block_m=64, wdtype="fp8",
          apply_router_weight_on_input=True),
+    # tail tile of 128 valid weight rows in GEMM2 (N = H = 3 x 128), 3 K stages in GEMM1
+    dict(M=200, H=384, I=640, E=6, topk=2, block_m=128, wdtype="fp8"),
+    # a single K stage in GEMM2 (K = I = 128)
+    dict(M=90, H=256, I=128, E=4, topk=2, block_m=128, wdtype="fp8"),
+    dict(M=64, H=384, I=256, E=3, topk=2, block_m=32, wdtype="fp8"),
 ]
 
 
