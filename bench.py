@@ -109,10 +109,11 @@ class Step:
         self.o = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
         adt = torch.float8_e4m3fn if self.fp8 else torch.bfloat16
         self.z = torch.empty((cap, I), dtype=adt, device=dev)
-        self.zs = torch.empty((cap, I // 128), dtype=torch.float32, device=dev) if self.fp8 else None
+        self.zs = torch.empty((I // 128, cap), dtype=torch.float32, device=dev) if self.fp8 else None
         if self.fp8:
             self.xq = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
             self.xs = torch.empty((M, H // 128), dtype=torch.float32, device=dev)
+            self.xst = torch.empty((H // 128, cap), dtype=torch.float32, device=dev)
         self.w13 = d.w13q if self.fp8 else d.w13
         self.w2 = d.w2q if self.fp8 else d.w2
 
@@ -137,11 +138,13 @@ class Step:
         if self.fp8:
             lib.moe_quant_fp8_groups(m._ptr(d.x), self.p.M, self.p.H, m._ptr(self.xq),
                                      m._ptr(self.xs), s)
-            a1, a1s = self.xq, self.xs
+            a1, a1s = self.xq, self.xst
         ev[2].record()
         lib.moe_align_block_size(m._ptr(self.ids), self.p.M, self.p.topk, self.p.E,
                                  self.p.block_m, m._ptr(self.sorted), m._ptr(self.expert_ids),
                                  m._ptr(self.npp), m._ptr(self.inv), s)
+        if self.fp8:  # the activation scales follow the rows into the sorted order
+            m.moe_permute_scales(p, self.xs, self.sorted, self.npp, self.xst)
         ev[3].record()
         m.moe_expert_gemm(p, 1, a1, self.w13, self.sorted, self.expert_ids, self.npp, self.h,
                           a1s, d.w13s)

@@ -160,14 +160,16 @@ moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w1
  * analysis", 1.3 and "fused_moe_kernel"; "DeepGEMM FusedMoE on Blackwell",
  * 2.6.3 and 2.6.5): every block b of block_m rows uses expert expert_ids[b].
  *   which = 1: c[pos, 0:2I] = a[sorted_token_ids[pos] / topk, :] . w13[e]^T,
- *              a = x [M, H] (bf16, or e4m3 with a_scale [M, H/128]);
- *              padding rows (sorted id >= M*topk) read token 0 and are never
- *              consumed
- *   which = 2: c[pos, 0:H] = a[pos, :] . w2[e]^T, a = z [cap, I] (bf16, or
- *              e4m3 with a_scale [cap, I/128]); sorted_token_ids may be NULL
+ *              a = x [M, H] (bf16 or e4m3); padding rows (sorted id >= M*topk)
+ *              read token 0 and are never consumed
+ *   which = 2: c[pos, 0:H] = a[pos, :] . w2[e]^T, a = z [cap, I] (bf16 or
+ *              e4m3); sorted_token_ids may be NULL
  *   c [cap, N] bf16 out (fp32 accumulation, one rounding at the end).
- *   fp8: w_scale is [E, N/128, K/128]; every 128-wide K block's partial sum
- *   is multiplied by a_scale[row, block] * w_scale[e, n/128, block].
+ *   fp8: a_scale is [K/128, cap] fp32, group-major and indexed by sorted
+ *   position (a_scale[g * cap + pos] belongs to row pos of the layout; built
+ *   by moe_permute_scales for which = 1 and by moe_silu_and_mul for which = 2);
+ *   w_scale is [E, N/128, K/128]. Every 128-wide K block's partial sum is
+ *   multiplied by a_scale[block * cap + pos] * w_scale[e, n/128, block].
  */
 moe_status_t moe_expert_gemm(const moe_problem_t *p, int32_t which, const void *a,
                              const float *a_scale, const void *w, const float *w_scale,
@@ -180,12 +182,26 @@ moe_status_t moe_expert_gemm(const moe_problem_t *p, int32_t which, const void *
  * in fp32 (times topk_weights[item] when apply_router_weight_on_input),
  * padding rows set to 0.
  *   h [cap, 2I] bf16; z [cap, I] bf16 out, or for fp8 z [cap, I] e4m3 plus
- *   z_scale [cap, I/128] fp32 out (per-row, per-128 dynamic quantisation).
+ *   z_scale [I/128, cap] fp32 out (per-row, per-128 dynamic quantisation;
+ *   the scale of row pos and group g at z_scale[g * cap + pos]).
  */
 moe_status_t moe_silu_and_mul(const moe_problem_t *p, const void *h,
                               const int32_t *sorted_token_ids, const float *topk_weights,
                               const int32_t *num_tokens_post_padded, void *z, float *z_scale,
                               void *stream);
+
+/*
+ * The fp8 GEMM1 activation scales in the expert-sorted row order
+ * ("DeepGEMM FusedMoE on Blackwell", 2.5 and 2.6.2: the per-token group
+ * scales travel with the permuted rows, stored column-major for the GEMM):
+ *   scale  [M, H/128] fp32, as from moe_quant_fp8_groups(x)
+ *   out    [H/128, cap] fp32 out: out[g * cap + pos] = scale[sorted_token_ids[pos] / topk, g]
+ *          for pos < num_tokens_post_padded, 0 at padding positions; later
+ *          positions are not written
+ */
+moe_status_t moe_permute_scales(const moe_problem_t *p, const float *scale,
+                                const int32_t *sorted_token_ids,
+                                const int32_t *num_tokens_post_padded, float *out, void *stream);
 
 /*
  * Weighted unpermute-reduce ("DeepGEMM FusedMoE on Blackwell", 2.6.5,

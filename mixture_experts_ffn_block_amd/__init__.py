@@ -21,7 +21,7 @@ MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
 
 EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_quant_fp8_groups",
            "moe_workspace_bytes", "fused_experts", "moe_expert_gemm", "moe_silu_and_mul",
-           "moe_unpermute_reduce", "moe_status_string")
+           "moe_permute_scales", "moe_unpermute_reduce", "moe_status_string")
 
 
 class MoeProblem(ctypes.Structure):
@@ -59,11 +59,13 @@ def lib() -> ctypes.CDLL:
         PP = ctypes.POINTER(MoeProblem)
         L.moe_expert_gemm.argtypes = [PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_silu_and_mul.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_permute_scales.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_unpermute_reduce.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_status_string.argtypes = [_I32]
         L.moe_status_string.restype = ctypes.c_char_p
         for name in ("moe_topk", "moe_align_block_size", "moe_quant_fp8_groups", "fused_experts",
-                     "moe_expert_gemm", "moe_silu_and_mul", "moe_unpermute_reduce"):
+                     "moe_expert_gemm", "moe_silu_and_mul", "moe_permute_scales",
+                     "moe_unpermute_reduce"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -92,6 +94,23 @@ def _need(t: torch.Tensor, dtype, name: str):
     if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
         raise ValueError(f"{name}: expected a contiguous {dtype} device tensor, "
                          f"got {t.dtype} (contiguous={t.is_contiguous()}, device={t.device})")
+
+
+def _need_size(t: torch.Tensor | None, dtypes, numel: int, name: str):
+    """A device buffer the library will index up to `numel` elements of."""
+    if t is None:
+        raise ValueError(f"{name}: required")
+    if t.dtype not in dtypes or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected a contiguous device tensor of {dtypes}, got {t.dtype} "
+                         f"(contiguous={t.is_contiguous()}, device={t.device})")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: needs {numel} elements, has {t.numel()}")
+
+
+_F8 = (torch.float8_e4m3fn, torch.uint8)
+_BF = (torch.bfloat16, torch.int16, torch.uint16)
+_F32 = (torch.float32,)
+_I32T = (torch.int32,)
 
 
 # ----------------------------------------------------------------- entries ---
@@ -198,6 +217,19 @@ def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
                     a_scale: torch.Tensor | None = None, w_scale: torch.Tensor | None = None,
                     stream=None) -> torch.Tensor:
     """Grouped expert GEMM over the aligned layout (which = 1: x.w13^T, 2: z.w2^T)."""
+    fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128
+    cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
+    N, K = (2 * p.I, p.H) if which == 1 else (p.H, p.I)
+    _need_size(a, _F8 if fp8 else _BF, (p.M if which == 1 else cap) * K, "a")
+    _need_size(w, _F8 if fp8 else _BF, p.E * N * K, "w")
+    _need_size(expert_ids, _I32T, cap // p.block_m, "expert_ids")
+    _need_size(num_tokens_post_padded, _I32T, 1, "num_tokens_post_padded")
+    _need_size(c, _BF, cap * N, "c")
+    if which == 1:
+        _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
+    if fp8:
+        _need_size(a_scale, _F32, (K // 128) * cap, "a_scale [K/128, cap]")
+        _need_size(w_scale, _F32, p.E * (N // 128) * (K // 128), "w_scale")
     _check(lib().moe_expert_gemm(ctypes.byref(p), which, _ptr(a), _ptr(a_scale), _ptr(w),
                                  _ptr(w_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
                                  _ptr(num_tokens_post_padded), _ptr(c), _stream(stream)),
@@ -208,14 +240,42 @@ def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
 def moe_silu_and_mul(p: MoeProblem, h: torch.Tensor, sorted_token_ids: torch.Tensor,
                      topk_weights: torch.Tensor, num_tokens_post_padded: torch.Tensor,
                      z: torch.Tensor, z_scale: torch.Tensor | None = None, stream=None):
+    fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128
+    cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
+    _need_size(h, _BF, cap * 2 * p.I, "h")
+    _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
+    _need_size(topk_weights, _F32, p.M * p.topk, "topk_weights")
+    _need_size(num_tokens_post_padded, _I32T, 1, "num_tokens_post_padded")
+    _need_size(z, _F8 if fp8 else _BF, cap * p.I, "z")
+    if fp8:
+        _need_size(z_scale, _F32, (p.I // 128) * cap, "z_scale [I/128, cap]")
     _check(lib().moe_silu_and_mul(ctypes.byref(p), _ptr(h), _ptr(sorted_token_ids),
                                   _ptr(topk_weights), _ptr(num_tokens_post_padded), _ptr(z),
                                   _ptr(z_scale), _stream(stream)), "moe_silu_and_mul")
     return z, z_scale
 
 
+def moe_permute_scales(p: MoeProblem, scale: torch.Tensor, sorted_token_ids: torch.Tensor,
+                       num_tokens_post_padded: torch.Tensor, out: torch.Tensor, stream=None):
+    """Per-token fp8 group scales [M, H/128] -> group-major, sorted-order [H/128, cap]."""
+    cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
+    _need_size(scale, _F32, p.M * (p.H // 128), "scale")
+    _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
+    _need_size(num_tokens_post_padded, _I32T, 1, "num_tokens_post_padded")
+    _need_size(out, _F32, (p.H // 128) * cap, "out [H/128, cap]")
+    _check(lib().moe_permute_scales(ctypes.byref(p), _ptr(scale), _ptr(sorted_token_ids),
+                                    _ptr(num_tokens_post_padded), _ptr(out), _stream(stream)),
+           "moe_permute_scales")
+    return out
+
+
 def moe_unpermute_reduce(p: MoeProblem, o: torch.Tensor, inv_perm: torch.Tensor,
                          topk_weights: torch.Tensor, y: torch.Tensor, stream=None):
+    cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
+    _need_size(o, _BF, cap * p.H, "o")
+    _need_size(inv_perm, _I32T, p.M * p.topk, "inv_perm")
+    _need_size(topk_weights, _F32, p.M * p.topk, "topk_weights")
+    _need_size(y, _BF, p.M * p.H, "y")
     _check(lib().moe_unpermute_reduce(ctypes.byref(p), _ptr(o), _ptr(inv_perm),
                                       _ptr(topk_weights), _ptr(y), _stream(stream)),
            "moe_unpermute_reduce")

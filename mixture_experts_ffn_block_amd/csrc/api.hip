@@ -26,7 +26,7 @@ bool block_m_ok(int bm) { return bm == 16 || gemm_supported_block_m(bm); }
 
 struct Layout {
     int64_t cap, R;
-    int64_t sorted, expert_ids, npp, inv_perm, xq, xs, ho, z, zs, total;
+    int64_t sorted, expert_ids, npp, inv_perm, xq, xs, xst, ho, z, zs, total;
 };
 
 Layout layout(const moe_problem_t& p) {
@@ -42,10 +42,11 @@ Layout layout(const moe_problem_t& p) {
     L.inv_perm = take(L.R * 4);
     L.xq = fp8 ? take(p.M * p.H) : -1;
     L.xs = fp8 ? take(p.M * (p.H / 128) * 4) : -1;
+    L.xst = fp8 ? take(L.cap * (p.H / 128) * 4) : -1;  // GEMM1 scales by sorted position
     const int64_t h_bytes = L.cap * 2 * p.I * 2, o_bytes = L.cap * p.H * 2;
     L.ho = take(h_bytes > o_bytes ? h_bytes : o_bytes);
     L.z = take(L.cap * p.I * (fp8 ? 1 : 2));
-    L.zs = fp8 ? take(L.cap * (p.I / 128) * 4) : -1;
+    L.zs = fp8 ? take(L.cap * (p.I / 128) * 4) : -1;   // [I/128, cap]
     L.total = off;
     return L;
 }
@@ -102,6 +103,7 @@ hipError_t gemm_stage(const moe_problem_t& p, int which, const void* a, const fl
     g.group_m = kGroupM;
     if (fp8) {
         g.a_scale = a_scale;
+        g.a_scale_ld = cap;
         g.w_scale = w_scale;
         g.w_scale_expert = static_cast<int64_t>(N / 128) * (K / 128);
         g.scale_groups = K / 128;
@@ -120,6 +122,13 @@ hipError_t act_stage(const moe_problem_t& p, const void* h, const int32_t* sorte
                                    z_scale, sorted, weights, R, p.I, cap, npp, on_input, s);
     return launch_silu_mul_bf16(static_cast<const bf16_t*>(h), static_cast<bf16_t*>(z), sorted,
                                 weights, R, p.I, cap, npp, on_input, s);
+}
+
+hipError_t permute_stage(const moe_problem_t& p, const float* scale, const int32_t* sorted,
+                         const int32_t* npp, float* out, hipStream_t s) {
+    const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
+    return launch_permute_scales(scale, p.H / 128, p.topk, static_cast<int>(p.M * p.topk), sorted,
+                                 npp, cap, out, s);
 }
 
 hipError_t reduce_stage(const moe_problem_t& p, const void* o, const int32_t* inv_perm,
@@ -225,11 +234,16 @@ moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w1
                                reinterpret_cast<float*>(ws + L.xs), s);
         if (err != hipSuccess) return MOE_E_HIP;
         a1 = ws + L.xq;
-        a1_scale = reinterpret_cast<const float*>(ws + L.xs);
+        a1_scale = reinterpret_cast<const float*>(ws + L.xst);
     }
     err = launch_align(topk_ids, M * p->topk, p->E, p->block_m, L.cap, sorted, expert_ids, npp,
                        inv_perm, s);
     if (err != hipSuccess) return MOE_E_HIP;
+    if (fp8) {
+        err = permute_stage(*p, reinterpret_cast<const float*>(ws + L.xs), sorted, npp,
+                            reinterpret_cast<float*>(ws + L.xst), s);
+        if (err != hipSuccess) return MOE_E_HIP;
+    }
     err = gemm_stage(*p, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, s);
     if (err != hipSuccess) return MOE_E_HIP;
     err = act_stage(*p, ho, sorted, topk_weights, npp, z, reinterpret_cast<float*>(ws + L.zs), s);
@@ -268,6 +282,17 @@ moe_status_t moe_silu_and_mul(const moe_problem_t* p, const void* h,
     if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && !z_scale) return MOE_E_INVALID;
     return hip_status(act_stage(*p, h, sorted_token_ids, topk_weights, num_tokens_post_padded, z,
                                 z_scale, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute_scales(const moe_problem_t* p, const float* scale,
+                                const int32_t* sorted_token_ids,
+                                const int32_t* num_tokens_post_padded, float* out, void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->M == 0) return MOE_OK;
+    if (!scale || !sorted_token_ids || !num_tokens_post_padded || !out) return MOE_E_INVALID;
+    return hip_status(permute_stage(*p, scale, sorted_token_ids, num_tokens_post_padded, out,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_unpermute_reduce(const moe_problem_t* p, const void* o, const int32_t* inv_perm,

@@ -64,11 +64,13 @@ __device__ __forceinline__ u32x2_t quant_group8(const float (&v)[8], float* scal
 }
 
 // SiLU-and-mul, then per-row per-128 fp8 quantisation of the fp32 result.
-// One wavefront per (row, 4 groups).
+// One wavefront per (row, 4 groups). The scales are stored group-major,
+// zs[g * cap + pos], so that the GEMM reads a block's 128 row scales of one
+// group as one contiguous run.
 __global__ __launch_bounds__(256) void silu_mul_fp8_kernel(
     const bf16_t* __restrict__ h, uint8_t* __restrict__ zq, float* __restrict__ zs,
     const int32_t* __restrict__ sorted, const float* __restrict__ weights, int R, int I,
-    const int32_t* __restrict__ npp_ptr, int on_input) {
+    int64_t cap, const int32_t* __restrict__ npp_ptr, int on_input) {
     const int64_t pos = blockIdx.y;
     if (pos >= *npp_ptr) return;
     const int lane = threadIdx.x & 63;
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(256) void silu_mul_fp8_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-    const u32x2_t q = quant_group8(v, zs + pos * (I / 128) + i0 / 128, (lane & 15) == 0);
+    const u32x2_t q = quant_group8(v, zs + (i0 / 128) * cap + pos, (lane & 15) == 0);
     *reinterpret_cast<u32x2_t*>(zq + pos * I + i0) = q;
 }
 
@@ -111,6 +113,22 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict
     }
     const u32x2_t qq = quant_group8(v, scale + row * (cols / 128) + c0 / 128, (lane & 15) == 0);
     *reinterpret_cast<u32x2_t*>(q + row * cols + c0) = qq;
+}
+
+// Activation scales of GEMM1 in its row order: out[g * cap + pos] is the
+// scale of the token of sorted position pos (0 for padding positions), from
+// the per-token scales scale[token, g]. Positions >= npp are not written.
+// One thread per position; consecutive threads write consecutive floats.
+__global__ __launch_bounds__(256) void permute_scales_kernel(const float* __restrict__ scale,
+                                                             int groups, int topk, int R,
+                                                             const int32_t* __restrict__ sorted,
+                                                             const int32_t* __restrict__ npp_ptr,
+                                                             int64_t cap, float* __restrict__ out) {
+    const int64_t pos = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (pos >= *npp_ptr) return;
+    const int r = sorted[pos];
+    const float* src = r < R ? scale + static_cast<int64_t>(r / topk) * groups : nullptr;
+    for (int g = 0; g < groups; ++g) out[g * cap + pos] = src ? src[g] : 0.0f;
 }
 
 // ------------------------------------------------------------------ reduce --
@@ -157,7 +175,16 @@ hipError_t launch_silu_mul_fp8(const bf16_t* h, uint8_t* zq, float* zs, const in
                                const int32_t* npp, int on_input, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(ceil_div(I, 2048)), static_cast<unsigned>(cap));
     hipLaunchKernelGGL(silu_mul_fp8_kernel, grid, dim3(256), 0, stream, h, zq, zs, sorted,
-                       weights, R, I, npp, on_input);
+                       weights, R, I, cap, npp, on_input);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_scales(const float* scale, int groups, int topk, int R,
+                                 const int32_t* sorted, const int32_t* npp, int64_t cap,
+                                 float* out, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(cap, 256)));
+    hipLaunchKernelGGL(permute_scales_kernel, grid, dim3(256), 0, stream, scale, groups, topk, R,
+                       sorted, npp, cap, out);
     return hipGetLastError();
 }
 

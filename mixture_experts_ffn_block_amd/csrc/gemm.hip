@@ -67,6 +67,42 @@ struct Tile {
     static_assert(kLdsBytes <= 160 * 1024, "fits gfx950 LDS");
 };
 
+// ---- epilogue through LDS, shared by the copy-ring kernels -----------------
+// A wave's accumulators cover TM*32 token rows x TN*32 weight columns, a lane
+// holding 4 consecutive columns of one row per register quad (the swapped
+// MFMA orientation). Stored straight to C, every store instruction would
+// write 16 bytes into each of 32 rows; staged through the wave's own LDS
+// area first, every store instruction writes whole 128-byte lines (8 lanes x
+// 16 bytes per row). `stage` holds TM*32 rows of TN*64 + 16 bytes (the pad
+// spreads consecutive rows over the banks). col0 and N are multiples of 64,
+// so each 64-column chunk is wholly inside or outside C.
+template <int TM, int TN>
+__device__ __forceinline__ void store_block(const f32x16_t (&acc)[TN][TM], uint8_t* stage,
+                                            uint8_t* c, int64_t row0, int col0, int64_t ldc_bytes,
+                                            int N, int lane) {
+    constexpr int PITCH = TN * 64 + 16, CH = TN * 4, RPP = 64 / CH;
+    const int r32 = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x16_t& a = acc[tn][tm];
+                const int col = tn * 32 + 8 * q + 4 * half;
+                *reinterpret_cast<u32x2_t*>(stage + (tm * 32 + r32) * PITCH + col * 2) =
+                    u32x2_t{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+            }
+    const int ch = lane % CH;
+    const int col = col0 + ch * 8;
+#pragma unroll
+    for (int pass = 0; pass < TM * 32 / RPP; ++pass) {
+        const int row = pass * RPP + lane / CH;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + row * PITCH + ch * 16);
+        if (col < N) *reinterpret_cast<u32x4_t*>(c + (row0 + row) * ldc_bytes + col * 2) = v;
+    }
+}
+
 // ---- tile scheduling, shared by the LDS-tiled kernels ---------------------
 // The grid is sized for the worst-case number of expert blocks; only the
 // first npp / BM blocks hold rows, so the logical tiles are those of the real
@@ -142,7 +178,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs p) {
     const float* ws_row = nullptr;
     if constexpr (FP8) {
 #pragma unroll
-        for (int tm = 0; tm < T::TM; ++tm) xs_row[tm] = p.a_scale + src_row_of(tm * 32 + r32) * p.scale_groups;
+        for (int tm = 0; tm < T::TM; ++tm) xs_row[tm] = p.a_scale + m0 + tm * 32 + r32;  // group-major
         // a wave's WN (<= 128, dividing 128) weight rows lie in one 128-row scale
         // block; waves wholly past N (tail tile) read the last block, unused
         static_assert(128 % T::WN == 0, "wave columns within one scale block");
@@ -198,7 +234,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs p) {
         } else {
             float sx[T::TM];
 #pragma unroll
-            for (int tm = 0; tm < T::TM; ++tm) sx[tm] = xs_row[tm][kt];
+            for (int tm = 0; tm < T::TM; ++tm) sx[tm] = xs_row[tm][kt * p.a_scale_ld];
             const float sw = ws_row[kt];
             f32x16_t part[T::TN][T::TM];
 #pragma unroll
@@ -556,42 +592,70 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// fp8 W8A8 (128x128 weight blocks, per-row per-128 activation groups), same
-// DMA pipeline. One K stage is 128 e4m3 = one scale group, multiplied in two
-// v_mfma_scale_f32_32x32x64_f8f6f4 steps into a partial accumulator that is
-// then added to the fp32 accumulator times (token scale x weight-block scale)
-// ("fused_moe.py analysis", "FP8 W8A8", block-wise). The token scales of each
-// stage are copied into LDS next to the tiles (one 4-byte gather copy per
-// wave, so the copy count stays uniform); each wave's weight-block scale is a
-// scalar load. No other vector loads run in the loop, so the explicit vmcnt
-// counts stay exact.
-namespace dma {
+// fp8 W8A8 (e4m3 weights with one scale per 128x128 block, activations with
+// one scale per row and 128 columns; "fused_moe.py analysis", "FP8 W8A8",
+// block-wise; "DeepGEMM FusedMoE on Blackwell", 1.1 step 4 and 2.5). One K
+// stage is 128 e4m3 of every row, i.e. one scale group: two
+// v_mfma_scale_f32_32x32x64_f8f6f4 steps (unit block scales) sum it into a
+// partial tile, which is then added to the fp32 accumulator times
+// token scale x weight-block scale.
+//
+// Same direct-to-LDS copy ring as the bf16 kernel, with two waves per SIMD
+// (eight per workgroup): the per-stage scaling is vector-ALU work that one
+// wave does while the other wave of its SIMD keeps the matrix core busy.
+// With 64 x 64 outputs per wave every accumulator stays in an
+// architectural register, so the scaling needs no accumulator-register moves.
+// The activation scales are stored group-major by sorted position, so the
+// 128 row scales of a stage are 512 contiguous bytes, which wave 0 copies
+// into the stage's slot with one more 1 KB copy (lanes 32..63 repeat lanes
+// 0..31). The tile's weight-block scales, BN/128 rows of K/128 values, are
+// loaded into LDS once before the ring starts. The loop issues no other
+// vector memory instruction, so the explicit vmcnt counts stay exact.
+namespace f8 {
 
-__device__ __forceinline__ void copy4(const float* g, uint32_t lds) {
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = WM_ * WN_, STAGES = STAGES_;
+    static constexpr int ROWB = 128, CH = 8, ROWS_PER_COPY = 8;
+    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    static constexpr int SCALE_OFF = A_BYTES + B_BYTES, STAGE_BYTES = SCALE_OFF + 1024;
+    static constexpr int A_INSTR = A_BYTES / 1024 / NW, B_INSTR = B_BYTES / 1024 / NW;
+    static constexpr int L = A_INSTR + B_INSTR;  // copies per wave per stage (wave 0: L + 1)
+    static constexpr int WBLOCKS = BN / 128;     // weight-scale rows per tile
+    static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+    static_assert(A_INSTR * NW * 1024 == A_BYTES && B_INSTR * NW * 1024 == B_BYTES, "whole copies");
+    static_assert((A_INSTR == 2 || A_INSTR == 4) && (B_INSTR == 2 || B_INSTR % 4 == 0), "copy groups");
+    static_assert(BM == 128, "one 1 KB copy carries the 128 row scales");
+    static_assert(BN % 128 == 0 && 128 % (BN / WN) == 0, "a wave's weight rows lie in one 128-row scale block");
+    static_assert(STAGES >= 3 && STAGES * STAGE_BYTES <= 150 * 1024, "fits gfx950 LDS with the scale table");
+    static_assert(STAGE_BYTES % 1024 == 0, "stages keep the 1 KB swizzle alignment");
+    static_assert(3 * (L + 1) <= 63, "vmcnt range");
+    static_assert(NW * (BM / WM) * (BN / WN * 2 + 16) <= STAGES * STAGE_BYTES, "epilogue staging fits the ring");
+    // 128-byte rows, 16-byte chunks XOR-swizzled by (row / 2) % 8
+    __device__ static __forceinline__ int swz(int row, int chunk) { return row * CH + (chunk ^ ((row >> 1) & 7)); }
+};
+
+// one 1 KB copy (16 bytes per lane) to LDS address `lds`
+__device__ __forceinline__ void copy1(const void* g, uint32_t lds) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dword %2, off\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "s"(lds), "v"(g)
         : "memory");
 }
 
-}  // namespace dma
+}  // namespace f8
 
 template <class C, bool GATHER>
-__global__ __launch_bounds__(256) void expert_gemm_dma_fp8_kernel(GemmArgs p) {
-    using namespace dma;
+__global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p) {
     constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES, TM = C::TM, TN = C::TN;
-    constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR;
-    constexpr int SCALE_OFF = C::A_BYTES + C::B_BYTES;     // token scales after the tiles
-    constexpr int STAGE = C::STAGE_BYTES + 1024;           // 4 waves x 256 bytes of scales
-    constexpr int L = C::L + 1;                             // copies per wave per stage
-    static_assert(C::ROWB == 128 && C::WM == 1 && BM == 128, "one 128-wide scale group per stage");
-    static_assert(C::WN * 0 + BN / 4 <= 128 && 128 % (BN / 4) == 0, "wave rows in one scale block");
+    constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR, L = C::L;
+    constexpr int WROWS_M = BM / C::WM, WROWS_N = BN / C::WN;
     extern __shared__ __attribute__((aligned(1024))) u32x4_t smem[];
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) u32x4_t*)smem));
@@ -606,6 +670,7 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_fp8_kernel(GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const int r32 = lane & 31, half = lane >> 5;
 
     auto src_row_of = [&](int row) -> int64_t {
@@ -632,44 +697,48 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_fp8_kernel(GemmArgs p) {
         const int chunk = C::swz(row, cp_slot) - row * C::CH;
         b_off[i] = min(n0 + row, p.N - 1) * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
     }
-    // token scales: wave w copies rows 32w .. 32w+31 (both lane halves copy the same rows)
-    const float* xs_src = p.a_scale + src_row_of(wave * 32 + r32) * p.scale_groups;
-    // this wave's weight rows lie in one 128-row scale block: a scalar pointer
-    // (read through the constant address space so that it becomes a scalar
-    // load, which leaves the vector memory counter to the copies)
-    using cfloat = __attribute__((address_space(4))) const float;
-    cfloat* ws_row = (cfloat*)(p.w_scale) + static_cast<int64_t>(e) * p.w_scale_expert +
-                     static_cast<int64_t>(min((n0 + wave * (BN / 4)) / 128, p.N / 128 - 1)) * p.scale_groups;
+    // wave 0's scale copy: floats 4*(lane % 32) .. +3 of the stage's 128 row scales
+    const float* sc_src = p.a_scale + m0 + (lane & 31) * 4;
 
     const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds_base + wave * A_INSTR * 1024);
     const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_base + C::A_BYTES + wave * B_INSTR * 1024);
-    const uint32_t s_dst = __builtin_amdgcn_readfirstlane(lds_base + SCALE_OFF + wave * 256);
+    const uint32_t s_dst = lds_base + C::SCALE_OFF;
 
+    // the tile's weight-block scales: wtab[b * KT + k] = w_scale[e, n0/128 + b, k]
+    // (blocks past N repeat the last one; their rows are never stored)
     const int KT = p.K / 128;
-    constexpr int AG = A_INSTR >= 4 ? 4 : A_INSTR, BG = B_INSTR >= 4 ? 4 : B_INSTR;
-    static_assert(A_INSTR % AG == 0 && B_INSTR % BG == 0, "whole copy groups");
-    constexpr int NGROUPS = A_INSTR / AG + B_INSTR / BG + 1;  // + the scale copy
+    float* wtab = reinterpret_cast<float*>(smem + STAGES * (C::STAGE_BYTES / 16));
+    for (int i = tid; i < C::WBLOCKS * KT; i += C::NW * 64) {
+        const int b = min(n0 / 128 + i / KT, p.N / 128 - 1);
+        wtab[i] = p.w_scale[static_cast<int64_t>(e) * p.w_scale_expert + static_cast<int64_t>(b) * p.scale_groups + i % KT];
+    }
+    __syncthreads();
+
+    constexpr int AG = A_INSTR, BG = B_INSTR >= 4 ? 4 : B_INSTR;
+    constexpr int NGROUPS = 1 + B_INSTR / BG + 1;  // the last group is wave 0's scale copy
     auto copy = [&](int kt, int j) {
-        const uint32_t st = static_cast<uint32_t>(kt % STAGES) * STAGE;
+        const uint32_t st = static_cast<uint32_t>(kt % STAGES) * C::STAGE_BYTES;
         const int64_t off = static_cast<int64_t>(kt) * C::ROWB;
-        if (j < A_INSTR / AG) {
+        if (j == 0) {
             const uint8_t* g[AG];
 #pragma unroll
-            for (int i = 0; i < AG; ++i) g[i] = a_src[j * AG + i] + off;
-            copy_group<AG>(g, a_dst + st + j * AG * 1024);
-        } else if (j < A_INSTR / AG + B_INSTR / BG) {
-            const int jb = j - A_INSTR / AG;
+            for (int i = 0; i < AG; ++i) g[i] = a_src[i] + off;
+            dma::copy_group<AG>(g, a_dst + st);
+        } else if (j < NGROUPS - 1) {
+            const int jb = j - 1;
             const uint8_t* g[BG];
 #pragma unroll
             for (int i = 0; i < BG; ++i) g[i] = w_base + b_off[jb * BG + i] + off;
-            copy_group<BG>(g, b_dst + st + jb * BG * 1024);
-        } else {
-            copy4(xs_src + kt, s_dst + st);
+            dma::copy_group<BG>(g, b_dst + st + jb * BG * 1024);
+        } else if (wave == 0) {
+            f8::copy1(sc_src + static_cast<int64_t>(kt) * p.a_scale_ld, s_dst + st);
         }
     };
-    auto issue = [&](int kt) {
-#pragma unroll
-        for (int j = 0; j < NGROUPS; ++j) copy(kt, j);
+    auto wait_barrier = [&](int newer) {
+        if (wave == 0)
+            dma::wait_barrier<L + 1>(newer);
+        else
+            dma::wait_barrier<L>(newer);
     };
 
     f32x16_t acc[TN][TM], part[TN][TM];
@@ -678,28 +747,26 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_fp8_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = f32x16_t{};
 
-    const int brow = wave * (BN / 4);
+    const int arow = wm * WROWS_M, brow = wn * WROWS_N;
     struct Frag {
         i32x8_t a[TM], b[TN];
     };
-    auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * (STAGE / 16); };
+    auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * (C::STAGE_BYTES / 16); };
+    // lane (r32, half) holds 32 consecutive bytes of K: chunks 4ks + 2half, +1
     auto frag = [&](const u32x4_t* base, int row, int ks) {
         const u32x4_t lo = base[C::swz(row, 4 * ks + 2 * half)];
         const u32x4_t hi = base[C::swz(row, 4 * ks + 2 * half + 1)];
         return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
-    auto read_a = [&](int kt, int ks, Frag& f, int i) { f.a[i] = frag(stage_ptr(kt), i * 32 + r32, ks); };
-    auto read_b = [&](int kt, int ks, Frag& f, int i) {
-        f.b[i] = frag(stage_ptr(kt) + C::A_BYTES / 16, brow + i * 32 + r32, ks);
-    };
     auto read = [&](int kt, int ks, Frag& f) {
+        const u32x4_t* st = stage_ptr(kt);
 #pragma unroll
-        for (int i = 0; i < TN; ++i) read_b(kt, ks, f, i);
+        for (int i = 0; i < TN; ++i) f.b[i] = frag(st + C::A_BYTES / 16, brow + i * 32 + r32, ks);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) read_a(kt, ks, f, i);
+        for (int i = 0; i < TM; ++i) f.a[i] = frag(st, arow + i * 32 + r32, ks);
     };
-    // formats 0/0 = e4m3 x e4m3; E8M0 scale 127 = 1.0
+    // formats 0/0 = e4m3 x e4m3; E8M0 block scale 127 = 1.0
     auto mma = [&](const Frag& f, bool first) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
@@ -708,14 +775,13 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_fp8_kernel(GemmArgs p) {
                 part[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     f.b[tn], f.a[tm], first ? f32x16_t{} : part[tn][tm], 0, 0, 0, 127, 0, 127);
     };
-    // add the stage's partial sums with their scales; the token scale of row
-    // tm*32 + r32 was copied by wave tm into lane slot r32
+    // scale of tile row arow + tm*32 + r32 times the wave's weight-block scale
     auto fold = [&](int kt) {
-        const float sw = ws_row[kt];
-        const float* sx = reinterpret_cast<const float*>(stage_ptr(kt) + SCALE_OFF / 16);
+        const float* sx = reinterpret_cast<const float*>(stage_ptr(kt) + C::SCALE_OFF / 16);
+        const float sw = wtab[(brow / 128) * KT + kt];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-            const float sc = sx[tm * 64 + r32] * sw;
+            const float sc = sx[arow + tm * 32 + r32] * sw;
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
@@ -723,63 +789,49 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_fp8_kernel(GemmArgs p) {
         }
     };
 
-    // Pipeline per K stage kt (two MFMA steps). This kernel is bound by HBM,
-    // so the copies of stage kt+S-1 go out right after the barrier that ends
-    // every wave's use of stage kt-1 (whose slot they fill), before this
-    // stage's MFMAs: S-1 stages are in flight whenever a wave waits.
+    // Per K stage kt: wait until stage kt has landed and every wave is done
+    // with stage kt-1, then send the copies of stage kt+S-1 into kt-1's slot
+    // before this stage's MFMAs, so S-1 stages are in flight at every wait.
     Frag f0, f1;
-    for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
+    for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt)
+#pragma unroll
+        for (int j = 0; j < NGROUPS; ++j) copy(kt, j);
     for (int kt = 0; kt < KT; ++kt) {
-        wait_barrier<L>(min(STAGES - 2, KT - 1 - kt));
+        wait_barrier(min(STAGES - 2, KT - 1 - kt));
         const bool more = kt + STAGES - 1 < KT;
         read(kt, 0, f0);
-        if (more) {
-#pragma unroll
-            for (int j = 0; j < NGROUPS / 2; ++j) copy(kt + STAGES - 1, j);
-        }
+        if (more) copy(kt + STAGES - 1, 0);
         read(kt, 1, f1);
         mma(f0, true);
         if (more) {
 #pragma unroll
-            for (int j = NGROUPS / 2; j < NGROUPS; ++j) copy(kt + STAGES - 1, j);
+            for (int j = 1; j < NGROUPS; ++j) copy(kt + STAGES - 1, j);
         }
         mma(f1, false);
         fold(kt);
     }
 
-    uint8_t* c_base = reinterpret_cast<uint8_t*>(p.C);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        const int64_t row = m0 + tm * 32 + r32;
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + brow + tn * 32 + 8 * q + 4 * half;
-                if (n < p.N) {
-                    const f32x16_t& a = acc[tn][tm];
-                    u32x2_t v{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
-                    *reinterpret_cast<u32x2_t*>(c_base + row * p.ldc_bytes + n * 2) = v;
-                }
-            }
-        }
-    }
+    // every wave is past its last LDS read of the ring: reuse it for the epilogue
+    __syncthreads();
+    store_block<TM, TN>(acc, reinterpret_cast<uint8_t*>(smem) + wave * (TM * 32 * (TN * 64 + 16)),
+                        reinterpret_cast<uint8_t*>(p.C), m0 + arow, n0 + brow, p.ldc_bytes, p.N, lane);
 }
 
 template <class C>
-hipError_t launch_dma_fp8(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_fp8(const GemmArgs& a, hipStream_t stream) {
     const int n_tiles = (a.N + C::BN - 1) / C::BN;
     const dim3 grid(static_cast<unsigned>(a.m_blocks * n_tiles));
-    const size_t lds = C::STAGES * (C::STAGE_BYTES + 1024);
-    const void* fn = a.sorted ? reinterpret_cast<const void*>(expert_gemm_dma_fp8_kernel<C, true>)
-                              : reinterpret_cast<const void*>(expert_gemm_dma_fp8_kernel<C, false>);
+    const size_t lds = C::STAGES * C::STAGE_BYTES + static_cast<size_t>(C::WBLOCKS) * (a.K / 128) * 4;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const void* fn = a.sorted ? reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, true>)
+                              : reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, false>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          static_cast<int>(lds));
     if (err != hipSuccess) return err;
     if (a.sorted)
-        hipLaunchKernelGGL((expert_gemm_dma_fp8_kernel<C, true>), grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, true>), grid, dim3(C::NW * 64), lds, stream, a);
     else
-        hipLaunchKernelGGL((expert_gemm_dma_fp8_kernel<C, false>), grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, false>), grid, dim3(C::NW * 64), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -806,8 +858,8 @@ using Dma128 = dma::Cfg<128, 512, 1, 4, 64>;
 using Dma128w = dma::Cfg<128, 256, 1, 3, 128>;
 // 256 tokens x 256 weight rows, 64-byte rows, 2 x 2 waves of 128 x 128
 using Dma256 = dma::Cfg<256, 256, 2, 5, 64>;
-// fp8: 128 tokens x 256 weight rows, 128 e4m3 of K per stage (one scale group)
-using Dma128f8 = dma::Cfg<128, 256, 1, 3, 128>;
+// fp8: 128 tokens x 256 weight rows, 2 x 4 waves of 64 x 64, 3 stages
+using Fp8x128 = f8::Cfg<128, 256, 2, 4, 3>;
 
 template <int BM, int BN, bool FP8>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
@@ -836,7 +888,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStre
         switch (block_m) {
             case 32: return launch_tile<32, 256, true>(a, stream);
             case 64: return launch_tile<64, 256, true>(a, stream);
-            case 128: return launch_dma_fp8<Dma128f8>(a, stream);
+            case 128: return launch_fp8<Fp8x128>(a, stream);
         }
     }
     return hipErrorInvalidValue;

@@ -25,7 +25,8 @@ struct GemmArgs {
     int m_blocks;              // row blocks in the grid (capacity / block_m)
     int group_m;               // row blocks per scheduling group
     // fp8 only
-    const float* a_scale;      // per row of A, K/128 groups
+    const float* a_scale;      // [K/128, a_scale_ld] group-major, by sorted position
+    int64_t a_scale_ld;        // floats per group row of a_scale (the capacity)
     const float* w_scale;      // [E, N/128, K/128]
     int64_t w_scale_expert;    // floats per expert of w_scale
     int scale_groups;          // K / 128
@@ -43,8 +44,11 @@ hipError_t launch_silu_mul_bf16(const bf16_t* h, bf16_t* z, const int32_t* sorte
                                 const int32_t* npp, int on_input, hipStream_t stream);
 hipError_t launch_silu_mul_fp8(const bf16_t* h, uint8_t* zq, float* zs, const int32_t* sorted,
                                const float* weights, int R, int I, int64_t cap,
-                               const int32_t* npp, int on_input, hipStream_t stream);
+                               const int32_t* npp, int on_input, hipStream_t stream);  // zs [I/128, cap]
 hipError_t launch_quant_fp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q, float* scale,
                             hipStream_t stream);
+hipError_t launch_permute_scales(const float* scale, int groups, int topk, int R,
+                                 const int32_t* sorted, const int32_t* npp, int64_t cap,
+                                 float* out, hipStream_t stream);
 hipError_t launch_reduce(const bf16_t* o, const int32_t* inv_perm, const float* weights, int64_t M,
                          int k, int H, int use_weights, bf16_t* y, hipStream_t stream);

@@ -142,6 +142,79 @@ def test_quant_fp8_bit_exact():
     assert np.array_equal(bits8(q), q_ref)
 
 
+def test_permute_scales_bit_exact():
+    # per-token group scales follow their rows into the expert-sorted order,
+    # stored group-major; padding positions get 0, later positions untouched
+    M, k, E, B, H = 300, 4, 16, 128, 640
+    g = torch.Generator().manual_seed(5)
+    ids = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(M)]).to(torch.int32)
+    scale = torch.rand(M, H // 128, generator=g) + 0.5
+    prob = moe.make_problem(M, H, 256, E, k, B, moe.MOE_W_FP8_E4M3_BLOCK128)
+    s, e, npp, inv = moe.moe_align_block_size(ids.to(DEV), E, B)
+    cap = s.numel()
+    out = torch.full((H // 128, cap), float("nan"), device=DEV)
+    moe.moe_permute_scales(prob, scale.to(DEV), s, npp, out)
+    sn, n = s.cpu().numpy(), int(npp.item())
+    ref = np.zeros((H // 128, n), np.float32)
+    real = sn[:n] < M * k
+    ref[:, real] = scale.numpy()[sn[:n][real] // k].T
+    o = out.cpu().numpy()
+    assert n < cap and np.array_equal(o[:, :n], ref)
+    assert np.all(np.isnan(o[:, n:]))
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(M=150, H=512, I=256, E=7, topk=3, block_m=128, wdtype="fp8"),
+    dict(M=64, H=384, I=256, E=3, topk=2, block_m=32, wdtype="fp8"),
+    dict(M=40, H=256, I=384, E=5, topk=2, block_m=64, wdtype="fp8", apply_router_weight_on_input=True),
+    dict(M=130, H=640, I=384, E=5, topk=2, block_m=128),
+    dict(M=130, H=640, I=384, E=5, topk=2, block_m=16),
+    dict(M=300, H=512, I=384, E=3, topk=2, block_m=256),
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_stages_compose_to_fused(cfg):
+    # the exported stage entry points, launched one by one, give fused_experts' bits
+    p = synth.Problem(**cfg)
+    log(f"stages {cfg}")
+    d = to_dev(synth.make_inputs(p, "cpu"))
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    y_fused = run_layer(p, d, ids, w)
+    fp8 = p.wdtype == "fp8"
+    prob = moe.make_problem(p.M, p.H, p.I, p.E, p.topk, p.block_m,
+                            moe.MOE_W_FP8_E4M3_BLOCK128 if fp8 else moe.MOE_W_BF16, p.apply_router_weight_on_input)
+    s, e, npp, inv = moe.moe_align_block_size(ids, p.E, p.block_m)
+    cap = s.numel()
+    a1, a1s = d.x, None
+    if fp8:
+        a1, xs = moe.moe_quant_fp8_groups(d.x)
+        a1s = torch.empty((p.H // 128, cap), dtype=torch.float32, device=DEV)
+        moe.moe_permute_scales(prob, xs, s, npp, a1s)
+    h = torch.empty((cap, 2 * p.I), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_gemm(prob, 1, a1, d.w13q if fp8 else d.w13, s, e, npp, h, a1s, d.w13s)
+    z = torch.empty((cap, p.I), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16, device=DEV)
+    zs = torch.empty((p.I // 128, cap), dtype=torch.float32, device=DEV) if fp8 else None
+    moe.moe_silu_and_mul(prob, h, s, w, npp, z, zs)
+    o = torch.empty((cap, p.H), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_gemm(prob, 2, z, d.w2q if fp8 else d.w2, None, e, npp, o, zs, d.w2s)
+    y = torch.empty_like(d.x)
+    moe.moe_unpermute_reduce(prob, o, inv, w, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_fused)
+
+
+def test_stage_binding_rejects_row_major_scales():
+    # the GEMM reads a_scale as [K/128, cap]; a per-token [M, K/128] buffer is
+    # refused by the binding before anything is launched
+    p = synth.Problem(M=150, H=512, I=256, E=7, topk=3, block_m=128, wdtype="fp8")
+    d = to_dev(synth.make_inputs(p, "cpu"))
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    prob = moe.make_problem(p.M, p.H, p.I, p.E, p.topk, p.block_m, moe.MOE_W_FP8_E4M3_BLOCK128)
+    s, e, npp, inv = moe.moe_align_block_size(ids, p.E, p.block_m)
+    xq, xs = moe.moe_quant_fp8_groups(d.x)
+    h = torch.empty((s.numel(), 2 * p.I), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="a_scale"):
+        moe.moe_expert_gemm(prob, 1, xq, d.w13q, s, e, npp, h, xs, d.w13s)
+
+
 # ------------------------------------------------------------- full layer ---
 
 SMALL = [
