@@ -114,6 +114,7 @@ class Step:
             self.xq = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
             self.xs = torch.empty((M, H // 128), dtype=torch.float32, device=dev)
             self.xst = torch.empty((H // 128, cap), dtype=torch.float32, device=dev)
+        self.act_fused = moe.moe_expert_gemm_act_supported(self.prob)
         self.w13 = d.w13q if self.fp8 else d.w13
         self.w2 = d.w2q if self.fp8 else d.w2
 
@@ -146,10 +147,15 @@ class Step:
         if self.fp8:  # the activation scales follow the rows into the sorted order
             m.moe_permute_scales(p, self.xs, self.sorted, self.npp, self.xst)
         ev[3].record()
-        m.moe_expert_gemm(p, 1, a1, self.w13, self.sorted, self.expert_ids, self.npp, self.h,
-                          a1s, d.w13s)
-        ev[4].record()
-        m.moe_silu_and_mul(p, self.h, self.sorted, self.w, self.npp, self.z, self.zs)
+        if self.act_fused:  # GEMM1 with the activation in its epilogue; no separate act stage
+            m.moe_expert_gemm_act(p, a1, a1s, self.w13, d.w13s, self.sorted, self.expert_ids,
+                                  self.npp, self.w, self.z, self.zs)
+            ev[4].record()
+        else:
+            m.moe_expert_gemm(p, 1, a1, self.w13, self.sorted, self.expert_ids, self.npp, self.h,
+                              a1s, d.w13s)
+            ev[4].record()
+            m.moe_silu_and_mul(p, self.h, self.sorted, self.w, self.npp, self.z, self.zs)
         ev[5].record()
         m.moe_expert_gemm(p, 2, self.z, self.w2, None, self.expert_ids, self.npp, self.o,
                           self.zs, d.w2s)
@@ -158,8 +164,9 @@ class Step:
         ev[7].record()
 
 
-def algorithmic(p: synth.Problem, touched: int):
-    """Algorithmic FLOP and HBM bytes of the step and of GEMM1 (padding excluded)."""
+def algorithmic(p: synth.Problem, touched: int, act_fused: bool = False):
+    """Algorithmic FLOP and HBM bytes of the step and of GEMM1 (padding excluded);
+    with the activation fused into GEMM1 that kernel writes z instead of h."""
     R = p.M * p.topk
     wb = 1 if p.wdtype == "fp8" else 2
     flops_g1 = 4.0 * R * p.H * p.I
@@ -173,9 +180,12 @@ def algorithmic(p: synth.Problem, touched: int):
     y_b = p.M * p.H * 2
     logits_b = p.M * p.E * 4
     xin_g1 = p.M * p.H * wb + (p.M * (p.H // 128) * 4 if p.wdtype == "fp8" else 0)
-    h_b = R * 2 * p.I * 2
+    if act_fused:
+        out_g1 = R * p.I * wb + (R * (p.I // 128) * 4 if p.wdtype == "fp8" else 0)
+    else:
+        out_g1 = R * 2 * p.I * 2
     return dict(flops=flops, bytes=w13_b + w2_b + x_b + y_b + logits_b,
-                flops_g1=flops_g1, bytes_g1=w13_b + xin_g1 + h_b)
+                flops_g1=flops_g1, bytes_g1=w13_b + xin_g1 + out_g1)
 
 
 def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.Tensor,
@@ -279,7 +289,7 @@ def main():
                 for j, name in enumerate(Step.STAGES)}
     staged_total = float(np.mean([e[0].elapsed_time(e[7]) for e in evs]))
 
-    alg = algorithmic(p, touched)
+    alg = algorithmic(p, touched, st.act_fused)
     tflops = alg["flops"] / (ms * 1e-3) / 1e12
     tok_s = p.M / (ms * 1e-3)
     dt = "fp8" if p.wdtype == "fp8" else "bf16"
@@ -294,7 +304,8 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = "gemm1 (grouped expert GEMM, gathered token rows x w13)"
+    roof["kernel"] = ("gemm1 + SiLU-and-mul epilogue (grouped expert GEMM, gathered token rows x w13, writes z)"
+                      if st.act_fused else "gemm1 (grouped expert GEMM, gathered token rows x w13)")
     roof["avg_ms"] = round(stage_ms["gemm1"], 4)
     t_star = max(alg["flops"] / (PEAK_TFLOPS[dt] * 1e12), alg["bytes"] / (PEAK_HBM_GBS * 1e9))
 

@@ -149,7 +149,10 @@ moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w1
 
 /*
  * The stages of fused_experts, for callers that build their own pipeline or
- * time the stages one by one. fused_experts launches exactly these kernels.
+ * time the stages one by one. fused_experts launches exactly these kernels:
+ * for fp8, moe_quant_fp8_groups(x) and moe_permute_scales after the align;
+ * GEMM1 then activation as moe_expert_gemm_act where available, else
+ * moe_expert_gemm(1) and moe_silu_and_mul; moe_expert_gemm(2); the reduce.
  * `p` has the same meaning as for fused_experts; cap is
  * moe_align_capacity(M, topk, E, block_m); the layout arrays are those of
  * moe_align_block_size. Rows at or past num_tokens_post_padded are skipped.
@@ -189,6 +192,24 @@ moe_status_t moe_silu_and_mul(const moe_problem_t *p, const void *h,
                               const int32_t *sorted_token_ids, const float *topk_weights,
                               const int32_t *num_tokens_post_padded, void *z, float *z_scale,
                               void *stream);
+
+/*
+ * GEMM1 with SiLU-and-mul fused into its epilogue: the result of
+ * moe_expert_gemm(which = 1) followed by moe_silu_and_mul, bit for bit,
+ * without writing h. Available where moe_expert_gemm_act_supported(p) is 1
+ * (host-only, pure): fp8 weights, block_m 128, H >= 256; otherwise
+ * MOE_E_UNSUPPORTED. fused_experts uses it where it is available.
+ *   x [M, H] e4m3, x_scale [H/128, cap] (from moe_permute_scales), w13 and
+ *   w13_scale as for fused_experts, topk_weights [M, topk] (alpha when
+ *   apply_router_weight_on_input), z [cap, I] e4m3 out, z_scale [I/128, cap]
+ *   fp32 out (as moe_silu_and_mul writes them).
+ */
+int32_t moe_expert_gemm_act_supported(const moe_problem_t *p);
+moe_status_t moe_expert_gemm_act(const moe_problem_t *p, const void *x, const float *x_scale,
+                                 const void *w13, const float *w13_scale,
+                                 const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                                 const int32_t *num_tokens_post_padded, const float *topk_weights,
+                                 void *z, float *z_scale, void *stream);
 
 /*
  * The fp8 GEMM1 activation scales in the expert-sorted row order

@@ -21,7 +21,8 @@ MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
 
 EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_quant_fp8_groups",
            "moe_workspace_bytes", "fused_experts", "moe_expert_gemm", "moe_silu_and_mul",
-           "moe_permute_scales", "moe_unpermute_reduce", "moe_status_string")
+           "moe_expert_gemm_act_supported", "moe_expert_gemm_act", "moe_permute_scales",
+           "moe_unpermute_reduce", "moe_status_string")
 
 
 class MoeProblem(ctypes.Structure):
@@ -60,12 +61,15 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_gemm.argtypes = [PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_silu_and_mul.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P]
         L.moe_permute_scales.argtypes = [PP, _P, _P, _P, _P, _P]
+        L.moe_expert_gemm_act_supported.argtypes = [PP]
+        L.moe_expert_gemm_act_supported.restype = _I32
+        L.moe_expert_gemm_act.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_unpermute_reduce.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_status_string.argtypes = [_I32]
         L.moe_status_string.restype = ctypes.c_char_p
         for name in ("moe_topk", "moe_align_block_size", "moe_quant_fp8_groups", "fused_experts",
                      "moe_expert_gemm", "moe_silu_and_mul", "moe_permute_scales",
-                     "moe_unpermute_reduce"):
+                     "moe_expert_gemm_act", "moe_unpermute_reduce"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -252,6 +256,34 @@ def moe_silu_and_mul(p: MoeProblem, h: torch.Tensor, sorted_token_ids: torch.Ten
     _check(lib().moe_silu_and_mul(ctypes.byref(p), _ptr(h), _ptr(sorted_token_ids),
                                   _ptr(topk_weights), _ptr(num_tokens_post_padded), _ptr(z),
                                   _ptr(z_scale), _stream(stream)), "moe_silu_and_mul")
+    return z, z_scale
+
+
+def moe_expert_gemm_act_supported(p: MoeProblem) -> bool:
+    return bool(lib().moe_expert_gemm_act_supported(ctypes.byref(p)))
+
+
+def moe_expert_gemm_act(p: MoeProblem, x: torch.Tensor, x_scale: torch.Tensor, w13: torch.Tensor,
+                        w13_scale: torch.Tensor, sorted_token_ids: torch.Tensor,
+                        expert_ids: torch.Tensor, num_tokens_post_padded: torch.Tensor,
+                        topk_weights: torch.Tensor, z: torch.Tensor, z_scale: torch.Tensor,
+                        stream=None):
+    """GEMM1 with SiLU-and-mul fused in its epilogue (fp8, block_m 128): -> (z, z_scale)."""
+    cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
+    _need_size(x, _F8, p.M * p.H, "x")
+    _need_size(x_scale, _F32, (p.H // 128) * cap, "x_scale [H/128, cap]")
+    _need_size(w13, _F8, p.E * 2 * p.I * p.H, "w13")
+    _need_size(w13_scale, _F32, p.E * (2 * p.I // 128) * (p.H // 128), "w13_scale")
+    _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
+    _need_size(expert_ids, _I32T, cap // p.block_m, "expert_ids")
+    _need_size(num_tokens_post_padded, _I32T, 1, "num_tokens_post_padded")
+    _need_size(topk_weights, _F32, p.M * p.topk, "topk_weights")
+    _need_size(z, _F8, cap * p.I, "z")
+    _need_size(z_scale, _F32, (p.I // 128) * cap, "z_scale [I/128, cap]")
+    _check(lib().moe_expert_gemm_act(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(w13),
+                                     _ptr(w13_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
+                                     _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(z),
+                                     _ptr(z_scale), _stream(stream)), "moe_expert_gemm_act")
     return z, z_scale
 
 

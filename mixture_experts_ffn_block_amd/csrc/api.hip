@@ -111,6 +111,50 @@ hipError_t gemm_stage(const moe_problem_t& p, int which, const void* a, const fl
     return p.block_m == 16 ? launch_stream_gemm(g, s) : launch_grouped_gemm(g, p.block_m, fp8, s);
 }
 
+// GEMM1 with SiLU-and-mul in its epilogue: z[pos] = act(x[token(pos)] w13[e]^T)
+bool act_fused(const moe_problem_t& p) {
+    return gemm_act_supported(p.block_m, p.wdtype == MOE_W_FP8_E4M3_BLOCK128, p.H);
+}
+
+hipError_t gemm_act_stage(const moe_problem_t& p, const void* a, const float* a_scale,
+                          const void* w13, const float* w13_scale, const int32_t* sorted,
+                          const int32_t* expert_ids, const int32_t* npp, const float* weights,
+                          void* z, float* z_scale, hipStream_t s) {
+    const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    const int esz = fp8 ? 1 : 2;
+    const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
+    GemmArgs g{};
+    g.A = a;
+    g.lda_bytes = static_cast<int64_t>(p.H) * esz;
+    g.sorted = sorted;
+    g.topk = p.topk;
+    g.R = static_cast<int>(p.M * p.topk);
+    g.W = w13;
+    g.w_expert_bytes = static_cast<int64_t>(2) * p.I * p.H * esz;
+    g.ldw_bytes = static_cast<int64_t>(p.H) * esz;
+    g.expert_ids = expert_ids;
+    g.npp = npp;
+    g.C = z;
+    g.ldc_bytes = static_cast<int64_t>(p.I) * esz;
+    g.N = p.I;  // output columns; gate rows [0, I), up rows [I, 2I)
+    g.K = p.H;
+    g.m_blocks = static_cast<int>(cap / p.block_m);
+    g.group_m = kGroupM;
+    g.act = 1;
+    g.act_weights = weights;
+    g.act_on_input = p.apply_router_weight_on_input ? 1 : 0;
+    if (fp8) {
+        g.a_scale = a_scale;
+        g.a_scale_ld = cap;
+        g.w_scale = w13_scale;
+        g.w_scale_expert = static_cast<int64_t>(2 * p.I / 128) * (p.H / 128);
+        g.scale_groups = p.H / 128;
+        g.z_scale = z_scale;
+        g.z_scale_ld = cap;
+    }
+    return launch_grouped_gemm(g, p.block_m, fp8, s);
+}
+
 hipError_t act_stage(const moe_problem_t& p, const void* h, const int32_t* sorted,
                      const float* weights, const int32_t* npp, void* z, float* z_scale,
                      hipStream_t s) {
@@ -244,10 +288,17 @@ moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w1
                             reinterpret_cast<float*>(ws + L.xst), s);
         if (err != hipSuccess) return MOE_E_HIP;
     }
-    err = gemm_stage(*p, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, s);
-    if (err != hipSuccess) return MOE_E_HIP;
-    err = act_stage(*p, ho, sorted, topk_weights, npp, z, reinterpret_cast<float*>(ws + L.zs), s);
-    if (err != hipSuccess) return MOE_E_HIP;
+    float* zs = fp8 ? reinterpret_cast<float*>(ws + L.zs) : nullptr;
+    if (act_fused(*p)) {
+        err = gemm_act_stage(*p, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp,
+                             topk_weights, z, zs, s);
+        if (err != hipSuccess) return MOE_E_HIP;
+    } else {
+        err = gemm_stage(*p, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, s);
+        if (err != hipSuccess) return MOE_E_HIP;
+        err = act_stage(*p, ho, sorted, topk_weights, npp, z, zs, s);
+        if (err != hipSuccess) return MOE_E_HIP;
+    }
     err = gemm_stage(*p, 2, z, reinterpret_cast<const float*>(ws + L.zs), w2, w2_scale, sorted,
                      expert_ids, npp, ho, s);
     if (err != hipSuccess) return MOE_E_HIP;
@@ -268,6 +319,27 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, int32_t which, const void* 
     if (fp8 && (!a_scale || !w_scale)) return MOE_E_INVALID;
     return hip_status(gemm_stage(*p, which, a, a_scale, w, w_scale, sorted_token_ids, expert_ids,
                                  num_tokens_post_padded, c, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_expert_gemm_act_supported(const moe_problem_t* p) {
+    return check_problem(p) == MOE_OK && act_fused(*p) ? 1 : 0;
+}
+
+moe_status_t moe_expert_gemm_act(const moe_problem_t* p, const void* x, const float* x_scale,
+                                 const void* w13, const float* w13_scale,
+                                 const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                                 const int32_t* num_tokens_post_padded, const float* topk_weights,
+                                 void* z, float* z_scale, void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!act_fused(*p)) return MOE_E_UNSUPPORTED;
+    if (p->M == 0) return MOE_OK;
+    if (!x || !x_scale || !w13 || !w13_scale || !sorted_token_ids || !expert_ids ||
+        !num_tokens_post_padded || !topk_weights || !z || !z_scale)
+        return MOE_E_INVALID;
+    return hip_status(gemm_act_stage(*p, x, x_scale, w13, w13_scale, sorted_token_ids, expert_ids,
+                                     num_tokens_post_padded, topk_weights, z, z_scale,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_silu_and_mul(const moe_problem_t* p, const void* h,

@@ -73,33 +73,39 @@ struct Tile {
 // MFMA orientation). Stored straight to C, every store instruction would
 // write 16 bytes into each of 32 rows; staged through the wave's own LDS
 // area first, every store instruction writes whole 128-byte lines (8 lanes x
-// 16 bytes per row). `stage` holds TM*32 rows of TN*64 + 16 bytes (the pad
-// spreads consecutive rows over the banks). col0 and N are multiples of 64,
-// so each 64-column chunk is wholly inside or outside C.
-template <int TM, int TN>
+// 16 bytes per row). `stage` holds TMP*32 rows of TN*64 + 16 bytes (the pad
+// spreads consecutive rows over the banks; TMP row tiles per pass, the
+// passes reusing the area in the wave's program order). col0 and N are
+// multiples of 64, so each 64-column chunk is wholly inside or outside C.
+template <int TM, int TN, int TMP>
 __device__ __forceinline__ void store_block(const f32x16_t (&acc)[TN][TM], uint8_t* stage,
                                             uint8_t* c, int64_t row0, int col0, int64_t ldc_bytes,
                                             int N, int lane) {
+    // TMP row tiles of 32 per pass: `stage` holds TMP*32 rows of TN*64 + 16 bytes
     constexpr int PITCH = TN * 64 + 16, CH = TN * 4, RPP = 64 / CH;
+    static_assert(TM % TMP == 0, "whole passes");
     const int r32 = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x16_t& a = acc[tn][tm];
-                const int col = tn * 32 + 8 * q + 4 * half;
-                *reinterpret_cast<u32x2_t*>(stage + (tm * 32 + r32) * PITCH + col * 2) =
-                    u32x2_t{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
-            }
     const int ch = lane % CH;
     const int col = col0 + ch * 8;
 #pragma unroll
-    for (int pass = 0; pass < TM * 32 / RPP; ++pass) {
-        const int row = pass * RPP + lane / CH;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + row * PITCH + ch * 16);
-        if (col < N) *reinterpret_cast<u32x4_t*>(c + (row0 + row) * ldc_bytes + col * 2) = v;
+    for (int t0 = 0; t0 < TM; t0 += TMP) {
+#pragma unroll
+        for (int tm = t0; tm < t0 + TMP; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16_t& a = acc[tn][tm];
+                    const int cc = tn * 32 + 8 * q + 4 * half;
+                    *reinterpret_cast<u32x2_t*>(stage + ((tm - t0) * 32 + r32) * PITCH + cc * 2) =
+                        u32x2_t{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+                }
+#pragma unroll
+        for (int pass = 0; pass < TMP * 32 / RPP; ++pass) {
+            const int row = pass * RPP + lane / CH;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + row * PITCH + ch * 16);
+            if (col < N) *reinterpret_cast<u32x4_t*>(c + (row0 + t0 * 32 + row) * ldc_bytes + col * 2) = v;
+        }
     }
 }
 
@@ -605,12 +611,34 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
 // wave does while the other wave of its SIMD keeps the matrix core busy.
 // With 64 x 64 outputs per wave every accumulator stays in an
 // architectural register, so the scaling needs no accumulator-register moves.
-// The activation scales are stored group-major by sorted position, so the
-// 128 row scales of a stage are 512 contiguous bytes, which wave 0 copies
-// into the stage's slot with one more 1 KB copy (lanes 32..63 repeat lanes
-// 0..31). The tile's weight-block scales, BN/128 rows of K/128 values, are
-// loaded into LDS once before the ring starts. The loop issues no other
-// vector memory instruction, so the explicit vmcnt counts stay exact.
+//
+// The kernel is persistent: one workgroup per CU walks its share of the
+// tiles as one continuous stream of K stages, so the copies of the next
+// tile's first stages are in flight while the current tile finishes and
+// writes its outputs (no pipeline fill or store drain between tiles).
+// Workgroup h runs on XCD h % 8 and takes every (grid/8)-th tile of that
+// XCD's contiguous range of the logical tile order.
+//
+// Per stage the ring slot holds the A and B rows plus the scales: wave 0
+// copies the stage's 128 row scales (the activation scales are stored
+// group-major by sorted position, 512 contiguous bytes), wave 1 copies the
+// tile's weight-block scales of that K block (one 4-byte copy). For a
+// gathered A, wave 0 also copies the next tile's 128 sorted ids into one of
+// three id slots when the current tile's first stage goes out, so switching
+// tiles (and the SiLU epilogue) reads the row indices from LDS. The loop
+// issues no other vector memory instruction, so the explicit vmcnt counts
+// hold (an id copy only makes one wait stricter).
+//
+// With ACT the tile is GEMM1 with SiLU-and-mul fused into the epilogue
+// ("DeepGEMM FusedMoE on Blackwell", 2.6.4, done here in the GEMM's
+// epilogue instead of a separate pass): its 256 weight rows are 128 gate
+// rows and the matching 128 up rows, interleaved in 32-row groups so that
+// every wave holds the gate and the up value of the same outputs (tile
+// rows 64w..64w+31 gate, 64w+32..64w+63 up, of output columns 32w..32w+31).
+// The epilogue rounds both to bf16 (the value GEMM1 would store), forms
+// z = alpha * SiLU(g) * u in fp32, and quantises each row's 128 outputs to
+// e4m3 with scale amax / 448, exactly as the separate activation pass does,
+// then writes z and its scales; h never reaches HBM.
 namespace f8 {
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
@@ -618,19 +646,28 @@ struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = WM_ * WN_, STAGES = STAGES_;
     static constexpr int ROWB = 128, CH = 8, ROWS_PER_COPY = 8;
     static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-    static constexpr int SCALE_OFF = A_BYTES + B_BYTES, STAGE_BYTES = SCALE_OFF + 1024;
+    static constexpr int SCALE_OFF = A_BYTES + B_BYTES;   // 1 KB of row scales, then weight scales
+    static constexpr int WSCALE_OFF = SCALE_OFF + 1024;
+    static constexpr int STAGE_BYTES = SCALE_OFF + 2048;
+    static constexpr int IDS_OFF = STAGES * STAGE_BYTES;  // three 1 KB slots of sorted ids
+    static constexpr int LDS_BYTES = IDS_OFF + 3072;
     static constexpr int A_INSTR = A_BYTES / 1024 / NW, B_INSTR = B_BYTES / 1024 / NW;
-    static constexpr int L = A_INSTR + B_INSTR;  // copies per wave per stage (wave 0: L + 1)
+    static constexpr int L = A_INSTR + B_INSTR;  // copies per wave per stage (waves 0 and 1: L + 1)
     static constexpr int WBLOCKS = BN / 128;     // weight-scale rows per tile
     static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+    static constexpr int EPI_BYTES = 32 * (TN * 64 + 16);  // one 32-row pass of a wave's epilogue
+    static constexpr bool FP8_OUT = true;                  // SiLU epilogue output: e4m3 z
     static_assert(A_INSTR * NW * 1024 == A_BYTES && B_INSTR * NW * 1024 == B_BYTES, "whole copies");
     static_assert((A_INSTR == 2 || A_INSTR == 4) && (B_INSTR == 2 || B_INSTR % 4 == 0), "copy groups");
-    static_assert(BM == 128, "one 1 KB copy carries the 128 row scales");
-    static_assert(BN % 128 == 0 && 128 % (BN / WN) == 0, "a wave's weight rows lie in one 128-row scale block");
-    static_assert(STAGES >= 3 && STAGES * STAGE_BYTES <= 150 * 1024, "fits gfx950 LDS with the scale table");
+    static_assert(BM == 128, "one 1 KB copy carries the 128 row scales and the 128 sorted ids");
+    static_assert(BN % 128 == 0 && 128 % (BN / WN) == 0 && WBLOCKS <= 64,
+                  "a wave's weight rows lie in one 128-row scale block");
+    static_assert(STAGES >= 3 && LDS_BYTES <= 160 * 1024, "fits gfx950 LDS");
     static_assert(STAGE_BYTES % 1024 == 0, "stages keep the 1 KB swizzle alignment");
-    static_assert(3 * (L + 1) <= 63, "vmcnt range");
-    static_assert(NW * (BM / WM) * (BN / WN * 2 + 16) <= STAGES * STAGE_BYTES, "epilogue staging fits the ring");
+    static_assert(3 * (L + 2) <= 63, "vmcnt range");
+    static_assert(NW * EPI_BYTES <= STAGE_BYTES, "epilogue staging fits one ring slot");
+    static_assert(BN == 256 && WN == 4 && TN == 2, "SiLU epilogue: a wave's two column tiles are gate and up");
+    static_assert(BM * (128 + 16) + 4 * BM * 4 <= STAGE_BYTES, "SiLU epilogue staging fits one ring slot");
     // 128-byte rows, 16-byte chunks XOR-swizzled by (row / 2) % 8
     __device__ static __forceinline__ int swz(int row, int chunk) { return row * CH + (chunk ^ ((row >> 1) & 7)); }
 };
@@ -649,109 +686,164 @@ __device__ __forceinline__ void copy1(const void* g, uint32_t lds) {
         : "memory");
 }
 
+// one 256-byte copy (4 bytes per lane) to LDS address `lds`
+__device__ __forceinline__ void copy1_dword(const void* g, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(g)
+        : "memory");
+}
+
 }  // namespace f8
 
-template <class C, bool GATHER>
+template <class C, bool GATHER, bool ACT>
 __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p) {
+    static_assert(!ACT || GATHER, "the SiLU epilogue belongs to GEMM1");
     constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES, TM = C::TM, TN = C::TN;
     constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR, L = C::L;
-    constexpr int WROWS_M = BM / C::WM, WROWS_N = BN / C::WN;
     extern __shared__ __attribute__((aligned(1024))) u32x4_t smem[];
+    uint8_t* const lds8 = reinterpret_cast<uint8_t*>(smem);
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) u32x4_t*)smem));
 
-    TilePos tp;
-    if (!tile_of<BM, BN>(p, tp)) return;
-    const int mb = tp.mb, nb = tp.nb;
-    const int64_t m0 = static_cast<int64_t>(mb) * BM;
-    const int e = p.expert_ids[mb];
-    if (e < 0) return;
-    const int n0 = nb * BN;
+    // ---- this workgroup's tiles --------------------------------------------
+    constexpr int TILE_COLS = ACT ? BN / 2 : BN;  // output columns per tile
+    const int n_tiles = (p.N + TILE_COLS - 1) / TILE_COLS;
+    const int m_real = min(p.m_blocks, (*p.npp + BM - 1) / BM);
+    const int total = m_real * n_tiles;
+    const int per_xcd = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int q8 = total >> 3, rem = total & 7;
+    const int x0 = xcd * q8 + min(xcd, rem), xn = q8 + (xcd < rem ? 1 : 0);
+    const int my_n = slot < xn ? (xn - slot + per_xcd - 1) / per_xcd : 0;
+    if (my_n == 0) return;
+    const int KT = p.K / 128;
+    const int G = my_n * KT;  // stages of this workgroup
+    // logical order: group_m expert blocks down one column of tiles, then the next column
+    auto tile_pos = [&](int i, int& mb, int& nb) {
+        const int t = x0 + slot + i * per_xcd;
+        const int per_group = p.group_m * n_tiles;
+        const int first_mb = (t / per_group) * p.group_m;
+        const int rig = min(p.group_m, m_real - first_mb);
+        mb = first_mb + (t % per_group) % rig;
+        nb = (t % per_group) / rig;
+    };
+    using cint = __attribute__((address_space(4))) const int32_t;  // scalar loads
+    const cint* eids = (const cint*)(p.expert_ids);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int r32 = lane & 31, half = lane >> 5;
+    const int cp_row = lane / C::CH, cp_slot = lane % C::CH;
 
-    auto src_row_of = [&](int row) -> int64_t {
-        if constexpr (GATHER) {
-            const int r = p.sorted[m0 + row];
-            return r < p.R ? r / p.topk : 0;  // padding rows read token 0
+    // ---- issue side: sources of the tile whose stages are being copied ------
+    const uint8_t* a_src[A_INSTR];
+    const uint8_t* w_tile = nullptr;
+    int32_t b_off[B_INSTR];
+    const float* sc_src = nullptr;  // wave 0: row scales; wave 1: weight-block scales
+    auto ids_slot = [&](int i) { return reinterpret_cast<const int32_t*>(lds8 + C::IDS_OFF + (i % 3) * 1024); };
+    auto setup_issue = [&](int i) {
+        int mb, nb;
+        tile_pos(i, mb, nb);
+        const int e = eids[mb];
+        const int64_t m0 = static_cast<int64_t>(mb) * BM;
+        const int n0 = nb * TILE_COLS;
+#pragma unroll
+        for (int c = 0; c < A_INSTR; ++c) {
+            const int row = (wave * A_INSTR + c) * C::ROWS_PER_COPY + cp_row;
+            const int chunk = C::swz(row, cp_slot) - row * C::CH;
+            int64_t src_row = m0 + row;
+            if constexpr (GATHER) {
+                const int r = i == 0 ? p.sorted[m0 + row] : ids_slot(i)[row];
+                src_row = r < p.R ? r / p.topk : 0;  // padding rows read token 0
+            }
+            a_src[c] = reinterpret_cast<const uint8_t*>(p.A) + src_row * p.lda_bytes + chunk * 16;
+        }
+        w_tile = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
+#pragma unroll
+        for (int c = 0; c < B_INSTR; ++c) {
+            const int row = (wave * B_INSTR + c) * C::ROWS_PER_COPY + cp_row;
+            const int chunk = C::swz(row, cp_slot) - row * C::CH;
+            // ACT: tile row r is gate (r / 32 even) or up row of output column
+            // n0 + 32 * (r / 64) + r % 32
+            const int wrow = ACT ? ((row >> 5) & 1) * p.N + n0 + (row >> 6) * 32 + (row & 31)
+                                 : min(n0 + row, p.N - 1);
+            b_off[c] = wrow * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
+        }
+        if (wave == 0) {
+            sc_src = p.a_scale + m0 + (lane & 31) * 4;
         } else {
-            return m0 + row;
+            // lane b < WBLOCKS: weight-block row n0/128 + b (rows past N repeat the
+            // last); ACT: lane 0 the gate block, lane 1 the up block
+            const int b = ACT ? (lane & 1) * (p.N / 128) + n0 / 128
+                              : min(n0 / 128 + min(lane, C::WBLOCKS - 1), p.N / 128 - 1);
+            sc_src = p.w_scale + static_cast<int64_t>(e) * p.w_scale_expert +
+                     static_cast<int64_t>(b) * p.scale_groups;
         }
     };
-    const int cp_row = lane / C::CH, cp_slot = lane % C::CH;
-    const uint8_t* a_src[A_INSTR];
-#pragma unroll
-    for (int i = 0; i < A_INSTR; ++i) {
-        const int row = (wave * A_INSTR + i) * C::ROWS_PER_COPY + cp_row;
-        const int chunk = C::swz(row, cp_slot) - row * C::CH;
-        a_src[i] = reinterpret_cast<const uint8_t*>(p.A) + src_row_of(row) * p.lda_bytes + chunk * 16;
-    }
-    const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
-    int32_t b_off[B_INSTR];
-#pragma unroll
-    for (int i = 0; i < B_INSTR; ++i) {
-        const int row = (wave * B_INSTR + i) * C::ROWS_PER_COPY + cp_row;
-        const int chunk = C::swz(row, cp_slot) - row * C::CH;
-        b_off[i] = min(n0 + row, p.N - 1) * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
-    }
-    // wave 0's scale copy: floats 4*(lane % 32) .. +3 of the stage's 128 row scales
-    const float* sc_src = p.a_scale + m0 + (lane & 31) * 4;
-
+    // copies of stage gs (tile gs / KT, K block gs % KT), in two parts
     const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds_base + wave * A_INSTR * 1024);
     const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_base + C::A_BYTES + wave * B_INSTR * 1024);
-    const uint32_t s_dst = lds_base + C::SCALE_OFF;
-
-    // the tile's weight-block scales: wtab[b * KT + k] = w_scale[e, n0/128 + b, k]
-    // (blocks past N repeat the last one; their rows are never stored)
-    const int KT = p.K / 128;
-    float* wtab = reinterpret_cast<float*>(smem + STAGES * (C::STAGE_BYTES / 16));
-    for (int i = tid; i < C::WBLOCKS * KT; i += C::NW * 64) {
-        const int b = min(n0 / 128 + i / KT, p.N / 128 - 1);
-        wtab[i] = p.w_scale[static_cast<int64_t>(e) * p.w_scale_expert + static_cast<int64_t>(b) * p.scale_groups + i % KT];
-    }
-    __syncthreads();
-
-    constexpr int AG = A_INSTR, BG = B_INSTR >= 4 ? 4 : B_INSTR;
-    constexpr int NGROUPS = 1 + B_INSTR / BG + 1;  // the last group is wave 0's scale copy
-    auto copy = [&](int kt, int j) {
-        const uint32_t st = static_cast<uint32_t>(kt % STAGES) * C::STAGE_BYTES;
+    constexpr int BG = B_INSTR >= 4 ? 4 : B_INSTR;
+    auto issue_a = [&](int gs) {
+        const int i = gs / KT, kt = gs - i * KT;
+        if (kt == 0) {
+            if (gs > 0) setup_issue(i);
+            // the next tile's sorted ids, for its setup (read after this stage has landed)
+            if (GATHER && wave == 0 && i + 1 < my_n) {
+                int mb1, nb1;
+                tile_pos(i + 1, mb1, nb1);
+                f8::copy1(p.sorted + static_cast<int64_t>(mb1) * BM + (lane & 31) * 4,
+                          lds_base + C::IDS_OFF + ((i + 1) % 3) * 1024);
+            }
+        }
+        const uint32_t st = static_cast<uint32_t>(gs % STAGES) * C::STAGE_BYTES;
         const int64_t off = static_cast<int64_t>(kt) * C::ROWB;
-        if (j == 0) {
-            const uint8_t* g[AG];
+        const uint8_t* g[A_INSTR];
 #pragma unroll
-            for (int i = 0; i < AG; ++i) g[i] = a_src[i] + off;
-            dma::copy_group<AG>(g, a_dst + st);
-        } else if (j < NGROUPS - 1) {
-            const int jb = j - 1;
+        for (int c = 0; c < A_INSTR; ++c) g[c] = a_src[c] + off;
+        dma::copy_group<A_INSTR>(g, a_dst + st);
+    };
+    auto issue_rest = [&](int gs) {
+        const int kt = gs % KT;
+        const uint32_t st = static_cast<uint32_t>(gs % STAGES) * C::STAGE_BYTES;
+        const int64_t off = static_cast<int64_t>(kt) * C::ROWB;
+#pragma unroll
+        for (int j = 0; j < B_INSTR / BG; ++j) {
             const uint8_t* g[BG];
 #pragma unroll
-            for (int i = 0; i < BG; ++i) g[i] = w_base + b_off[jb * BG + i] + off;
-            dma::copy_group<BG>(g, b_dst + st + jb * BG * 1024);
-        } else if (wave == 0) {
-            f8::copy1(sc_src + static_cast<int64_t>(kt) * p.a_scale_ld, s_dst + st);
+            for (int c = 0; c < BG; ++c) g[c] = w_tile + b_off[j * BG + c] + off;
+            dma::copy_group<BG>(g, b_dst + st + j * BG * 1024);
         }
+        if (wave == 0)
+            f8::copy1(sc_src + static_cast<int64_t>(kt) * p.a_scale_ld, lds_base + st + C::SCALE_OFF);
+        else if (wave == 1)
+            f8::copy1_dword(sc_src + kt, lds_base + st + C::WSCALE_OFF);
     };
     auto wait_barrier = [&](int newer) {
-        if (wave == 0)
+        if (wave <= 1)
             dma::wait_barrier<L + 1>(newer);
         else
             dma::wait_barrier<L>(newer);
     };
 
+    // ---- compute side -------------------------------------------------------
     f32x16_t acc[TN][TM], part[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = f32x16_t{};
-
-    const int arow = wm * WROWS_M, brow = wn * WROWS_N;
+    const int arow = wm * (BM / C::WM), brow = wn * (BN / C::WN);
     struct Frag {
         i32x8_t a[TM], b[TN];
     };
-    auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * (C::STAGE_BYTES / 16); };
+    auto stage_ptr = [&](int g) { return smem + (g % STAGES) * (C::STAGE_BYTES / 16); };
     // lane (r32, half) holds 32 consecutive bytes of K: chunks 4ks + 2half, +1
     auto frag = [&](const u32x4_t* base, int row, int ks) {
         const u32x4_t lo = base[C::swz(row, 4 * ks + 2 * half)];
@@ -759,8 +851,8 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
-    auto read = [&](int kt, int ks, Frag& f) {
-        const u32x4_t* st = stage_ptr(kt);
+    auto read = [&](int g, int ks, Frag& f) {
+        const u32x4_t* st = stage_ptr(g);
 #pragma unroll
         for (int i = 0; i < TN; ++i) f.b[i] = frag(st + C::A_BYTES / 16, brow + i * 32 + r32, ks);
 #pragma unroll
@@ -776,63 +868,158 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
                     f.b[tn], f.a[tm], first ? f32x16_t{} : part[tn][tm], 0, 0, 0, 127, 0, 127);
     };
     // scale of tile row arow + tm*32 + r32 times the wave's weight-block scale
-    auto fold = [&](int kt) {
-        const float* sx = reinterpret_cast<const float*>(stage_ptr(kt) + C::SCALE_OFF / 16);
-        const float sw = wtab[(brow / 128) * KT + kt];
+    // (ACT: column tile tn = 0 holds gate rows, tn = 1 up rows, each its own block)
+    auto fold = [&](int g) {
+        const float* sx = reinterpret_cast<const float*>(stage_ptr(g) + C::SCALE_OFF / 16);
+        const float* swb = reinterpret_cast<const float*>(stage_ptr(g) + C::WSCALE_OFF / 16);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-            const float sc = sx[arow + tm * 32 + r32] * sw;
+            const float x = sx[arow + tm * 32 + r32];
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
+            for (int tn = 0; tn < TN; ++tn) {
+                const float sc = x * swb[ACT ? tn : brow / 128];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[tn][tm][r] += part[tn][tm][r] * sc;
+            }
         }
     };
 
-    // Per K stage kt: wait until stage kt has landed and every wave is done
-    // with stage kt-1, then send the copies of stage kt+S-1 into kt-1's slot
-    // before this stage's MFMAs, so S-1 stages are in flight at every wait.
-    Frag f0, f1;
-    for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt)
+    // SiLU-and-mul epilogue of one tile (ACT): `ws` is a free ring slot, `ids`
+    // the tile's 128 sorted ids, m0 its first row, nb its 128-column block of z.
+    // Lane (r32, half) holds, for row arow + tm*32 + r32, the gate (tn = 0) and
+    // up (tn = 1) sums of columns 32*wn + 8q + 4*half + j.
+    auto act_epilogue = [&](const f32x16_t (&a)[TN][TM], uint8_t* ws, const int32_t* ids, int64_t m0,
+                            int nb) {
+        constexpr int ZP = 128 + 16;                       // staged z row pitch (bytes)
+        float* amax_part = reinterpret_cast<float*>(ws + BM * ZP);  // [4][BM]
+        float v[TM][16];
 #pragma unroll
-        for (int j = 0; j < NGROUPS; ++j) copy(kt, j);
-    for (int kt = 0; kt < KT; ++kt) {
-        wait_barrier(min(STAGES - 2, KT - 1 - kt));
-        const bool more = kt + STAGES - 1 < KT;
-        read(kt, 0, f0);
-        if (more) copy(kt + STAGES - 1, 0);
-        read(kt, 1, f1);
-        mma(f0, true);
-        if (more) {
+        for (int tm = 0; tm < TM; ++tm) {
+            const int rl = arow + tm * 32 + r32;
+            const int r = ids[rl];
+            const bool real = r < p.R;
+            const float alpha = (real && p.act_on_input) ? p.act_weights[r] : 1.0f;
+            float m = 0.0f;
 #pragma unroll
-            for (int j = 1; j < NGROUPS; ++j) copy(kt + STAGES - 1, j);
+            for (int i = 0; i < 16; ++i) {
+                const float gt = bf16_to_f32(f32_to_bf16(a[0][tm][i]));
+                const float up = bf16_to_f32(f32_to_bf16(a[1][tm][i]));
+                v[tm][i] = real ? alpha * silu_f32(gt) * up : 0.0f;
+                m = fmaxf(m, fabsf(v[tm][i]));
+            }
+            m = fmaxf(m, __shfl_xor(m, 32, 64));  // the other half of the row's 32 columns
+            if (half == 0) amax_part[wn * BM + rl] = m;
         }
-        mma(f1, false);
-        fold(kt);
-    }
+        // barriers that wait only for LDS traffic: the copies in flight stay in flight
+        auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+        if constexpr (C::FP8_OUT) {
+            lds_barrier();
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const int rl = arow + tm * 32 + r32;
+                const float m = fmaxf(fmaxf(amax_part[rl], amax_part[BM + rl]),
+                                      fmaxf(amax_part[2 * BM + rl], amax_part[3 * BM + rl]));
+                const float s = m / 448.0f;
+                if (wn == 0 && half == 0) p.z_scale[nb * p.z_scale_ld + m0 + rl] = s;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float c4[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        c4[j] = m == 0.0f ? 0.0f : fminf(fmaxf(v[tm][4 * q + j] / s, -448.0f), 448.0f);
+                    *reinterpret_cast<uint32_t*>(ws + rl * ZP + wn * 32 + 8 * q + 4 * half) =
+                        cvt_e4m3x4(c4[0], c4[1], c4[2], c4[3]);
+                }
+            }
+            lds_barrier();
+            // 128 rows x 128 bytes: 8 lanes per row, 8 rows per wave per pass
+            uint8_t* zc = reinterpret_cast<uint8_t*>(p.C);
+#pragma unroll
+            for (int pass = 0; pass < BM / (8 * C::NW); ++pass) {
+                const int rl = (pass * C::NW + wave) * 8 + lane / 8;
+                const u32x4_t z16 = *reinterpret_cast<const u32x4_t*>(ws + rl * ZP + (lane % 8) * 16);
+                *reinterpret_cast<u32x4_t*>(zc + (m0 + rl) * p.ldc_bytes + nb * 128 + (lane % 8) * 16) = z16;
+            }
+        }
+    };
 
-    // every wave is past its last LDS read of the ring: reuse it for the epilogue
-    __syncthreads();
-    store_block<TM, TN>(acc, reinterpret_cast<uint8_t*>(smem) + wave * (TM * 32 * (TN * 64 + 16)),
-                        reinterpret_cast<uint8_t*>(p.C), m0 + arow, n0 + brow, p.ldc_bytes, p.N, lane);
+    // Per stage g: wait until stage g has landed and every wave is done with
+    // stage g-1, send the copies of stage g+S-1 into g-1's slot, then the
+    // MFMAs and the scaling of stage g. After a tile's last stage its
+    // outputs go out through that stage's slot, which the copies reuse only
+    // after the next barrier.
+    setup_issue(0);
+    if (ACT && wave == 0) {  // tile 0's sorted ids, for its epilogue
+        int mb0, nb0;
+        tile_pos(0, mb0, nb0);
+        f8::copy1(p.sorted + static_cast<int64_t>(mb0) * BM + (lane & 31) * 4, lds_base + C::IDS_OFF);
+    }
+    for (int gs = 0; gs < STAGES - 1 && gs < G; ++gs) {
+        issue_a(gs);
+        issue_rest(gs);
+    }
+    Frag f0, f1;
+    int c_tile = 0, kt = 0;
+    for (int g = 0; g < G; ++g) {
+        wait_barrier(min(STAGES - 2, G - 1 - g));
+        const int gs = g + STAGES - 1;
+        const bool more = gs < G;
+        read(g, 0, f0);
+        if (more) issue_a(gs);
+        read(g, 1, f1);
+        mma(f0, true);
+        if (more) issue_rest(gs);
+        mma(f1, false);
+        fold(g);
+        if (++kt == KT) {
+            kt = 0;
+            int mb, nb;
+            tile_pos(c_tile, mb, nb);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // slot g is free
+            uint8_t* free_slot = lds8 + (g % STAGES) * C::STAGE_BYTES;
+            if constexpr (ACT)
+                act_epilogue(acc, free_slot, ids_slot(c_tile), static_cast<int64_t>(mb) * BM, nb);
+            else
+                store_block<TM, TN, 1>(acc, free_slot + wave * C::EPI_BYTES, reinterpret_cast<uint8_t*>(p.C),
+                                       static_cast<int64_t>(mb) * BM + arow, nb * BN + brow, p.ldc_bytes,
+                                       p.N, lane);
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int j = 0; j < TM; ++j) acc[i][j] = f32x16_t{};
+            ++c_tile;
+        }
+    }
+}
+
+// one workgroup per CU (multiple of 8 so that every XCD gets the same count)
+int persistent_grid() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
+        cus[dev] = n / 8 * 8;
+    }
+    return cus[dev];
+}
+
+template <class C, bool GATHER, bool ACT>
+hipError_t launch_fp8_as(const GemmArgs& a, hipStream_t stream) {
+    const size_t lds = C::LDS_BYTES;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, GATHER, ACT>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+    const dim3 grid(static_cast<unsigned>(persistent_grid()));
+    hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, GATHER, ACT>), grid, dim3(C::NW * 64), lds, stream, a);
+    return hipGetLastError();
 }
 
 template <class C>
 hipError_t launch_fp8(const GemmArgs& a, hipStream_t stream) {
-    const int n_tiles = (a.N + C::BN - 1) / C::BN;
-    const dim3 grid(static_cast<unsigned>(a.m_blocks * n_tiles));
-    const size_t lds = C::STAGES * C::STAGE_BYTES + static_cast<size_t>(C::WBLOCKS) * (a.K / 128) * 4;
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
-    const void* fn = a.sorted ? reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, true>)
-                              : reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, false>);
-    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(lds));
-    if (err != hipSuccess) return err;
-    if (a.sorted)
-        hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, true>), grid, dim3(C::NW * 64), lds, stream, a);
-    else
-        hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, false>), grid, dim3(C::NW * 64), lds, stream, a);
-    return hipGetLastError();
+    if (a.act) return a.sorted ? launch_fp8_as<C, true, true>(a, stream) : hipErrorInvalidValue;
+    return a.sorted ? launch_fp8_as<C, true, false>(a, stream) : launch_fp8_as<C, false, false>(a, stream);
 }
 
 template <class C>
@@ -876,7 +1063,12 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
 
 int gemm_supported_block_m(int bm) { return bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
+bool gemm_act_supported(int block_m, bool fp8, int K) {
+    return fp8 && block_m == 128 && K >= 128 * (Fp8x128::STAGES - 1);
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStream_t stream) {
+    if (a.act && !gemm_act_supported(block_m, fp8, a.K)) return hipErrorInvalidValue;
     if (!fp8) {
         switch (block_m) {
             case 32: return launch_tile<32, 256, false>(a, stream);
@@ -888,7 +1080,11 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStre
         switch (block_m) {
             case 32: return launch_tile<32, 256, true>(a, stream);
             case 64: return launch_tile<64, 256, true>(a, stream);
-            case 128: return launch_fp8<Fp8x128>(a, stream);
+            // the streaming kernel needs K / 128 >= STAGES - 1 (one tile's stages fill the
+            // ring start); a single 128-wide K block takes the register-staged kernel
+            case 128:
+                if (a.K >= 128 * (Fp8x128::STAGES - 1)) return launch_fp8<Fp8x128>(a, stream);
+                return a.act ? hipErrorInvalidValue : launch_tile<128, 256, true>(a, stream);
         }
     }
     return hipErrorInvalidValue;

@@ -30,6 +30,14 @@ struct GemmArgs {
     const float* w_scale;      // [E, N/128, K/128]
     int64_t w_scale_expert;    // floats per expert of w_scale
     int scale_groups;          // K / 128
+    // SiLU-and-mul epilogue (GEMM1 only): W holds gate rows [0, N) and up rows
+    // [N, 2N); C is z [rows, N] (e4m3 with z_scale, or bf16) with
+    // z = alpha * SiLU(bf16(gate)) * bf16(up), padding rows 0
+    int act;
+    const float* act_weights;  // topk_weights [R] (alpha when act_on_input)
+    int act_on_input;
+    float* z_scale;            // fp8: [N/128, z_scale_ld] group-major
+    int64_t z_scale_ld;
 };
 
 hipError_t launch_topk_softmax(const float* logits, int64_t M, int E, int k, int renormalize,
@@ -38,6 +46,7 @@ hipError_t launch_align(const int32_t* ids, int64_t R, int E, int B, int64_t cap
                         int32_t* expert_ids, int32_t* npp, int32_t* inv_perm, hipStream_t stream);
 int gemm_supported_block_m(int bm);
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStream_t stream);
+bool gemm_act_supported(int block_m, bool fp8, int K);  // a fused SiLU-and-mul GEMM1 exists
 hipError_t launch_stream_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_silu_mul_bf16(const bf16_t* h, bf16_t* z, const int32_t* sorted,
                                 const float* weights, int R, int I, int64_t cap,
