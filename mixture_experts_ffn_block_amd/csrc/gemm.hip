@@ -104,7 +104,9 @@ __device__ __forceinline__ void store_block(const f32x16_t (&acc)[TN][TM], uint8
         for (int pass = 0; pass < TMP * 32 / RPP; ++pass) {
             const int row = pass * RPP + lane / CH;
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + row * PITCH + ch * 16);
-            if (col < N) *reinterpret_cast<u32x4_t*>(c + (row0 + t0 * 32 + row) * ldc_bytes + col * 2) = v;
+            // streaming stores: C is not read again by this kernel
+            if (col < N)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(c + (row0 + t0 * 32 + row) * ldc_bytes + col * 2));
         }
     }
 }
@@ -938,7 +940,8 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
             for (int pass = 0; pass < BM / (8 * C::NW); ++pass) {
                 const int rl = (pass * C::NW + wave) * 8 + lane / 8;
                 const u32x4_t z16 = *reinterpret_cast<const u32x4_t*>(ws + rl * ZP + (lane % 8) * 16);
-                *reinterpret_cast<u32x4_t*>(zc + (m0 + rl) * p.ldc_bytes + nb * 128 + (lane % 8) * 16) = z16;
+                __builtin_nontemporal_store(
+                    z16, reinterpret_cast<u32x4_t*>(zc + (m0 + rl) * p.ldc_bytes + nb * 128 + (lane % 8) * 16));
             }
         }
     };

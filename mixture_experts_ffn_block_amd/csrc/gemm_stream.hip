@@ -8,13 +8,13 @@
 // expert's weights once from HBM.
 //
 // gfx950 design: no LDS. A wavefront owns 16 token rows x 64 weight rows (four
-// v_mfma_f32_16x16x32_bf16 column tiles). Per 128-wide K chunk every lane
-// loads 64 contiguous bytes of one weight row (four 16-byte loads per column
-// tile) and 64 bytes of one token row straight into the MFMA operand
-// registers: lanes l and l+16k read consecutive 64-byte pieces of the same
-// row, so a wave reads 256 contiguous bytes per row. Both operands assign the
-// same K index to the same (lane, register) slot, so the MFMA's sum over K
-// is exact regardless of the order the slots take. The next chunk is loaded
+// v_mfma_f32_16x16x32_bf16 column tiles). Per 128-wide K chunk (256 bytes of
+// a row) every lane loads four 16-byte pieces of one weight row per column
+// tile, and of one token row, straight into the MFMA operand registers: load
+// s gives lane group k = lane / 16 the piece at 64*s + 16*k, so each load
+// instruction reads 64 contiguous bytes of each of its 16 rows. Both
+// operands assign the same K index to the same (lane, register) slot, so the
+// MFMA's sum over K is exact regardless of the order the slots take. The next chunk is loaded
 // while the current one is multiplied. The token rows (tiny) are re-read by
 // every wave from L2; the weights stream from HBM once per expert block.
 #include "common.h"
@@ -47,13 +47,13 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void stream_gemm_bf16_kernel(Gemm
         const int r = p.sorted[m0 + row16];
         src_row = r < p.R ? r / p.topk : 0;  // padding rows read token 0
     }
-    const uint8_t* a_ptr = reinterpret_cast<const uint8_t*>(p.A) + src_row * p.lda_bytes + kq * 64;
+    const uint8_t* a_ptr = reinterpret_cast<const uint8_t*>(p.A) + src_row * p.lda_bytes + kq * 16;
     const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
     const uint8_t* w_ptr[kTilesPerWave];
 #pragma unroll
     for (int t = 0; t < kTilesPerWave; ++t) {
         const int n = min(nw0 + 16 * t + row16, p.N - 1);
-        w_ptr[t] = w_base + static_cast<int64_t>(n) * p.ldw_bytes + kq * 64;
+        w_ptr[t] = w_base + static_cast<int64_t>(n) * p.ldw_bytes + kq * 16;
     }
 
     f32x4_t acc[kTilesPerWave];
@@ -65,12 +65,12 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void stream_gemm_bf16_kernel(Gemm
     auto load = [&](int kc, u32x4_t (&a)[4], u32x4_t (&w)[kTilesPerWave][4]) {
         const int64_t off = static_cast<int64_t>(kc) * 256;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const u32x4_t*>(a_ptr + off + 16 * s);
+        for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const u32x4_t*>(a_ptr + off + 64 * s);
 #pragma unroll
         for (int t = 0; t < kTilesPerWave; ++t)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                w[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(w_ptr[t] + off + 16 * s));
+                w[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(w_ptr[t] + off + 64 * s));
     };
     load(0, a_cur, w_cur);
     for (int kc = 0; kc < KC; ++kc) {
