@@ -538,11 +538,9 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
             for (int tm = 0; tm < TM; ++tm)
                 acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (next_kt >= 0) {
-                read_b(next_kt, 0, g, tn);
+            read_b(next_kt, 0, g, tn);
 #pragma unroll
-                for (int i = tn * TM / TN; i < (tn + 1) * TM / TN; ++i) read_a(next_kt, 0, g, i);
-            }
+            for (int i = tn * TM / TN; i < (tn + 1) * TM / TN; ++i) read_a(next_kt, 0, g, i);
             if (ck >= 0) {
 #pragma unroll
                 for (int j = tn * NGROUPS / TN; j < (tn + 1) * NGROUPS / TN; ++j) copy(ck, j);
@@ -562,41 +560,33 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
     for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
     wait_barrier<C::L>(min(STAGES - 2, KT - 1));
     read(0, 0, fs[0]);
-    for (int kt = 0; kt < KT; ++kt) {
+    auto steps_but_last = [&](int kt) {
 #pragma unroll
         for (int ks = 0; ks + 1 < NKS; ++ks) {
             read(kt, ks + 1, fs[(ks + 1) & 1]);
             mma(fs[ks & 1]);
             interleave();
         }
-        int next = -1, ck = -1;
-        if (kt + 1 < KT) {
-            // tile kt+1 landed (tiles kt+2 .. kt+S-2 may still be in flight);
-            // every wave has finished reading the stage of tile kt-1
-            wait_barrier<C::L>(min(STAGES - 3, KT - 2 - kt));
-            next = kt + 1;
-            if (kt + STAGES - 1 < KT) ck = kt + STAGES - 1;
-        }
-        mma_and_prefetch(fs[1], next, fs[0], ck);
+    };
+    // (the last K tile is peeled off, so the reads of the next tile's first
+    // set are unconditional and the LDS counter waits stay exact)
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+        steps_but_last(kt);
+        // tile kt+1 landed (tiles kt+2 .. kt+S-2 may still be in flight);
+        // every wave has finished reading the stage of tile kt-1
+        wait_barrier<C::L>(min(STAGES - 3, KT - 2 - kt));
+        mma_and_prefetch(fs[1], kt + 1, fs[0], kt + STAGES - 1 < KT ? kt + STAGES - 1 : -1);
     }
+    steps_but_last(KT - 1);
+    mma(fs[1]);
 
-    uint8_t* c_base = reinterpret_cast<uint8_t*>(p.C);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        const int64_t row = m0 + arow + tm * 32 + r32;
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + brow + tn * 32 + 8 * q + 4 * half;
-                if (n < p.N) {
-                    const f32x16_t& a = acc[tn][tm];
-                    u32x2_t v{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
-                    *reinterpret_cast<u32x2_t*>(c_base + row * p.ldc_bytes + n * 2) = v;
-                }
-            }
-        }
-    }
+    // no copies are in flight; once every wave is past its last fragment
+    // read, the ring holds the epilogue staging
+    __syncthreads();
+    constexpr int TMP = TM >= 2 ? 2 : 1;  // 32-row tiles per staging pass
+    static_assert(4 * TMP * 32 * (TN * 64 + 16) <= STAGES * C::STAGE_BYTES, "staging fits the ring");
+    store_block<TM, TN, TMP>(acc, reinterpret_cast<uint8_t*>(smem) + wave * (TMP * 32 * (TN * 64 + 16)),
+                             reinterpret_cast<uint8_t*>(p.C), m0 + arow, n0 + brow, p.ldc_bytes, p.N, lane);
 }
 
 // ---------------------------------------------------------------------------
