@@ -18,7 +18,7 @@ namespace {
 constexpr int64_t kAlign = 256;
 constexpr int kMaxE = 256;
 constexpr int kMaxTopk = 32;
-constexpr int kGroupM = 8;
+constexpr int kGroupM = 32;  // blocks per tile-scheduling window (groups never span two experts)
 
 int64_t up(int64_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 

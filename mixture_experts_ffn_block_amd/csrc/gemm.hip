@@ -118,11 +118,30 @@ __device__ __forceinline__ void store_block(const f32x16_t (&acc)[TN][TM], uint8
 // which come last in the logical order, would leave whole XCDs idle).
 // Hardware id h runs on XCD h % 8; XCD x receives the contiguous logical range
 // starting at x*q + min(x, rem), a bijection onto [0, total), so tiles that
-// share token rows or weight rows meet in one L2. The logical order walks
-// group_m expert blocks down one column of tiles before the next column.
+// share token rows or weight rows meet in one L2.
+// Logical order: the blocks are cut into groups, each a maximal run of blocks
+// of one expert inside an aligned window of group_m blocks, and a group's tiles
+// are walked down one column of tiles before the next column. A group never
+// mixes two experts, so its tiles of one column share a single weight tile.
+// Group [gs, ge) owns exactly the logical tiles [gs, ge) x n_tiles, so a
+// workgroup finds its group from at most 2 * group_m expert ids.
 struct TilePos {
     int mb, nb;
 };
+__device__ __forceinline__ void tile_in_group(const GemmArgs& p, int tile, int n_tiles, int m_real,
+                                              TilePos& t) {
+    using cint = __attribute__((address_space(4))) const int32_t;  // scalar loads
+    const cint* eids = (const cint*)(p.expert_ids);
+    const int b0 = tile / n_tiles;
+    const int w0 = b0 / p.group_m * p.group_m, w1 = min(w0 + p.group_m, m_real);
+    const int e0 = eids[b0];
+    int gs = b0, ge = b0 + 1;
+    while (gs > w0 && eids[gs - 1] == e0) --gs;
+    while (ge < w1 && eids[ge] == e0) ++ge;
+    const int local = tile - gs * n_tiles, rows = ge - gs;
+    t.mb = gs + local % rows;
+    t.nb = local / rows;
+}
 template <int BM, int BN>
 __device__ __forceinline__ bool tile_of(const GemmArgs& p, TilePos& t) {
     const int n_tiles = (p.N + BN - 1) / BN;
@@ -131,12 +150,7 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, TilePos& t) {
     const int hw = blockIdx.x;
     if (hw >= total) return false;
     const int xcd = hw & 7, q8 = total >> 3, rem = total & 7;
-    const int tile = xcd * q8 + min(xcd, rem) + (hw >> 3);
-    const int per_group = p.group_m * n_tiles;
-    const int first_mb = (tile / per_group) * p.group_m;
-    const int rows_in_group = min(p.group_m, m_real - first_mb);
-    t.mb = first_mb + (tile % per_group) % rows_in_group;
-    t.nb = (tile % per_group) / rows_in_group;
+    tile_in_group(p, xcd * q8 + min(xcd, rem) + (hw >> 3), n_tiles, m_real, t);
     return true;
 }
 
@@ -386,7 +400,7 @@ __device__ __forceinline__ void wait_barrier(int newer) {
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Geometry: BM x BN tile, WM x WN waves (4 in total), each wave TM x TN MFMA
+// Geometry: BM x BN tile, WM x WN waves (NW in total), each wave TM x TN MFMA
 // tiles of 32 x 32; STAGES LDS stages of (BM + BN) rows of ROWB bytes (ROWB/2
 // bf16 of K, so ROWB/32 MFMA K steps per stage).
 //
@@ -395,14 +409,15 @@ __device__ __forceinline__ void wait_barrier(int newer) {
 // serves together (16 consecutive rows, one logical chunk) land in 16 distinct
 // 16-byte bank groups of a 256-byte bank row: (r >> 2) & 3 for 64-byte rows,
 // (r >> 1) & 7 for 128-byte rows.
-template <int BM_, int BN_, int WM_, int STAGES_, int ROWB_>
+template <int BM_, int BN_, int WM_, int STAGES_, int ROWB_, int NW_ = 4>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, STAGES = STAGES_;
+    static constexpr int NW = NW_;  // waves per workgroup
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = NW_ / WM_, STAGES = STAGES_;
     static constexpr int ROWB = ROWB_, CH = ROWB / 16, KS = ROWB / 2, NKS = ROWB / 32;
     static constexpr int ROWS_PER_COPY = 1024 / ROWB;
     static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 1 KB copies per wave
-    static constexpr int B_INSTR = B_BYTES / 1024 / 4;
+    static constexpr int A_INSTR = A_BYTES / 1024 / NW;  // 1 KB copies per wave
+    static constexpr int B_INSTR = B_BYTES / 1024 / NW;
     static constexpr int L = A_INSTR + B_INSTR;
     static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
     static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte rows");
@@ -418,7 +433,7 @@ struct Cfg {
 }  // namespace dma
 
 template <class C, bool GATHER>
-__global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p) {
     using namespace dma;
     constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES, TM = C::TM, TN = C::TN;
     constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR, NKS = C::NKS;
@@ -584,7 +599,7 @@ __global__ __launch_bounds__(256) void expert_gemm_dma_kernel(GemmArgs p) {
     // read, the ring holds the epilogue staging
     __syncthreads();
     constexpr int TMP = TM >= 2 ? 2 : 1;  // 32-row tiles per staging pass
-    static_assert(4 * TMP * 32 * (TN * 64 + 16) <= STAGES * C::STAGE_BYTES, "staging fits the ring");
+    static_assert(C::NW * TMP * 32 * (TN * 64 + 16) <= STAGES * C::STAGE_BYTES, "staging fits the ring");
     store_block<TM, TN, TMP>(acc, reinterpret_cast<uint8_t*>(smem) + wave * (TMP * 32 * (TN * 64 + 16)),
                              reinterpret_cast<uint8_t*>(p.C), m0 + arow, n0 + brow, p.ldc_bytes, p.N, lane);
 }
@@ -716,14 +731,12 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
     if (my_n == 0) return;
     const int KT = p.K / 128;
     const int G = my_n * KT;  // stages of this workgroup
-    // logical order: group_m expert blocks down one column of tiles, then the next column
+    // logical order: that of tile_of (expert-aligned groups, column by column)
     auto tile_pos = [&](int i, int& mb, int& nb) {
-        const int t = x0 + slot + i * per_xcd;
-        const int per_group = p.group_m * n_tiles;
-        const int first_mb = (t / per_group) * p.group_m;
-        const int rig = min(p.group_m, m_real - first_mb);
-        mb = first_mb + (t % per_group) % rig;
-        nb = (t % per_group) / rig;
+        TilePos tp;
+        tile_in_group(p, x0 + slot + i * per_xcd, n_tiles, m_real, tp);
+        mb = tp.mb;
+        nb = tp.nb;
     };
     using cint = __attribute__((address_space(4))) const int32_t;  // scalar loads
     const cint* eids = (const cint*)(p.expert_ids);
@@ -1026,9 +1039,9 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
                                          static_cast<int>(lds));
     if (err != hipSuccess) return err;
     if (a.sorted)
-        hipLaunchKernelGGL((expert_gemm_dma_kernel<C, true>), grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((expert_gemm_dma_kernel<C, true>), grid, dim3(C::NW * 64), lds, stream, a);
     else
-        hipLaunchKernelGGL((expert_gemm_dma_kernel<C, false>), grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((expert_gemm_dma_kernel<C, false>), grid, dim3(C::NW * 64), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -1036,8 +1049,9 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
 using Dma128 = dma::Cfg<128, 512, 1, 4, 64>;
 // 128 tokens x 256 weight rows, 128-byte rows, 1 x 4 waves of 128 x 64
 using Dma128w = dma::Cfg<128, 256, 1, 3, 128>;
-// 256 tokens x 256 weight rows, 64-byte rows, 2 x 2 waves of 128 x 128
-using Dma256 = dma::Cfg<256, 256, 2, 5, 64>;
+// 256 tokens x 256 weight rows, 64-byte rows, 2 x 4 waves of 128 x 64 (two per SIMD:
+// one wave's MFMAs cover the other's waits)
+using Dma256 = dma::Cfg<256, 256, 2, 5, 64, 8>;
 // fp8: 128 tokens x 256 weight rows, 2 x 4 waves of 64 x 64, 3 stages
 using Fp8x128 = f8::Cfg<128, 256, 2, 4, 3>;
 
