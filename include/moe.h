@@ -197,12 +197,15 @@ moe_status_t moe_silu_and_mul(const moe_problem_t *p, const void *h,
  * GEMM1 with SiLU-and-mul fused into its epilogue: the result of
  * moe_expert_gemm(which = 1) followed by moe_silu_and_mul, bit for bit,
  * without writing h. Available where moe_expert_gemm_act_supported(p) is 1
- * (host-only, pure): fp8 weights, block_m 128, H >= 256; otherwise
- * MOE_E_UNSUPPORTED. fused_experts uses it where it is available.
- *   x [M, H] e4m3, x_scale [H/128, cap] (from moe_permute_scales), w13 and
- *   w13_scale as for fused_experts, topk_weights [M, topk] (alpha when
- *   apply_router_weight_on_input), z [cap, I] e4m3 out, z_scale [I/128, cap]
- *   fp32 out (as moe_silu_and_mul writes them).
+ * (host-only, pure): bf16 weights with block_m 128 or 256, or fp8 weights
+ * with block_m 128 and H >= 256; otherwise MOE_E_UNSUPPORTED. fused_experts
+ * uses it where it is available.
+ *   bf16: x [M, H] bf16, z [cap, I] bf16 out; x_scale, w13_scale and z_scale
+ *   are unused (may be NULL).
+ *   fp8: x [M, H] e4m3, x_scale [H/128, cap] (from moe_permute_scales), w13
+ *   and w13_scale as for fused_experts, z [cap, I] e4m3 out, z_scale
+ *   [I/128, cap] fp32 out (as moe_silu_and_mul writes them).
+ *   topk_weights [M, topk]: alpha when apply_router_weight_on_input.
  */
 int32_t moe_expert_gemm_act_supported(const moe_problem_t *p);
 moe_status_t moe_expert_gemm_act(const moe_problem_t *p, const void *x, const float *x_scale,

@@ -263,23 +263,28 @@ def moe_expert_gemm_act_supported(p: MoeProblem) -> bool:
     return bool(lib().moe_expert_gemm_act_supported(ctypes.byref(p)))
 
 
-def moe_expert_gemm_act(p: MoeProblem, x: torch.Tensor, x_scale: torch.Tensor, w13: torch.Tensor,
-                        w13_scale: torch.Tensor, sorted_token_ids: torch.Tensor,
-                        expert_ids: torch.Tensor, num_tokens_post_padded: torch.Tensor,
-                        topk_weights: torch.Tensor, z: torch.Tensor, z_scale: torch.Tensor,
-                        stream=None):
-    """GEMM1 with SiLU-and-mul fused in its epilogue (fp8, block_m 128): -> (z, z_scale)."""
+def moe_expert_gemm_act(p: MoeProblem, x: torch.Tensor, x_scale: torch.Tensor | None,
+                        w13: torch.Tensor, w13_scale: torch.Tensor | None,
+                        sorted_token_ids: torch.Tensor, expert_ids: torch.Tensor,
+                        num_tokens_post_padded: torch.Tensor, topk_weights: torch.Tensor,
+                        z: torch.Tensor, z_scale: torch.Tensor | None = None, stream=None):
+    """GEMM1 with SiLU-and-mul fused in its epilogue -> (z, z_scale).
+
+    bf16 weights (block_m 128 or 256): z [cap, I] bf16, the scales are unused.
+    fp8 weights (block_m 128): z [cap, I] e4m3 with z_scale [I/128, cap]."""
+    fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128
     cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
-    _need_size(x, _F8, p.M * p.H, "x")
-    _need_size(x_scale, _F32, (p.H // 128) * cap, "x_scale [H/128, cap]")
-    _need_size(w13, _F8, p.E * 2 * p.I * p.H, "w13")
-    _need_size(w13_scale, _F32, p.E * (2 * p.I // 128) * (p.H // 128), "w13_scale")
+    _need_size(x, _F8 if fp8 else _BF, p.M * p.H, "x")
+    _need_size(w13, _F8 if fp8 else _BF, p.E * 2 * p.I * p.H, "w13")
     _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
     _need_size(expert_ids, _I32T, cap // p.block_m, "expert_ids")
     _need_size(num_tokens_post_padded, _I32T, 1, "num_tokens_post_padded")
     _need_size(topk_weights, _F32, p.M * p.topk, "topk_weights")
-    _need_size(z, _F8, cap * p.I, "z")
-    _need_size(z_scale, _F32, (p.I // 128) * cap, "z_scale [I/128, cap]")
+    _need_size(z, _F8 if fp8 else _BF, cap * p.I, "z")
+    if fp8:
+        _need_size(x_scale, _F32, (p.H // 128) * cap, "x_scale [H/128, cap]")
+        _need_size(w13_scale, _F32, p.E * (2 * p.I // 128) * (p.H // 128), "w13_scale")
+        _need_size(z_scale, _F32, (p.I // 128) * cap, "z_scale [I/128, cap]")
     _check(lib().moe_expert_gemm_act(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(w13),
                                      _ptr(w13_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
                                      _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(z),

@@ -334,9 +334,10 @@ moe_status_t moe_expert_gemm_act(const moe_problem_t* p, const void* x, const fl
     if (st != MOE_OK) return st;
     if (!act_fused(*p)) return MOE_E_UNSUPPORTED;
     if (p->M == 0) return MOE_OK;
-    if (!x || !x_scale || !w13 || !w13_scale || !sorted_token_ids || !expert_ids ||
-        !num_tokens_post_padded || !topk_weights || !z || !z_scale)
+    const bool fp8 = p->wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    if (!x || !w13 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !topk_weights || !z)
         return MOE_E_INVALID;
+    if (fp8 && (!x_scale || !w13_scale || !z_scale)) return MOE_E_INVALID;
     return hip_status(gemm_act_stage(*p, x, x_scale, w13, w13_scale, sorted_token_ids, expert_ids,
                                      num_tokens_post_padded, topk_weights, z, z_scale,
                                      static_cast<hipStream_t>(stream)));

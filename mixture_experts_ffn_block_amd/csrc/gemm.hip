@@ -432,8 +432,9 @@ struct Cfg {
 
 }  // namespace dma
 
-template <class C, bool GATHER>
+template <class C, bool GATHER, bool ACT>
 __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p) {
+    static_assert(!ACT || GATHER, "the SiLU epilogue belongs to GEMM1");
     using namespace dma;
     constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES, TM = C::TM, TN = C::TN;
     constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR, NKS = C::NKS;
@@ -441,13 +442,16 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) u32x4_t*)smem));
 
+    // ACT: a tile covers BN / 2 output columns (z), its BN weight rows being the gate
+    // and up rows of those columns (see below)
+    constexpr int TILE_COLS = ACT ? BN / 2 : BN;
     TilePos tp;
-    if (!tile_of<BM, BN>(p, tp)) return;
+    if (!tile_of<BM, TILE_COLS>(p, tp)) return;
     const int mb = tp.mb, nb = tp.nb;
     const int64_t m0 = static_cast<int64_t>(mb) * BM;
     const int e = p.expert_ids[mb];
     if (e < 0) return;
-    const int n0 = nb * BN;
+    const int n0 = nb * TILE_COLS;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, half = lane >> 5;
@@ -474,7 +478,11 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
     for (int i = 0; i < B_INSTR; ++i) {
         const int row = (wave * B_INSTR + i) * C::ROWS_PER_COPY + cp_row;
         const int chunk = C::swz(row, cp_slot) - row * C::CH;
-        b_off[i] = min(n0 + row, p.N - 1) * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
+        // ACT: tile row r is a gate row (r / 32 even) or up row (odd) of output column
+        // n0 + 32 * (r / 64) + r % 32; gate rows are w13 rows [0, N), up rows [N, 2N)
+        const int wrow = ACT ? ((row >> 5) & 1) * p.N + min(n0 + (row >> 6) * 32 + (row & 31), p.N - 1)
+                             : min(n0 + row, p.N - 1);
+        b_off[i] = wrow * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
     }
     // LDS destinations are wave-uniform: keep them in scalar registers
     const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds_base + wave * A_INSTR * 1024);
@@ -600,8 +608,35 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
     __syncthreads();
     constexpr int TMP = TM >= 2 ? 2 : 1;  // 32-row tiles per staging pass
     static_assert(C::NW * TMP * 32 * (TN * 64 + 16) <= STAGES * C::STAGE_BYTES, "staging fits the ring");
-    store_block<TM, TN, TMP>(acc, reinterpret_cast<uint8_t*>(smem) + wave * (TMP * 32 * (TN * 64 + 16)),
-                             reinterpret_cast<uint8_t*>(p.C), m0 + arow, n0 + brow, p.ldc_bytes, p.N, lane);
+    if constexpr (ACT) {
+        // SiLU-and-mul: column tiles 2j (gate) and 2j + 1 (up) of a wave hold the same
+        // outputs; both are rounded to bf16 (the values GEMM1 would store), then
+        // z = alpha * SiLU(g) * u in fp32 (alpha = the routed item's weight in on-input
+        // mode, else 1; padding rows 0), written in place into column tile j
+        static_assert(TN % 2 == 0 && (BN / C::WN) % 64 == 0, "gate/up column tile pairs");
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int r = p.sorted[m0 + arow + tm * 32 + r32];
+            const bool real = r < p.R;
+            const float alpha = (real && p.act_on_input) ? p.act_weights[r] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < TN / 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float g = bf16_to_f32(f32_to_bf16(acc[2 * j][tm][i]));
+                    const float u = bf16_to_f32(f32_to_bf16(acc[2 * j + 1][tm][i]));
+                    acc[j][tm][i] = real ? alpha * silu_f32(g) * u : 0.0f;
+                }
+        }
+        static_assert(C::NW * TMP * 32 * (TN / 2 * 64 + 16) <= STAGES * C::STAGE_BYTES, "staging fits the ring");
+        store_block<TM, TN / 2, TMP>(reinterpret_cast<const f32x16_t(&)[TN / 2][TM]>(acc),
+                                     reinterpret_cast<uint8_t*>(smem) + wave * (TMP * 32 * (TN / 2 * 64 + 16)),
+                                     reinterpret_cast<uint8_t*>(p.C), m0 + arow, n0 + brow / 2, p.ldc_bytes,
+                                     p.N, lane);
+    } else {
+        store_block<TM, TN, TMP>(acc, reinterpret_cast<uint8_t*>(smem) + wave * (TMP * 32 * (TN * 64 + 16)),
+                                 reinterpret_cast<uint8_t*>(p.C), m0 + arow, n0 + brow, p.ldc_bytes, p.N, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1028,21 +1063,23 @@ hipError_t launch_fp8(const GemmArgs& a, hipStream_t stream) {
     return a.sorted ? launch_fp8_as<C, true, false>(a, stream) : launch_fp8_as<C, false, false>(a, stream);
 }
 
-template <class C>
-hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
-    const int n_tiles = (a.N + C::BN - 1) / C::BN;
+template <class C, bool GATHER, bool ACT>
+hipError_t launch_dma_as(const GemmArgs& a, hipStream_t stream) {
+    const int cols = ACT ? C::BN / 2 : C::BN;
+    const int n_tiles = (a.N + cols - 1) / cols;
     const dim3 grid(static_cast<unsigned>(a.m_blocks * n_tiles));
     const size_t lds = C::STAGES * C::STAGE_BYTES;
-    const void* fn = a.sorted ? reinterpret_cast<const void*>(expert_gemm_dma_kernel<C, true>)
-                              : reinterpret_cast<const void*>(expert_gemm_dma_kernel<C, false>);
-    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(lds));
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(expert_gemm_dma_kernel<C, GATHER, ACT>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (err != hipSuccess) return err;
-    if (a.sorted)
-        hipLaunchKernelGGL((expert_gemm_dma_kernel<C, true>), grid, dim3(C::NW * 64), lds, stream, a);
-    else
-        hipLaunchKernelGGL((expert_gemm_dma_kernel<C, false>), grid, dim3(C::NW * 64), lds, stream, a);
+    hipLaunchKernelGGL((expert_gemm_dma_kernel<C, GATHER, ACT>), grid, dim3(C::NW * 64), lds, stream, a);
     return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
+    if (a.act) return a.sorted ? launch_dma_as<C, true, true>(a, stream) : hipErrorInvalidValue;
+    return a.sorted ? launch_dma_as<C, true, false>(a, stream) : launch_dma_as<C, false, false>(a, stream);
 }
 
 // 128 tokens x 512 weight rows, 64-byte rows, 1 x 4 waves of 128 x 128
@@ -1071,7 +1108,8 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
 int gemm_supported_block_m(int bm) { return bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 bool gemm_act_supported(int block_m, bool fp8, int K) {
-    return fp8 && block_m == 128 && K >= 128 * (Fp8x128::STAGES - 1);
+    if (!fp8) return block_m == 128 || block_m == 256;
+    return block_m == 128 && K >= 128 * (Fp8x128::STAGES - 1);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStream_t stream) {

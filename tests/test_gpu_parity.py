@@ -191,7 +191,7 @@ def test_stages_compose_to_fused(cfg):
     z = torch.empty((cap, p.I), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16, device=DEV)
     zs = torch.empty((p.I // 128, cap), dtype=torch.float32, device=DEV) if fp8 else None
     if moe.moe_expert_gemm_act_supported(prob):
-        moe.moe_expert_gemm_act(prob, a1, a1s, d.w13q, d.w13s, s, e, npp, w, z, zs)
+        moe.moe_expert_gemm_act(prob, a1, a1s, d.w13q if fp8 else d.w13, d.w13s, s, e, npp, w, z, zs)
     else:
         h = torch.empty((cap, 2 * p.I), dtype=torch.bfloat16, device=DEV)
         moe.moe_expert_gemm(prob, 1, a1, d.w13q if fp8 else d.w13, s, e, npp, h, a1s, d.w13s)
@@ -210,38 +210,54 @@ def test_stages_compose_to_fused(cfg):
     dict(M=300, H=256, I=128, E=4, topk=2, block_m=128, wdtype="fp8",        # 2 K stages
          apply_router_weight_on_input=True),
     dict(M=1, H=512, I=256, E=4, topk=2, block_m=128, wdtype="fp8"),         # one token
+    dict(M=150, H=512, I=384, E=7, topk=3, block_m=128, wdtype="bf16"),       # 2 column tiles, ragged
+    dict(M=300, H=256, I=640, E=5, topk=2, block_m=256, wdtype="bf16"),       # 5 column tiles
+    dict(M=90, H=384, I=256, E=4, topk=2, block_m=256, wdtype="bf16",
+         apply_router_weight_on_input=True),
+    dict(M=1, H=256, I=128, E=4, topk=2, block_m=128, wdtype="bf16"),         # one token, tail tile
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_gemm_act_matches_gemm_then_act(cfg):
     # the fused SiLU epilogue gives the bits of GEMM1 (h in bf16) followed by
-    # the separate activation + quantisation pass
+    # the separate activation (+ quantisation for fp8) pass
     p = synth.Problem(**cfg)
     log(f"gemm_act {cfg}")
+    fp8 = p.wdtype == "fp8"
     d = to_dev(synth.make_inputs(p, "cpu"))
     ids, w = moe.moe_topk(d.logits, p.topk)
-    prob = moe.make_problem(p.M, p.H, p.I, p.E, p.topk, p.block_m, moe.MOE_W_FP8_E4M3_BLOCK128,
+    prob = moe.make_problem(p.M, p.H, p.I, p.E, p.topk, p.block_m,
+                            moe.MOE_W_FP8_E4M3_BLOCK128 if fp8 else moe.MOE_W_BF16,
                             p.apply_router_weight_on_input)
     assert moe.moe_expert_gemm_act_supported(prob)
     s, e, npp, inv = moe.moe_align_block_size(ids, p.E, p.block_m)
     cap, n = s.numel(), int(npp.item())
-    xq, xs = moe.moe_quant_fp8_groups(d.x)
-    xst = torch.empty((p.H // 128, cap), dtype=torch.float32, device=DEV)
-    moe.moe_permute_scales(prob, xs, s, npp, xst)
     h = torch.empty((cap, 2 * p.I), dtype=torch.bfloat16, device=DEV)
-    moe.moe_expert_gemm(prob, 1, xq, d.w13q, s, e, npp, h, xst, d.w13s)
-    z0 = torch.zeros((cap, p.I), dtype=torch.float8_e4m3fn, device=DEV)
-    zs0 = torch.zeros((p.I // 128, cap), dtype=torch.float32, device=DEV)
+    if fp8:
+        xq, xs = moe.moe_quant_fp8_groups(d.x)
+        xst = torch.empty((p.H // 128, cap), dtype=torch.float32, device=DEV)
+        moe.moe_permute_scales(prob, xs, s, npp, xst)
+        x, w13, w13s = xq, d.w13q, d.w13s
+        zdt = torch.float8_e4m3fn
+        zs0 = torch.zeros((p.I // 128, cap), dtype=torch.float32, device=DEV)
+        zs1 = torch.zeros_like(zs0)
+    else:
+        x, xst, w13, w13s = d.x, None, d.w13, None
+        zdt = torch.bfloat16
+        zs0 = zs1 = None
+    moe.moe_expert_gemm(prob, 1, x, w13, s, e, npp, h, xst, w13s)
+    z0 = torch.zeros((cap, p.I), dtype=zdt, device=DEV)
     moe.moe_silu_and_mul(prob, h, s, w, npp, z0, zs0)
-    z1 = torch.zeros_like(z0)
-    zs1 = torch.zeros_like(zs0)
-    moe.moe_expert_gemm_act(prob, xq, xst, d.w13q, d.w13s, s, e, npp, w, z1, zs1)
+    z1 = torch.full_like(z0, 1.0) if not fp8 else torch.zeros_like(z0)
+    moe.moe_expert_gemm_act(prob, x, xst, w13, w13s, s, e, npp, w, z1, zs1)
     torch.cuda.synchronize()
     assert torch.equal(z0[:n].view(torch.uint8), z1[:n].view(torch.uint8))
-    assert torch.equal(zs0[:, :n], zs1[:, :n])
+    if fp8:
+        assert torch.equal(zs0[:, :n], zs1[:, :n])
 
 
 def test_gemm_act_unsupported_cases():
-    for kw in (dict(wdtype=moe.MOE_W_BF16, block_m=128, H=512), dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128,
-               block_m=64, H=512), dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=128, H=128)):
+    for kw in (dict(wdtype=moe.MOE_W_BF16, block_m=64, H=512), dict(wdtype=moe.MOE_W_BF16, block_m=16, H=512),
+               dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=64, H=512),
+               dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=128, H=128)):
         prob = moe.make_problem(64, kw["H"], 256, 8, 2, kw["block_m"], kw["wdtype"])
         assert not moe.moe_expert_gemm_act_supported(prob)
 
