@@ -197,7 +197,7 @@ moe_status_t moe_silu_and_mul(const moe_problem_t *p, const void *h,
  * GEMM1 with SiLU-and-mul fused into its epilogue: the result of
  * moe_expert_gemm(which = 1) followed by moe_silu_and_mul, bit for bit,
  * without writing h. Available where moe_expert_gemm_act_supported(p) is 1
- * (host-only, pure): bf16 weights with block_m 128 or 256, or fp8 weights
+ * (host-only, pure): bf16 weights with block_m 16, 128 or 256, or fp8 weights
  * with block_m 128 and H >= 256; otherwise MOE_E_UNSUPPORTED. fused_experts
  * uses it where it is available.
  *   bf16: x [M, H] bf16, z [cap, I] bf16 out; x_scale, w13_scale and z_scale

@@ -152,7 +152,7 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const void* a, const float* a_
         g.z_scale = z_scale;
         g.z_scale_ld = cap;
     }
-    return launch_grouped_gemm(g, p.block_m, fp8, s);
+    return p.block_m == 16 ? launch_stream_gemm(g, s) : launch_grouped_gemm(g, p.block_m, fp8, s);
 }
 
 hipError_t act_stage(const moe_problem_t& p, const void* h, const int32_t* sorted,

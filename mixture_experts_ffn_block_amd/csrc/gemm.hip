@@ -1108,7 +1108,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
 int gemm_supported_block_m(int bm) { return bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 bool gemm_act_supported(int block_m, bool fp8, int K) {
-    if (!fp8) return block_m == 128 || block_m == 256;
+    if (!fp8) return block_m == 16 || block_m == 128 || block_m == 256;
     return block_m == 128 && K >= 128 * (Fp8x128::STAGES - 1);
 }
 

@@ -215,6 +215,9 @@ def test_stages_compose_to_fused(cfg):
     dict(M=90, H=384, I=256, E=4, topk=2, block_m=256, wdtype="bf16",
          apply_router_weight_on_input=True),
     dict(M=1, H=256, I=128, E=4, topk=2, block_m=128, wdtype="bf16"),         # one token, tail tile
+    dict(M=32, H=2048, I=768, E=128, topk=8, block_m=16, wdtype="bf16"),      # decode shape
+    dict(M=21, H=384, I=256, E=6, topk=3, block_m=16, wdtype="bf16",          # 128-byte chunks
+         apply_router_weight_on_input=True),
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_gemm_act_matches_gemm_then_act(cfg):
     # the fused SiLU epilogue gives the bits of GEMM1 (h in bf16) followed by
@@ -255,7 +258,7 @@ def test_gemm_act_matches_gemm_then_act(cfg):
 
 
 def test_gemm_act_unsupported_cases():
-    for kw in (dict(wdtype=moe.MOE_W_BF16, block_m=64, H=512), dict(wdtype=moe.MOE_W_BF16, block_m=16, H=512),
+    for kw in (dict(wdtype=moe.MOE_W_BF16, block_m=64, H=512), dict(wdtype=moe.MOE_W_BF16, block_m=32, H=512),
                dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=64, H=512),
                dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=128, H=128)):
         prob = moe.make_problem(64, kw["H"], 256, 8, 2, kw["block_m"], kw["wdtype"])
