@@ -115,6 +115,7 @@ class Step:
             self.xs = torch.empty((M, H // 128), dtype=torch.float32, device=dev)
             self.xst = torch.empty((H // 128, cap), dtype=torch.float32, device=dev)
         self.act_fused = moe.moe_expert_gemm_act_supported(self.prob)
+        self.gws = moe.gemm_workspace_for(self.prob, dev)  # split-K tail of the second GEMM
         self.w13 = d.w13q if self.fp8 else d.w13
         self.w2 = d.w2q if self.fp8 else d.w2
 
@@ -158,7 +159,7 @@ class Step:
             m.moe_silu_and_mul(p, self.h, self.sorted, self.w, self.npp, self.z, self.zs)
         ev[5].record()
         m.moe_expert_gemm(p, 2, self.z, self.w2, None, self.expert_ids, self.npp, self.o,
-                          self.zs, d.w2s)
+                          self.zs, d.w2s, workspace=self.gws)
         ev[6].record()
         m.moe_unpermute_reduce(p, self.o, self.inv, self.w, self.y)
         ev[7].record()

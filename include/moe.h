@@ -173,11 +173,20 @@ moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w1
  *   by moe_permute_scales for which = 1 and by moe_silu_and_mul for which = 2);
  *   w_scale is [E, N/128, K/128]. Every 128-wide K block's partial sum is
  *   multiplied by a_scale[block * cap + pos] * w_scale[e, n/128, block].
+ *   workspace (device, may be NULL): at least moe_expert_gemm_workspace_bytes(p)
+ *   bytes, else MOE_E_WORKSPACE. With it, which = 2 on bf16 weights (block_m
+ *   128 / 256) cuts the tiles of a last, at most half-full round of tiles into
+ *   2 or 4 K ranges, summed in fp32 in a fixed order: the result is
+ *   deterministic, and is what fused_experts computes (it always passes one);
+ *   without it the K sum runs in one pass, and the bits can differ in the last
+ *   place. Calls that share a workspace must not overlap.
  */
+size_t moe_expert_gemm_workspace_bytes(const moe_problem_t *p);  /* host, pure; 0 if none is used */
 moe_status_t moe_expert_gemm(const moe_problem_t *p, int32_t which, const void *a,
                              const float *a_scale, const void *w, const float *w_scale,
                              const int32_t *sorted_token_ids, const int32_t *expert_ids,
-                             const int32_t *num_tokens_post_padded, void *c, void *stream);
+                             const int32_t *num_tokens_post_padded, void *c, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /*
  * SiLU-and-mul ("DeepGEMM FusedMoE on Blackwell", 2.6.4; "fused_moe.py

@@ -20,7 +20,8 @@ MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
 
 EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_quant_fp8_groups",
-           "moe_workspace_bytes", "fused_experts", "moe_expert_gemm", "moe_silu_and_mul",
+           "moe_workspace_bytes", "fused_experts", "moe_expert_gemm_workspace_bytes",
+           "moe_expert_gemm", "moe_silu_and_mul",
            "moe_expert_gemm_act_supported", "moe_expert_gemm_act", "moe_permute_scales",
            "moe_unpermute_reduce", "moe_status_string")
 
@@ -58,7 +59,9 @@ def lib() -> ctypes.CDLL:
         L.fused_experts.argtypes = [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]
         PP = ctypes.POINTER(MoeProblem)
-        L.moe_expert_gemm.argtypes = [PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_expert_gemm_workspace_bytes.argtypes = [PP]
+        L.moe_expert_gemm_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_expert_gemm.argtypes = [PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_silu_and_mul.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P]
         L.moe_permute_scales.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_expert_gemm_act_supported.argtypes = [PP]
@@ -219,8 +222,11 @@ def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
                     sorted_token_ids: torch.Tensor | None, expert_ids: torch.Tensor,
                     num_tokens_post_padded: torch.Tensor, c: torch.Tensor,
                     a_scale: torch.Tensor | None = None, w_scale: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
-    """Grouped expert GEMM over the aligned layout (which = 1: x.w13^T, 2: z.w2^T)."""
+                    stream=None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped expert GEMM over the aligned layout (which = 1: x.w13^T, 2: z.w2^T).
+
+    workspace (from gemm_workspace_for) enables the split-K tail of the second GEMM, as
+    fused_experts runs it."""
     fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128
     cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
     N, K = (2 * p.I, p.H) if which == 1 else (p.H, p.I)
@@ -236,9 +242,17 @@ def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
         _need_size(w_scale, _F32, p.E * (N // 128) * (K // 128), "w_scale")
     _check(lib().moe_expert_gemm(ctypes.byref(p), which, _ptr(a), _ptr(a_scale), _ptr(w),
                                  _ptr(w_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
-                                 _ptr(num_tokens_post_padded), _ptr(c), _stream(stream)),
+                                 _ptr(num_tokens_post_padded), _ptr(c), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                 _stream(stream)),
            "moe_expert_gemm")
     return c
+
+
+def gemm_workspace_for(p: MoeProblem, device="cuda") -> torch.Tensor | None:
+    """A workspace for moe_expert_gemm (None if the configuration uses none)."""
+    n = lib().moe_expert_gemm_workspace_bytes(ctypes.byref(p))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def moe_silu_and_mul(p: MoeProblem, h: torch.Tensor, sorted_token_ids: torch.Tensor,

@@ -26,8 +26,16 @@ bool block_m_ok(int bm) { return bm == 16 || gemm_supported_block_m(bm); }
 
 struct Layout {
     int64_t cap, R;
-    int64_t sorted, expert_ids, npp, inv_perm, xq, xs, xst, ho, z, zs, total;
+    int64_t sorted, expert_ids, npp, inv_perm, xq, xs, xst, ho, z, zs, split, total;
 };
+
+// split-K workspace of the second GEMM (bf16 weights, block_m 128 / 256, the DMA
+// tiles of 64 Ki outputs): kSplitSlots fp32 partial tiles, then one counter per slot
+constexpr int64_t kTileOutputs = 128 * 512;
+int64_t split_bytes(const moe_problem_t& p) {
+    if (p.wdtype != MOE_W_BF16 || (p.block_m != 128 && p.block_m != 256)) return 0;
+    return kSplitSlots * kTileOutputs * 4 + kSplitSlots * 4;
+}
 
 Layout layout(const moe_problem_t& p) {
     Layout L{};
@@ -47,6 +55,7 @@ Layout layout(const moe_problem_t& p) {
     L.ho = take(h_bytes > o_bytes ? h_bytes : o_bytes);
     L.z = take(L.cap * p.I * (fp8 ? 1 : 2));
     L.zs = fp8 ? take(L.cap * (p.I / 128) * 4) : -1;   // [I/128, cap]
+    L.split = split_bytes(p) ? take(split_bytes(p)) : -1;
     L.total = off;
     return L;
 }
@@ -78,7 +87,8 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_
 // which == 2: C[pos, :H]  = A[pos] w2[e]^T
 hipError_t gemm_stage(const moe_problem_t& p, int which, const void* a, const float* a_scale,
                       const void* w, const float* w_scale, const int32_t* sorted,
-                      const int32_t* expert_ids, const int32_t* npp, void* c, hipStream_t s) {
+                      const int32_t* expert_ids, const int32_t* npp, void* c, void* split_ws,
+                      hipStream_t s) {
     const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
     const int esz = fp8 ? 1 : 2;  // bytes per weight / activation element
     const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
@@ -107,6 +117,15 @@ hipError_t gemm_stage(const moe_problem_t& p, int which, const void* a, const fl
         g.w_scale = w_scale;
         g.w_scale_expert = static_cast<int64_t>(N / 128) * (K / 128);
         g.scale_groups = K / 128;
+    }
+    if (which == 2 && split_ws != nullptr && split_bytes(p) > 0) {
+        g.part = static_cast<float*>(split_ws);
+        g.part_cnt = reinterpret_cast<int*>(static_cast<uint8_t*>(split_ws) + kSplitSlots * kTileOutputs * 4);
+        g.part_slots = kSplitSlots;
+        g.n_cu = concurrent_tiles();
+        // the counters start at zero (a kernel, not a memset: callers may capture this)
+        const hipError_t err = launch_zero_i32(g.part_cnt, kSplitSlots, s);
+        if (err != hipSuccess) return err;
     }
     return p.block_m == 16 ? launch_stream_gemm(g, s) : launch_grouped_gemm(g, p.block_m, fp8, s);
 }
@@ -294,21 +313,27 @@ moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w1
                              topk_weights, z, zs, s);
         if (err != hipSuccess) return MOE_E_HIP;
     } else {
-        err = gemm_stage(*p, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, s);
+        err = gemm_stage(*p, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, nullptr, s);
         if (err != hipSuccess) return MOE_E_HIP;
         err = act_stage(*p, ho, sorted, topk_weights, npp, z, zs, s);
         if (err != hipSuccess) return MOE_E_HIP;
     }
     err = gemm_stage(*p, 2, z, reinterpret_cast<const float*>(ws + L.zs), w2, w2_scale, sorted,
-                     expert_ids, npp, ho, s);
+                     expert_ids, npp, ho, L.split >= 0 ? ws + L.split : nullptr, s);
     if (err != hipSuccess) return MOE_E_HIP;
     return hip_status(reduce_stage(*p, ho, inv_perm, topk_weights, y, s));
+}
+
+size_t moe_expert_gemm_workspace_bytes(const moe_problem_t* p) {
+    if (check_problem(p) != MOE_OK) return 0;
+    return static_cast<size_t>(split_bytes(*p));
 }
 
 moe_status_t moe_expert_gemm(const moe_problem_t* p, int32_t which, const void* a,
                              const float* a_scale, const void* w, const float* w_scale,
                              const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                             const int32_t* num_tokens_post_padded, void* c, void* stream) {
+                             const int32_t* num_tokens_post_padded, void* c, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     const moe_status_t st = check_problem(p);
     if (st != MOE_OK) return st;
     if (which != 1 && which != 2) return MOE_E_INVALID;
@@ -317,8 +342,9 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, int32_t which, const void* 
     if (!a || !w || !expert_ids || !num_tokens_post_padded || !c) return MOE_E_INVALID;
     if (which == 1 && !sorted_token_ids) return MOE_E_INVALID;
     if (fp8 && (!a_scale || !w_scale)) return MOE_E_INVALID;
+    if (workspace != nullptr && workspace_bytes < static_cast<size_t>(split_bytes(*p))) return MOE_E_WORKSPACE;
     return hip_status(gemm_stage(*p, which, a, a_scale, w, w_scale, sorted_token_ids, expert_ids,
-                                 num_tokens_post_padded, c, static_cast<hipStream_t>(stream)));
+                                 num_tokens_post_padded, c, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_expert_gemm_act_supported(const moe_problem_t* p) {

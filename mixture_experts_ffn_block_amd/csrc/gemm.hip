@@ -154,6 +154,55 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, TilePos& t) {
     return true;
 }
 
+// Split-K of the last round (for the DMA-tiled GEMM without a gather). With
+// W = n_cu workgroups running at once and T real tiles, T = F W + tail: the F W
+// tiles of the full rounds run whole, and when the tail would fill at most half
+// a round, each tail tile is cut into S = 2 or 4 K ranges that fill one round
+// (S divides the K stages; tail S <= part_slots). Workgroup h < F W takes tile h
+// in the XCD-contiguous order of the F W tiles. The S ranges of a tail tile run
+// on one XCD (workgroup h runs on XCD h % 8, and F W is a multiple of 8): unit
+// u = h - F W serves tail tile j = u % 8 + 8 ((u / 8) / S), K range (u / 8) % S,
+// so its partial tiles and its counter stay in that XCD's L2. The grid has
+// W + 32 extra workgroups for this (8 ceil(tail / 8) S <= W + 7 S).
+struct SplitPos {
+    int tile, S, chunk, slot, tail_tile;  // slot: partial tile index; -1 for a whole tile
+};
+template <int BM, int COLS>
+__device__ __forceinline__ bool split_tile_of(const GemmArgs& p, int KT, TilePos& t, SplitPos& sp) {
+    const int n_tiles = (p.N + COLS - 1) / COLS;
+    const int m_real = min(p.m_blocks, (*p.npp + BM - 1) / BM);
+    const int total = m_real * n_tiles;
+    const int hw = blockIdx.x;
+    const int W = p.n_cu, F = total / W, tail = total - F * W;
+    int S = 1;
+    if (p.part != nullptr && tail > 0 && 2 * tail <= W) {
+        S = 4 * tail <= W ? 4 : 2;
+        while (S > 1 && (KT % S != 0 || tail * S > p.part_slots)) S >>= 1;
+    }
+    const int main_tiles = S == 1 ? total : F * W;
+    sp.S = 1;
+    sp.chunk = 0;
+    sp.slot = -1;
+    sp.tail_tile = -1;
+    if (hw < main_tiles) {
+        const int xcd = hw & 7, q8 = main_tiles >> 3, rem = main_tiles & 7;
+        sp.tile = xcd * q8 + min(xcd, rem) + (hw >> 3);
+    } else if (S > 1) {
+        const int u = hw - main_tiles, q = u >> 3;
+        const int j = (u & 7) + 8 * (q / S);
+        if (j >= tail) return false;
+        sp.S = S;
+        sp.chunk = q % S;
+        sp.tail_tile = j;
+        sp.slot = j * S + sp.chunk;
+        sp.tile = main_tiles + j;
+    } else {
+        return false;
+    }
+    tile_in_group(p, sp.tile, n_tiles, m_real, t);
+    return true;
+}
+
 // Both operands are staged through LDS: 8 consecutive lanes load one row's
 // 128-byte K slice, so every global load instruction reads whole cache lines.
 // The next K tile is loaded into registers while the current one is
@@ -445,8 +494,14 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
     // ACT: a tile covers BN / 2 output columns (z), its BN weight rows being the gate
     // and up rows of those columns (see below)
     constexpr int TILE_COLS = ACT ? BN / 2 : BN;
+    constexpr bool SPLIT = !GATHER;  // the split-K tail applies to the second GEMM
     TilePos tp;
-    if (!tile_of<BM, TILE_COLS>(p, tp)) return;
+    SplitPos sp{0, 1, 0, -1, -1};
+    if constexpr (SPLIT) {
+        if (!split_tile_of<BM, TILE_COLS>(p, p.K / C::KS, tp, sp)) return;
+    } else {
+        if (!tile_of<BM, TILE_COLS>(p, tp)) return;
+    }
     const int mb = tp.mb, nb = tp.nb;
     const int64_t m0 = static_cast<int64_t>(mb) * BM;
     const int e = p.expert_ids[mb];
@@ -488,7 +543,14 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
     const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds_base + wave * A_INSTR * 1024);
     const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_base + C::A_BYTES + wave * B_INSTR * 1024);
 
-    const int KT = p.K / C::KS;
+    // a split tile covers K stages [chunk KT / S, (chunk + 1) KT / S)
+    const int KT = p.K / C::KS / sp.S;
+    if (sp.S > 1) {
+        const int64_t k_off = static_cast<int64_t>(sp.chunk) * KT * C::ROWB;
+#pragma unroll
+        for (int i = 0; i < A_INSTR; ++i) a_src[i] += k_off;
+        w_base += k_off;
+    }
     // copy group j of K tile kt: groups of 4 (or 2) consecutive 1 KB copies
     constexpr int AG = A_INSTR >= 4 ? 4 : A_INSTR, BG = B_INSTR >= 4 ? 4 : B_INSTR;
     static_assert(A_INSTR % AG == 0 && B_INSTR % BG == 0, "whole copy groups");
@@ -608,6 +670,50 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
     __syncthreads();
     constexpr int TMP = TM >= 2 ? 2 : 1;  // 32-row tiles per staging pass
     static_assert(C::NW * TMP * 32 * (TN * 64 + 16) <= STAGES * C::STAGE_BYTES, "staging fits the ring");
+    if constexpr (SPLIT) {
+        if (sp.slot >= 0) {
+            // Every K range writes its fp32 partial tile (in accumulator register
+            // order: index ((wave, tn, tm, r), lane)), then counts itself in; the
+            // last to arrive sums the S partials in range order (deterministic),
+            // stores the tile and resets the counter. All ranges of a tile run on
+            // one XCD, whose L2 holds the partials and the counter: stores are
+            // complete in L2 once vmcnt drains (the L1 writes through), the
+            // counter's atomic is performed in L2, and the partials were never in
+            // the reading CU's L1 (each is read once, by the last arrival).
+            constexpr int TILE_F = C::NW * TN * TM * 16 * 64;
+            static_assert(TILE_F == BM * BN, "one partial per output");
+            float* part = p.part + static_cast<int64_t>(sp.slot) * TILE_F;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        part[(((wave * TN + tn) * TM + tm) * 16 + r) * 64 + lane] = acc[tn][tm][r];
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            int* cnt = p.part_cnt + sp.tail_tile;
+            int* flag = reinterpret_cast<int*>(smem);
+            if (tid == 0) *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const int arrived = *flag;
+            if (arrived != sp.S - 1) return;
+            const float* first = p.part + static_cast<int64_t>(sp.slot - sp.chunk) * TILE_F;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t idx = (((wave * TN + tn) * TM + tm) * 16 + r) * 64 + lane;
+                        float v = first[idx];
+                        for (int c = 1; c < sp.S; ++c) v += first[static_cast<int64_t>(c) * TILE_F + idx];
+                        acc[tn][tm][r] = v;
+                    }
+            if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();  // the flag's LDS word is reused by the staging below
+        }
+    }
     if constexpr (ACT) {
         // SiLU-and-mul: column tiles 2j (gate) and 2j + 1 (up) of a wave hold the same
         // outputs; both are rounded to bf16 (the values GEMM1 would store), then
@@ -1033,6 +1139,11 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
     }
 }
 
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
 // one workgroup per CU (multiple of 8 so that every XCD gets the same count)
 int persistent_grid() {
     static int cus[64] = {};
@@ -1067,7 +1178,9 @@ template <class C, bool GATHER, bool ACT>
 hipError_t launch_dma_as(const GemmArgs& a, hipStream_t stream) {
     const int cols = ACT ? C::BN / 2 : C::BN;
     const int n_tiles = (a.N + cols - 1) / cols;
-    const dim3 grid(static_cast<unsigned>(a.m_blocks * n_tiles));
+    // the split-K tail adds one round of workgroups (at most n_cu + 32 of them)
+    const int extra = (!GATHER && a.part != nullptr) ? a.n_cu + 32 : 0;
+    const dim3 grid(static_cast<unsigned>(a.m_blocks * n_tiles + extra));
     const size_t lds = C::STAGES * C::STAGE_BYTES;
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(expert_gemm_dma_kernel<C, GATHER, ACT>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -1104,6 +1217,14 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int concurrent_tiles() { return persistent_grid(); }
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
 
 int gemm_supported_block_m(int bm) { return bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 

@@ -38,7 +38,16 @@ struct GemmArgs {
     int act_on_input;
     float* z_scale;            // fp8: [N/128, z_scale_ld] group-major
     int64_t z_scale_ld;
+    // split-K of a last, partly filled round of tiles (non-gathered GEMM on the DMA
+    // tiles): part holds part_slots fp32 partial tiles, part_cnt one arrival counter
+    // per split tile (zero before the launch; the last arrival resets it); null: off
+    float* part;
+    int* part_cnt;
+    int part_slots;
+    int n_cu;                  // workgroups of this kernel that run at once (one per CU)
 };
+
+constexpr int kSplitSlots = 256;  // partial tiles of the split-K workspace
 
 hipError_t launch_topk_softmax(const float* logits, int64_t M, int E, int k, int renormalize,
                                int32_t* ids, float* weights, hipStream_t stream);
@@ -59,5 +68,7 @@ hipError_t launch_quant_fp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q,
 hipError_t launch_permute_scales(const float* scale, int groups, int topk, int R,
                                  const int32_t* sorted, const int32_t* npp, int64_t cap,
                                  float* out, hipStream_t stream);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream);
+int concurrent_tiles();  // workgroups of the LDS-tiled GEMMs that run at once
 hipError_t launch_reduce(const bf16_t* o, const int32_t* inv_perm, const float* weights, int64_t M,
                          int k, int H, int use_weights, bf16_t* y, hipStream_t stream);

@@ -197,7 +197,8 @@ def test_stages_compose_to_fused(cfg):
         moe.moe_expert_gemm(prob, 1, a1, d.w13q if fp8 else d.w13, s, e, npp, h, a1s, d.w13s)
         moe.moe_silu_and_mul(prob, h, s, w, npp, z, zs)
     o = torch.empty((cap, p.H), dtype=torch.bfloat16, device=DEV)
-    moe.moe_expert_gemm(prob, 2, z, d.w2q if fp8 else d.w2, None, e, npp, o, zs, d.w2s)
+    moe.moe_expert_gemm(prob, 2, z, d.w2q if fp8 else d.w2, None, e, npp, o, zs, d.w2s,
+                        workspace=moe.gemm_workspace_for(prob, DEV))
     y = torch.empty_like(d.x)
     moe.moe_unpermute_reduce(prob, o, inv, w, y)
     torch.cuda.synchronize()
