@@ -394,12 +394,22 @@ namespace dma {
 // Copies of 1 KB each into consecutive 1 KB LDS blocks starting at `lds`. M0
 // holds the LDS base; the instruction offset is added to both the LDS and the
 // global address, so copy i passes its global address minus i KB. One M0 write
-// serves up to four copies (the offset field reaches 4095).
+// serves up to four copies (the offset field reaches 4095); groups of 1, 2 or 4.
 template <int N>
 __device__ __forceinline__ void copy_group(const uint8_t* const (&g)[N], uint32_t lds) {
-    static_assert(N == 2 || N == 4, "groups of 2 or 4 copies");
+    static_assert(N == 1 || N == 2 || N == 4, "groups of 1, 2 or 4 copies");
     uint32_t saved;
-    if constexpr (N == 4)
+    if constexpr (N == 1)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %2, off\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(lds), "v"(g[0])
+            : "memory");
+    else if constexpr (N == 4)
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
             "s_mov_b32 m0, %1\n\t"
@@ -1195,8 +1205,8 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
     return a.sorted ? launch_dma_as<C, true, false>(a, stream) : launch_dma_as<C, false, false>(a, stream);
 }
 
-// 128 tokens x 512 weight rows, 64-byte rows, 1 x 4 waves of 128 x 128
-using Dma128 = dma::Cfg<128, 512, 1, 4, 64>;
+// 128 tokens x 512 weight rows, 64-byte rows, 1 x 8 waves of 128 x 64 (two per SIMD)
+using Dma128 = dma::Cfg<128, 512, 1, 4, 64, 8>;
 // 128 tokens x 256 weight rows, 128-byte rows, 1 x 4 waves of 128 x 64
 using Dma128w = dma::Cfg<128, 256, 1, 3, 128>;
 // 256 tokens x 256 weight rows, 64-byte rows, 2 x 4 waves of 128 x 64 (two per SIMD:
