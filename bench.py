@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill_m4096", choices=list(synth.WORKLOADS))
     ap.add_argument("--block-m", type=int, default=None, help="override the workload's block_m")
+    ap.add_argument("--weight-layout", default="auto", choices=("auto", "rows", "mfma16"),
+                    help="element order of w13/w2: auto = the MFMA16 order where the library "
+                         "supports it (bf16, block_m 16), else row-major")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -84,15 +87,20 @@ def parse():
 class Step:
     """Device buffers and the two ways of running one step."""
 
-    def __init__(self, p: synth.Problem, d: synth.Inputs):
+    def __init__(self, p: synth.Problem, d: synth.Inputs, layout: str = "auto"):
         import mixture_experts_ffn_block_amd as moe
         self.moe, self.p, self.d = moe, p, d
         self.fp8 = p.wdtype == "fp8"
         dev = d.x.device
         M, H, I, E, k, B = p.M, p.H, p.I, p.E, p.topk, p.block_m
-        self.prob = moe.make_problem(M, H, I, E, k, B,
-                                     moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16,
-                                     p.apply_router_weight_on_input)
+        wdt = moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16
+        rows = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input)
+        packable = not self.fp8 and B == 16
+        if layout == "mfma16" and not packable:
+            raise SystemExit("--weight-layout mfma16 needs bf16 weights and block_m 16")
+        self.layout = "mfma16" if packable and layout in ("auto", "mfma16") else "rows"
+        self.wl = moe.MOE_LAYOUT_MFMA16 if self.layout == "mfma16" else moe.MOE_LAYOUT_ROWS
+        self.prob = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input, self.wl)
         self.ids = torch.empty((M, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((M, k), dtype=torch.float32, device=dev)
         self.y = torch.empty_like(d.x)
@@ -118,13 +126,16 @@ class Step:
         self.gws = moe.gemm_workspace_for(self.prob, dev)  # split-K tail of the second GEMM
         self.w13 = d.w13q if self.fp8 else d.w13
         self.w2 = d.w2q if self.fp8 else d.w2
+        if self.layout == "mfma16":  # weight preparation, once, outside every timed region
+            self.w13 = moe.moe_pack_weights(rows, 1, d.w13)
+            self.w2 = moe.moe_pack_weights(rows, 2, d.w2)
 
     def fused(self):
         m, d = self.moe, self.d
         m.moe_topk(d.logits, self.p.topk, out=(self.ids, self.w))
         m.fused_experts(d.x, self.w13, self.w2, self.ids, self.w, self.p.block_m,
                         d.w13s, d.w2s, self.p.apply_router_weight_on_input, out=self.y,
-                        workspace=self.ws)
+                        workspace=self.ws, weight_layout=self.wl)
 
     STAGES = ("router", "quant", "align", "gemm1", "act", "gemm2", "reduce")
 
@@ -250,7 +261,7 @@ def main():
     p = synth.Problem.named(args.workload, **over)
     print(f"# workload {args.workload}: {p}", file=sys.stderr, flush=True)
     d = synth.make_inputs(p, "cuda")
-    st = Step(p, d)
+    st = Step(p, d, args.weight_layout)
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -317,6 +328,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": args.workload, "M": p.M, "H": p.H, "I": p.I, "E": p.E,
                    "topk": p.topk, "block_m": p.block_m, "weights": p.wdtype,
+                   "weight_layout": st.layout,
                    "experts_touched": touched, "seed": p.seed},
         "step_roofline_frac": round(t_star / (ms * 1e-3), 4),
         "roofline": roof,

@@ -33,9 +33,10 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_E_INVALID = 1,     /* null pointer, negative size, topk outside [1, min(E, 32)] */
-    MOE_E_UNSUPPORTED = 2, /* E > 256, H or I not a multiple of 128, unknown block_m or
-                              dtype, fp8 with block_m 16 or 256, more than 2^31 routed rows,
-                              one expert's w13 of 2 GiB or more */
+    MOE_E_UNSUPPORTED = 2, /* E > 256, H or I not a multiple of 128, unknown block_m,
+                              dtype or weight layout, fp8 with block_m 16 or 256, the
+                              MFMA16 layout other than bf16 with block_m 16, more than
+                              2^31 routed rows, one expert's w13 of 2 GiB or more */
     MOE_E_WORKSPACE = 3,   /* workspace_bytes < moe_workspace_bytes(p) */
     MOE_E_HIP = 4          /* a kernel launch failed (hipGetLastError) */
 } moe_status_t;
@@ -45,6 +46,27 @@ typedef enum {
     MOE_W_FP8_E4M3_BLOCK128 = 1  /* e4m3 weights with one fp32 scale per 128x128 block;
                                     activations quantised per token per 128 columns */
 } moe_wdtype_t;
+
+/*
+ * Element order of w13 and w2 in memory. Weights are prepared once after
+ * loading into the order the kernel reads best ("DeepGEMM FusedMoE on
+ * Blackwell", 2.8 (c): expert weights and scales are post-processed into the
+ * kernel's packed layout; "vLLM modular_kernel.py notes", 10.1: expert
+ * weights may arrive in a 6-D packed layout).
+ *   MOE_LAYOUT_ROWS:   w [E, N, K] row-major (K contiguous).
+ *   MOE_LAYOUT_MFMA16: the same E*N*K values, each 16-row x 32-column block
+ *     stored as the 1 KB operand of one 16x16x32 bf16 matrix-core step:
+ *       packed[e][n/16][k/32][(k%32)/8][n%16][k%8] = w[e][n][k],
+ *     i.e. w.view(E, N/16, 16, K/32, 4, 8).permute(0, 1, 3, 4, 2, 5).
+ *     A 16-row tile is then one contiguous run along K, and every 1 KB piece
+ *     is read by one load instruction. bf16 weights with block_m 16 only
+ *     (the decode path, which is bound by streaming the weights from HBM).
+ *     Written by moe_pack_weights.
+ */
+typedef enum {
+    MOE_LAYOUT_ROWS = 0,
+    MOE_LAYOUT_MFMA16 = 1
+} moe_wlayout_t;
 
 /* Sizes and options of one fused_experts call. */
 typedef struct {
@@ -57,6 +79,7 @@ typedef struct {
     int32_t wdtype;    /* moe_wdtype_t */
     int32_t apply_router_weight_on_input; /* 0: weight the expert outputs in the final sum;
                                              1: weight the SiLU-and-mul output instead */
+    int32_t weight_layout; /* moe_wlayout_t of w13 and w2 (0: row-major) */
 } moe_problem_t;
 
 /*
@@ -136,6 +159,7 @@ size_t moe_workspace_bytes(const moe_problem_t *p);
  *   w13_scale     [E, 2I/128, H/128] fp32 for fp8 (NULL is MOE_E_INVALID), ignored for bf16
  *   w2            [E, H, I] bf16 or e4m3
  *   w2_scale      [E, H/128, I/128] fp32 for fp8 (NULL is MOE_E_INVALID), ignored for bf16
+ *                 (w13 and w2 in the element order p->weight_layout names)
  *   topk_ids      [M, topk] int32, topk_weights [M, topk] fp32 (as from moe_topk)
  *   y             [M, H] bf16 out; may be the same buffer as x (in place)
  *   workspace     device scratch of at least moe_workspace_bytes(p) bytes,
@@ -156,6 +180,7 @@ moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w1
  * `p` has the same meaning as for fused_experts; cap is
  * moe_align_capacity(M, topk, E, block_m); the layout arrays are those of
  * moe_align_block_size. Rows at or past num_tokens_post_padded are skipped.
+ * Weights are in the element order p->weight_layout names.
  */
 
 /*
@@ -245,6 +270,18 @@ moe_status_t moe_permute_scales(const moe_problem_t *p, const float *scale,
  */
 moe_status_t moe_unpermute_reduce(const moe_problem_t *p, const void *o, const int32_t *inv_perm,
                                   const float *topk_weights, void *y, void *stream);
+
+/*
+ * Weight preparation: rewrite one weight tensor from MOE_LAYOUT_ROWS into
+ * MOE_LAYOUT_MFMA16 (a permutation: the bits of every element are kept).
+ *   which = 1: w = w13 [E, 2I, H];  which = 2: w = w2 [E, H, I]   (bf16)
+ *   w_packed: the same number of bytes, out; must not overlap w.
+ * p->wdtype must be MOE_W_BF16; p->M, block_m and weight_layout are not used
+ * (beyond the problem's validity). Run once, before fused_experts is called
+ * with weight_layout = MOE_LAYOUT_MFMA16.
+ */
+moe_status_t moe_pack_weights(const moe_problem_t *p, int32_t which, const void *w,
+                              void *w_packed, void *stream);
 
 /* Host-only: a static, human-readable name of a status code. */
 const char *moe_status_string(moe_status_t s);

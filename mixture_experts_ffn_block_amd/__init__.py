@@ -18,18 +18,20 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_MFMA16 = 0, 1
 
 EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_quant_fp8_groups",
            "moe_workspace_bytes", "fused_experts", "moe_expert_gemm_workspace_bytes",
            "moe_expert_gemm", "moe_silu_and_mul",
            "moe_expert_gemm_act_supported", "moe_expert_gemm_act", "moe_permute_scales",
-           "moe_unpermute_reduce", "moe_status_string")
+           "moe_unpermute_reduce", "moe_pack_weights", "moe_status_string")
 
 
 class MoeProblem(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("block_m", ctypes.c_int32),
-                ("wdtype", ctypes.c_int32), ("apply_router_weight_on_input", ctypes.c_int32)]
+                ("wdtype", ctypes.c_int32), ("apply_router_weight_on_input", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -68,11 +70,12 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_gemm_act_supported.restype = _I32
         L.moe_expert_gemm_act.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_unpermute_reduce.argtypes = [PP, _P, _P, _P, _P, _P]
+        L.moe_pack_weights.argtypes = [PP, _I32, _P, _P, _P]
         L.moe_status_string.argtypes = [_I32]
         L.moe_status_string.restype = ctypes.c_char_p
         for name in ("moe_topk", "moe_align_block_size", "moe_quant_fp8_groups", "fused_experts",
                      "moe_expert_gemm", "moe_silu_and_mul", "moe_permute_scales",
-                     "moe_expert_gemm_act", "moe_unpermute_reduce"):
+                     "moe_expert_gemm_act", "moe_unpermute_reduce", "moe_pack_weights"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -169,8 +172,9 @@ def moe_quant_fp8_groups(x: torch.Tensor, stream=None):
     return q, s
 
 
-def make_problem(M, H, I, E, topk, block_m, wdtype=MOE_W_BF16, on_input=False) -> MoeProblem:
-    return MoeProblem(M, H, I, E, topk, block_m, wdtype, int(on_input))
+def make_problem(M, H, I, E, topk, block_m, wdtype=MOE_W_BF16, on_input=False,
+                 weight_layout=MOE_LAYOUT_ROWS) -> MoeProblem:
+    return MoeProblem(M, H, I, E, topk, block_m, wdtype, int(on_input), weight_layout)
 
 
 def moe_workspace_bytes(p: MoeProblem) -> int:
@@ -186,8 +190,10 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
                   topk_weights: torch.Tensor, block_m: int, w13_scale: torch.Tensor | None = None,
                   w2_scale: torch.Tensor | None = None, apply_router_weight_on_input=False,
                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                  stream=None) -> torch.Tensor:
-    """y = fused MoE expert forward (bf16 [M, H]). `out` may be `x` (in place)."""
+                  stream=None, weight_layout=MOE_LAYOUT_ROWS) -> torch.Tensor:
+    """y = fused MoE expert forward (bf16 [M, H]). `out` may be `x` (in place).
+
+    weight_layout MOE_LAYOUT_MFMA16: w13 and w2 come from moe_pack_weights (same shapes)."""
     _need(x, torch.bfloat16, "x")
     fp8 = w13.dtype == torch.float8_e4m3fn
     wdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
@@ -204,7 +210,8 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
             or topk_ids.shape[0] != M:
         raise ValueError("fused_experts: inconsistent shapes")
     p = make_problem(M, H, N2 // 2, E, topk_ids.shape[1], block_m,
-                     MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16, apply_router_weight_on_input)
+                     MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16, apply_router_weight_on_input,
+                     weight_layout)
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
@@ -331,3 +338,17 @@ def moe_unpermute_reduce(p: MoeProblem, o: torch.Tensor, inv_perm: torch.Tensor,
                                       _ptr(topk_weights), _ptr(y), _stream(stream)),
            "moe_unpermute_reduce")
     return y
+
+
+def moe_pack_weights(p: MoeProblem, which: int, w: torch.Tensor, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """Rewrite bf16 w13 (which = 1, [E, 2I, H]) or w2 (which = 2, [E, H, I]) into the
+    MOE_LAYOUT_MFMA16 element order; the result has the same shape and bytes."""
+    N, K = (2 * p.I, p.H) if which == 1 else (p.H, p.I)
+    _need_size(w, _BF, p.E * N * K, "w")
+    if out is None:
+        out = torch.empty_like(w)
+    _need_size(out, _BF, p.E * N * K, "out")
+    _check(lib().moe_pack_weights(ctypes.byref(p), which, _ptr(w), _ptr(out), _stream(stream)),
+           "moe_pack_weights")
+    return out

@@ -69,6 +69,10 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->wdtype != MOE_W_BF16 && p->wdtype != MOE_W_FP8_E4M3_BLOCK128) return MOE_E_UNSUPPORTED;
     if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && (p->block_m == 16 || p->block_m == 256))
         return MOE_E_UNSUPPORTED;
+    if (p->weight_layout != MOE_LAYOUT_ROWS && p->weight_layout != MOE_LAYOUT_MFMA16)
+        return MOE_E_UNSUPPORTED;
+    if (p->weight_layout == MOE_LAYOUT_MFMA16 && (p->wdtype != MOE_W_BF16 || p->block_m != 16))
+        return MOE_E_UNSUPPORTED;
     // one expert's weight matrix is addressed with 32-bit byte offsets
     const int64_t esz = p->wdtype == MOE_W_FP8_E4M3_BLOCK128 ? 1 : 2;
     if (int64_t(2) * p->I * p->H * esz >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
@@ -111,6 +115,7 @@ hipError_t gemm_stage(const moe_problem_t& p, int which, const void* a, const fl
     g.K = K;
     g.m_blocks = static_cast<int>(cap / p.block_m);
     g.group_m = kGroupM;
+    g.w_packed = p.weight_layout == MOE_LAYOUT_MFMA16 ? 1 : 0;
     if (fp8) {
         g.a_scale = a_scale;
         g.a_scale_ld = cap;
@@ -159,6 +164,7 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const void* a, const float* a_
     g.K = p.H;
     g.m_blocks = static_cast<int>(cap / p.block_m);
     g.group_m = kGroupM;
+    g.w_packed = p.weight_layout == MOE_LAYOUT_MFMA16 ? 1 : 0;
     g.act = 1;
     g.act_weights = weights;
     g.act_on_input = p.apply_router_weight_on_input ? 1 : 0;
@@ -392,6 +398,22 @@ moe_status_t moe_permute_scales(const moe_problem_t* p, const float* scale,
     if (!scale || !sorted_token_ids || !num_tokens_post_padded || !out) return MOE_E_INVALID;
     return hip_status(permute_stage(*p, scale, sorted_token_ids, num_tokens_post_padded, out,
                                     static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_pack_weights(const moe_problem_t* p, int32_t which, const void* w, void* w_packed,
+                              void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (which != 1 && which != 2) return MOE_E_INVALID;
+    if (p->wdtype != MOE_W_BF16) return MOE_E_UNSUPPORTED;
+    if (!w || !w_packed) return MOE_E_INVALID;
+    const int N = which == 1 ? 2 * p->I : p->H, K = which == 1 ? p->H : p->I;
+    const int64_t bytes = static_cast<int64_t>(p->E) * N * K * 2;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_packed);
+    if (a < b + bytes && b < a + bytes) return MOE_E_INVALID;  // overlapping buffers
+    if (a % 16 || b % 16) return MOE_E_INVALID;
+    return hip_status(launch_pack_mfma16(static_cast<const bf16_t*>(w), static_cast<bf16_t*>(w_packed),
+                                         p->E, N, K, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_unpermute_reduce(const moe_problem_t* p, const void* o, const int32_t* inv_perm,

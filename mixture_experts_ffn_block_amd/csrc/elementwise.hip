@@ -12,7 +12,10 @@
 //   weights in fp32, then cast to bf16); "vLLM modular_kernel.py notes" 7.3.3
 //   (multiply by topk_weights, then sum over the top-k dimension).
 //
-// All three are HBM-bound; every thread moves 16-byte vectors.
+// * Weight packing: "DeepGEMM FusedMoE on Blackwell", 2.8 (c) (weights are
+//   rewritten once after loading into the layout the kernel reads).
+//
+// All are HBM-bound; every thread moves 16-byte vectors.
 #include "common.h"
 #include "kernels.h"
 
@@ -159,7 +162,34 @@ __global__ __launch_bounds__(256) void reduce_kernel(const bf16_t* __restrict__ 
     *reinterpret_cast<u32x4_t*>(y + t * H + n0) = out;
 }
 
+// ------------------------------------------------------------- weight pack --
+// One thread per 16-byte piece of the packed tensor (coalesced writes): piece
+// (e, tile, kf, lane) holds row 16 tile + (lane & 15), columns 32 kf + 8 (lane >> 4)
+// .. + 7 of expert e.
+__global__ __launch_bounds__(256) void pack_mfma16_kernel(const uint4* __restrict__ w,
+                                                          uint4* __restrict__ wp, int64_t pieces,
+                                                          int N, int K) {
+    const int64_t kfs = K / 32, tiles = N / 16;
+    for (int64_t d = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; d < pieces;
+         d += static_cast<int64_t>(gridDim.x) * 256) {
+        const int lane = static_cast<int>(d & 63);
+        const int64_t f = d >> 6;
+        const int64_t kf = f % kfs, tile = (f / kfs) % tiles, e = f / (kfs * tiles);
+        const int64_t n = tile * 16 + (lane & 15), k = kf * 32 + 8 * (lane >> 4);
+        wp[d] = w[((e * N + n) * K + k) / 8];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_pack_mfma16(const bf16_t* w, bf16_t* wp, int64_t E, int N, int K, hipStream_t stream) {
+    const int64_t pieces = E * N * K / 8;
+    const int64_t blocks = ceil_div(pieces, 256);
+    const dim3 grid(static_cast<unsigned>(blocks < 65536 ? blocks : 65536));
+    hipLaunchKernelGGL(pack_mfma16_kernel, grid, dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(w), reinterpret_cast<uint4*>(wp), pieces, N, K);
+    return hipGetLastError();
+}
 
 hipError_t launch_silu_mul_bf16(const bf16_t* h, bf16_t* z, const int32_t* sorted,
                                 const float* weights, int R, int I, int64_t cap,

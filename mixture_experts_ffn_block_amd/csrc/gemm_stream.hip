@@ -14,12 +14,28 @@
 // s gives lane group k = lane / 16 the piece at 64*s + 16*k, so each load
 // instruction reads 64 contiguous bytes of each of its 16 rows. Both
 // operands assign the same K index to the same (lane, register) slot, so the
-// MFMA's sum over K is exact regardless of the order the slots take. The next chunk is loaded
-// while the current one is multiplied. The token rows (tiny) are re-read by
-// every wave from L2; the weights stream from HBM once per expert block.
+// MFMA's sum over K is exact regardless of the order the slots take. Chunks
+// pass through a ring of D register buffers: D - 1 chunks are in flight while
+// one is multiplied, and the ring is unrolled so every buffer index is a
+// compile-time constant and the wait before each chunk counts exactly the
+// loads issued after it. The token rows (tiny) are re-read by every wave from
+// L2; the weights stream from HBM once per expert block.
+// Weights in the MFMA16 order (each 16-row x 32-column block stored as the
+// 1 KB operand of one MFMA step, lane by lane) are read 1 KB per instruction
+// from one contiguous run per 16-row tile: the same values in the same
+// registers as the row-major reads, so both orders give identical bits, and
+// HBM streams whole contiguous runs instead of 64 bytes from each of 16 rows
+// (about 6-7 TB/s against 5 TB/s on gfx950).
+// Each 64-row group of weight rows starts its K sweep at a different offset
+// (rotated in units of 256 K elements): waves that start together then read
+// different 512-byte phases of their rows instead of all hitting the same
+// phase of the same 4 KB-strided rows at once, which spreads the reads over
+// the HBM channels. The rotation depends only on the expert block and on the
+// output column, so GEMM1 with and without the SiLU epilogue add the K pieces
+// of every output in the same order and agree bit for bit.
 // GEMM1 with SiLU-and-mul in the epilogue: a wave owns the 16 gate rows and the
-// 16 matching up rows of 16 output columns (512-byte chunks), so a lane holds
-// gate and up of the same 4 outputs and writes z directly; h never reaches HBM.
+// 16 matching up rows of 16 output columns, so a lane holds gate and up of the
+// same 4 outputs and writes z directly; h never reaches HBM.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,9 +44,10 @@ namespace {
 constexpr int kWavesPerWG = 4;
 
 // TILES 16-row weight tiles per wave; per K chunk every row contributes S pieces of
-// 64 contiguous bytes (32 S bf16). ACT (GEMM1 with SiLU-and-mul, TILES = 2): tile 0
+// 64 contiguous bytes (32 S bf16), and D chunks share the register ring (the host
+// picks D dividing K / (32 S)). ACT (GEMM1 with SiLU-and-mul, TILES = 2): tile 0
 // holds the 16 gate rows and tile 1 the 16 up rows of the wave's 16 output columns.
-template <bool GATHER, bool ACT, int TILES, int S>
+template <bool GATHER, bool ACT, int TILES, int S, int D, bool PACKED>
 __global__ __launch_bounds__(kWavesPerWG * 64) void stream_gemm_bf16_kernel(GemmArgs p) {
     static_assert(!ACT || (GATHER && TILES == 2), "SiLU epilogue: GEMM1, one gate and one up tile");
     constexpr int kColsPerWave = ACT ? 16 : 16 * TILES;  // output columns
@@ -56,49 +73,75 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void stream_gemm_bf16_kernel(Gemm
     }
     const uint8_t* a_ptr = reinterpret_cast<const uint8_t*>(p.A) + src_row * p.lda_bytes + kq * 16;
     const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
+    // PS: bytes between consecutive 32-wide K pieces of one lane's weight row
+    constexpr int PS = PACKED ? 1024 : 64;
     const uint8_t* w_ptr[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-        // ACT: gate row n (t = 0) or up row N + n (t = 1) of output column n
-        const int n = ACT ? t * p.N + min(nw0 + row16, p.N - 1) : min(nw0 + 16 * t + row16, p.N - 1);
-        w_ptr[t] = w_base + static_cast<int64_t>(n) * p.ldw_bytes + kq * 16;
+        if constexpr (PACKED) {
+            // 16-row tiles (N is a multiple of 64 here): tile of gate row n0 or up row N + n0
+            const int tile = ACT ? t * (p.N / 16) + nw0 / 16 : min(nw0 / 16 + t, p.N / 16 - 1);
+            w_ptr[t] = w_base + static_cast<int64_t>(tile) * 16 * p.ldw_bytes + lane * 16;
+        } else {
+            // ACT: gate row n (t = 0) or up row N + n (t = 1) of output column n
+            const int n = ACT ? t * p.N + min(nw0 + row16, p.N - 1) : min(nw0 + 16 * t + row16, p.N - 1);
+            w_ptr[t] = w_base + static_cast<int64_t>(n) * p.ldw_bytes + kq * 16;
+        }
     }
 
     f32x4_t acc[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) acc[t] = f32x4_t{};
 
+    // K rotation: units of 8 pieces (256 K) where K allows, else 4 (S divides it).
+    // The 64-row group of the wave's rows: GEMM1 rows fold gate onto up (row mod N/2
+    // without the epilogue, the output column with it), so both forms rotate alike.
     const int KC = p.K / (32 * S);
-    u32x4_t a_cur[S], w_cur[TILES][S], a_nxt[S], w_nxt[TILES][S];
+    const int unit = (p.K / 32) % 8 == 0 ? 8 : 4;
+    const int n_units = p.K / (32 * unit);
+    const int grp = (ACT ? nw0 : nw0 % (p.N / 2)) >> 6;
+    const int shift = GATHER ? ((mb + grp) % n_units) * (unit / S) : 0;  // GEMM2: no gain measured
+
+    u32x4_t a_buf[D][S], w_buf[D][TILES][S];
     auto load = [&](int kc, u32x4_t (&a)[S], u32x4_t (&w)[TILES][S]) {
-        const int64_t off = static_cast<int64_t>(kc) * 64 * S;
+        int kr = kc + shift;
+        if (kr >= KC) kr -= KC;
+        const int64_t off = static_cast<int64_t>(kr) * 64 * S, woff = static_cast<int64_t>(kr) * PS * S;
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
 #pragma unroll
             for (int s = 0; s < S; ++s)
-                w[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(w_ptr[t] + off + 64 * s));
+                w[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(w_ptr[t] + woff + PS * s));
 #pragma unroll
         for (int s = 0; s < S; ++s) a[s] = *reinterpret_cast<const u32x4_t*>(a_ptr + off + 64 * s);
     };
-    load(0, a_cur, w_cur);
-    for (int kc = 0; kc < KC; ++kc) {
-        if (kc + 1 < KC) load(kc + 1, a_nxt, w_nxt);
+    auto multiply = [&](const u32x4_t (&a)[S], const u32x4_t (&w)[TILES][S]) {
 #pragma unroll
         for (int s = 0; s < S; ++s)
 #pragma unroll
             for (int t = 0; t < TILES; ++t)
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, w_cur[t][s]), __builtin_bit_cast(bf16x8_t, a_cur[s]),
-                    acc[t], 0, 0, 0);
-        if (kc + 1 < KC) {
+                    __builtin_bit_cast(bf16x8_t, w[t][s]), __builtin_bit_cast(bf16x8_t, a[s]), acc[t], 0, 0, 0);
+    };
+    // KC is a multiple of D (host): the last group of D chunks is peeled so that no
+    // load is conditional and the compiler's wait counts stay exact
 #pragma unroll
-            for (int s = 0; s < S; ++s) a_cur[s] = a_nxt[s];
+    for (int d = 0; d < D - 1; ++d) load(d, a_buf[d], w_buf[d]);
+    int kc0 = 0;
+    for (; kc0 < KC - D; kc0 += D) {
 #pragma unroll
-            for (int t = 0; t < TILES; ++t)
-#pragma unroll
-                for (int s = 0; s < S; ++s) w_cur[t][s] = w_nxt[t][s];
+        for (int d = 0; d < D; ++d) {
+            // program order kept: a chunk's loads all go out before the wait for
+            // the oldest chunk, never after it
+            load(kc0 + d + D - 1, a_buf[(d + D - 1) % D], w_buf[(d + D - 1) % D]);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(a_buf[d], w_buf[d]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    load(kc0 + D - 1, a_buf[D - 1], w_buf[D - 1]);
+#pragma unroll
+    for (int d = 0; d < D; ++d) multiply(a_buf[d], w_buf[d]);
 
     // 16x16 accumulator: lane holds token row (lane & 15) and 4 consecutive
     // weight rows 4*(lane >> 4) + 0..3 of each column tile
@@ -132,24 +175,41 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void stream_gemm_bf16_kernel(Gemm
     }
 }
 
-template <bool GATHER, bool ACT, int TILES, int S>
+template <bool GATHER, bool ACT, int TILES, int S, int D, bool PACKED>
 hipError_t launch_stream_as(const GemmArgs& a, hipStream_t stream) {
     constexpr int kColsPerWG = kWavesPerWG * (ACT ? 16 : 16 * TILES);
     const int n_wg = (a.N + kColsPerWG - 1) / kColsPerWG;
     const dim3 grid(static_cast<unsigned>(a.m_blocks * n_wg));
-    hipLaunchKernelGGL((stream_gemm_bf16_kernel<GATHER, ACT, TILES, S>), grid, dim3(kWavesPerWG * 64), 0, stream, a);
+    hipLaunchKernelGGL((stream_gemm_bf16_kernel<GATHER, ACT, TILES, S, D, PACKED>), grid,
+                       dim3(kWavesPerWG * 64), 0, stream, a);
     return hipGetLastError();
+}
+
+// ring depth: 4 chunks for the SiLU form, 2 for the 64-row form (deeper rings
+// measured no faster there), or the largest smaller depth dividing the chunks
+template <bool GATHER, bool ACT, int TILES, int S, bool PACKED>
+hipError_t launch_stream_ring(const GemmArgs& a, hipStream_t stream) {
+    const int kc = a.K / (32 * S);
+    if (ACT && kc % 4 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 4, PACKED>(a, stream);
+    if (kc % 2 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 2, PACKED>(a, stream);
+    return launch_stream_as<GATHER, ACT, TILES, S, 1, PACKED>(a, stream);
+}
+
+template <bool PACKED>
+hipError_t launch_stream_layout(const GemmArgs& a, hipStream_t stream) {
+    if (a.act) {
+        if (!a.sorted) return hipErrorInvalidValue;
+        return launch_stream_ring<true, true, 2, 4, PACKED>(a, stream);
+    }
+    return a.sorted ? launch_stream_ring<true, false, 4, 4, PACKED>(a, stream)
+                    : launch_stream_ring<false, false, 4, 4, PACKED>(a, stream);
 }
 
 }  // namespace
 
-// K is a multiple of 128 (checked on the host): 4 pieces of 64 bytes per row always
-// divide it; the SiLU variant takes 512-byte chunks where K allows
+// K is a multiple of 128 and N of 64 (checked on the host). Chunks of S = 4 pieces
+// of 32 K per row: two 16-row tiles in a ring of up to 4 chunks (SiLU form) or four
+// tiles in a ring of 2, so that two waves fit on a SIMD.
 hipError_t launch_stream_gemm(const GemmArgs& a, hipStream_t stream) {
-    if (a.act) {
-        if (!a.sorted) return hipErrorInvalidValue;
-        return (a.K / 32) % 8 == 0 ? launch_stream_as<true, true, 2, 8>(a, stream)
-                                   : launch_stream_as<true, true, 2, 4>(a, stream);
-    }
-    return a.sorted ? launch_stream_as<true, false, 4, 4>(a, stream) : launch_stream_as<false, false, 4, 4>(a, stream);
+    return a.w_packed ? launch_stream_layout<true>(a, stream) : launch_stream_layout<false>(a, stream);
 }

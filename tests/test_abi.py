@@ -49,6 +49,10 @@ def P(**kw):
     (dict(block_m=48), moe.MOE_E_UNSUPPORTED),
     (dict(wdtype=7), moe.MOE_E_UNSUPPORTED),
     (dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=16), moe.MOE_E_UNSUPPORTED),
+    (dict(weight_layout=2), moe.MOE_E_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_MFMA16, block_m=128), moe.MOE_E_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_MFMA16, block_m=64, wdtype=moe.MOE_W_FP8_E4M3_BLOCK128),
+     moe.MOE_E_UNSUPPORTED),
 ])
 def test_fused_experts_validation(kw, status):
     p = P(**kw)
@@ -104,3 +108,32 @@ def test_router_align_quant_validation():
     assert L.moe_quant_fp8_groups(None, 0, 128, None, None, None) == moe.MOE_OK
     for s in range(5):
         assert moe.status_string(s)
+
+
+def test_pack_weights_validation():
+    L = moe.lib()
+    p = P(weight_layout=moe.MOE_LAYOUT_MFMA16)
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 40)
+    assert L.moe_pack_weights(ctypes.byref(p), 3, a, b, None) == moe.MOE_E_INVALID
+    assert L.moe_pack_weights(ctypes.byref(p), 1, None, b, None) == moe.MOE_E_INVALID
+    assert L.moe_pack_weights(ctypes.byref(p), 2, a, None, None) == moe.MOE_E_INVALID
+    # w13 of this problem is 8 * 1024 * 256 * 2 bytes: a destination inside it overlaps
+    inside = ctypes.c_void_p((1 << 20) + 4096)
+    assert L.moe_pack_weights(ctypes.byref(p), 1, a, inside, None) == moe.MOE_E_INVALID
+    assert L.moe_pack_weights(ctypes.byref(p), 1, a, ctypes.c_void_p((1 << 40) + 8), None) \
+        == moe.MOE_E_INVALID  # 16-byte alignment
+    pf = P(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=128)
+    assert L.moe_pack_weights(ctypes.byref(pf), 1, a, b, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_pack_weights(ctypes.byref(P(H=200)), 1, a, b, None) == moe.MOE_E_UNSUPPORTED
+
+
+def test_problem_struct_matches_header():
+    # the ctypes mirror of moe_problem_t has the header's fields in the header's order
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    body = re.search(r"typedef struct \{(.*?)\} moe_problem_t;", src, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(int64_t|int32_t)\s+([^;]+);", body)
+    names = [n.strip() for _, decl in fields for n in decl.split(",")]
+    assert names == [f[0] for f in moe.MoeProblem._fields_]
+    kinds = [k for k, decl in fields for _ in decl.split(",")]
+    assert [ctypes.sizeof(f[1]) for f in moe.MoeProblem._fields_] == [8 if k == "int64_t" else 4 for k in kinds]
