@@ -72,9 +72,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill_m4096", choices=list(synth.WORKLOADS))
     ap.add_argument("--block-m", type=int, default=None, help="override the workload's block_m")
-    ap.add_argument("--weight-layout", default="auto", choices=("auto", "rows", "mfma16"),
-                    help="element order of w13/w2: auto = the MFMA16 order where the library "
-                         "supports it (bf16, block_m 16), else row-major")
+    ap.add_argument("--weight-layout", default="auto", choices=("auto", "rows", "tiled"),
+                    help="element order of w13/w2: auto = the tiled order where the library "
+                         "supports it (bf16 with block_m 16, 128 or 256), else row-major")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -95,11 +95,11 @@ class Step:
         M, H, I, E, k, B = p.M, p.H, p.I, p.E, p.topk, p.block_m
         wdt = moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16
         rows = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input)
-        packable = not self.fp8 and B == 16
-        if layout == "mfma16" and not packable:
-            raise SystemExit("--weight-layout mfma16 needs bf16 weights and block_m 16")
-        self.layout = "mfma16" if packable and layout in ("auto", "mfma16") else "rows"
-        self.wl = moe.MOE_LAYOUT_MFMA16 if self.layout == "mfma16" else moe.MOE_LAYOUT_ROWS
+        packable = not self.fp8 and B in (16, 128, 256)
+        if layout == "tiled" and not packable:
+            raise SystemExit("--weight-layout tiled needs bf16 weights and block_m 16, 128 or 256")
+        self.layout = "tiled" if packable and layout in ("auto", "tiled") else "rows"
+        self.wl = moe.MOE_LAYOUT_TILED if self.layout == "tiled" else moe.MOE_LAYOUT_ROWS
         self.prob = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input, self.wl)
         self.ids = torch.empty((M, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((M, k), dtype=torch.float32, device=dev)
@@ -126,7 +126,7 @@ class Step:
         self.gws = moe.gemm_workspace_for(self.prob, dev)  # split-K tail of the second GEMM
         self.w13 = d.w13q if self.fp8 else d.w13
         self.w2 = d.w2q if self.fp8 else d.w2
-        if self.layout == "mfma16":  # weight preparation, once, outside every timed region
+        if self.layout == "tiled":  # weight preparation, once, outside every timed region
             self.w13 = moe.moe_pack_weights(rows, 1, d.w13)
             self.w2 = moe.moe_pack_weights(rows, 2, d.w2)
 

@@ -35,8 +35,9 @@ typedef enum {
     MOE_E_INVALID = 1,     /* null pointer, negative size, topk outside [1, min(E, 32)] */
     MOE_E_UNSUPPORTED = 2, /* E > 256, H or I not a multiple of 128, unknown block_m,
                               dtype or weight layout, fp8 with block_m 16 or 256, the
-                              MFMA16 layout other than bf16 with block_m 16, more than
-                              2^31 routed rows, one expert's w13 of 2 GiB or more */
+                              tiled layout other than bf16 with block_m 16, 128 or 256,
+                              more than 2^31 routed rows, one expert's w13 of 2 GiB
+                              or more */
     MOE_E_WORKSPACE = 3,   /* workspace_bytes < moe_workspace_bytes(p) */
     MOE_E_HIP = 4          /* a kernel launch failed (hipGetLastError) */
 } moe_status_t;
@@ -53,19 +54,20 @@ typedef enum {
  * Blackwell", 2.8 (c): expert weights and scales are post-processed into the
  * kernel's packed layout; "vLLM modular_kernel.py notes", 10.1: expert
  * weights may arrive in a 6-D packed layout).
- *   MOE_LAYOUT_ROWS:   w [E, N, K] row-major (K contiguous).
- *   MOE_LAYOUT_MFMA16: the same E*N*K values, each 16-row x 32-column block
- *     stored as the 1 KB operand of one 16x16x32 bf16 matrix-core step:
- *       packed[e][n/16][k/32][(k%32)/8][n%16][k%8] = w[e][n][k],
- *     i.e. w.view(E, N/16, 16, K/32, 4, 8).permute(0, 1, 3, 4, 2, 5).
- *     A 16-row tile is then one contiguous run along K, and every 1 KB piece
- *     is read by one load instruction. bf16 weights with block_m 16 only
- *     (the decode path, which is bound by streaming the weights from HBM).
- *     Written by moe_pack_weights.
+ *   MOE_LAYOUT_ROWS:  w [E, N, K] row-major (K contiguous).
+ *   MOE_LAYOUT_TILED: the same E*N*K values in 16-row x 32-column tiles of
+ *     1 KB, row-major inside a tile, tiles ordered by row block then column
+ *     block:  tiled[e][n/16][k/32][n%16][k%32] = w[e][n][k],
+ *     i.e. w.view(E, N/16, 16, K/32, 32).permute(0, 1, 3, 2, 4).
+ *     Every 1 KB tile is what one load instruction of the kernels reads (16
+ *     rows x 32 columns), and a 16-row block is one contiguous run along K,
+ *     where row-major weights give 64 bytes from each of 16 rows 2*K bytes
+ *     apart. bf16 weights with block_m 16, 128 or 256. Written by
+ *     moe_pack_weights; results are bit-identical to MOE_LAYOUT_ROWS.
  */
 typedef enum {
     MOE_LAYOUT_ROWS = 0,
-    MOE_LAYOUT_MFMA16 = 1
+    MOE_LAYOUT_TILED = 1
 } moe_wlayout_t;
 
 /* Sizes and options of one fused_experts call. */
@@ -273,12 +275,12 @@ moe_status_t moe_unpermute_reduce(const moe_problem_t *p, const void *o, const i
 
 /*
  * Weight preparation: rewrite one weight tensor from MOE_LAYOUT_ROWS into
- * MOE_LAYOUT_MFMA16 (a permutation: the bits of every element are kept).
+ * MOE_LAYOUT_TILED (a permutation: the bits of every element are kept).
  *   which = 1: w = w13 [E, 2I, H];  which = 2: w = w2 [E, H, I]   (bf16)
  *   w_packed: the same number of bytes, out; must not overlap w.
  * p->wdtype must be MOE_W_BF16; p->M, block_m and weight_layout are not used
  * (beyond the problem's validity). Run once, before fused_experts is called
- * with weight_layout = MOE_LAYOUT_MFMA16.
+ * with weight_layout = MOE_LAYOUT_TILED.
  */
 moe_status_t moe_pack_weights(const moe_problem_t *p, int32_t which, const void *w,
                               void *w_packed, void *stream);

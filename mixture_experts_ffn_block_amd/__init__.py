@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
-MOE_LAYOUT_ROWS, MOE_LAYOUT_MFMA16 = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 
 EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_quant_fp8_groups",
            "moe_workspace_bytes", "fused_experts", "moe_expert_gemm_workspace_bytes",
@@ -193,7 +193,7 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
                   stream=None, weight_layout=MOE_LAYOUT_ROWS) -> torch.Tensor:
     """y = fused MoE expert forward (bf16 [M, H]). `out` may be `x` (in place).
 
-    weight_layout MOE_LAYOUT_MFMA16: w13 and w2 come from moe_pack_weights (same shapes)."""
+    weight_layout MOE_LAYOUT_TILED: w13 and w2 come from moe_pack_weights (same shapes)."""
     _need(x, torch.bfloat16, "x")
     fp8 = w13.dtype == torch.float8_e4m3fn
     wdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
@@ -343,7 +343,7 @@ def moe_unpermute_reduce(p: MoeProblem, o: torch.Tensor, inv_perm: torch.Tensor,
 def moe_pack_weights(p: MoeProblem, which: int, w: torch.Tensor, out: torch.Tensor | None = None,
                      stream=None) -> torch.Tensor:
     """Rewrite bf16 w13 (which = 1, [E, 2I, H]) or w2 (which = 2, [E, H, I]) into the
-    MOE_LAYOUT_MFMA16 element order; the result has the same shape and bytes."""
+    MOE_LAYOUT_TILED element order (16 x 32 tiles); the result has the same shape and bytes."""
     N, K = (2 * p.I, p.H) if which == 1 else (p.H, p.I)
     _need_size(w, _BF, p.E * N * K, "w")
     if out is None:

@@ -69,9 +69,10 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->wdtype != MOE_W_BF16 && p->wdtype != MOE_W_FP8_E4M3_BLOCK128) return MOE_E_UNSUPPORTED;
     if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && (p->block_m == 16 || p->block_m == 256))
         return MOE_E_UNSUPPORTED;
-    if (p->weight_layout != MOE_LAYOUT_ROWS && p->weight_layout != MOE_LAYOUT_MFMA16)
+    if (p->weight_layout != MOE_LAYOUT_ROWS && p->weight_layout != MOE_LAYOUT_TILED)
         return MOE_E_UNSUPPORTED;
-    if (p->weight_layout == MOE_LAYOUT_MFMA16 && (p->wdtype != MOE_W_BF16 || p->block_m != 16))
+    if (p->weight_layout == MOE_LAYOUT_TILED &&
+        (p->wdtype != MOE_W_BF16 || (p->block_m != 16 && p->block_m != 128 && p->block_m != 256)))
         return MOE_E_UNSUPPORTED;
     // one expert's weight matrix is addressed with 32-bit byte offsets
     const int64_t esz = p->wdtype == MOE_W_FP8_E4M3_BLOCK128 ? 1 : 2;
@@ -115,7 +116,7 @@ hipError_t gemm_stage(const moe_problem_t& p, int which, const void* a, const fl
     g.K = K;
     g.m_blocks = static_cast<int>(cap / p.block_m);
     g.group_m = kGroupM;
-    g.w_packed = p.weight_layout == MOE_LAYOUT_MFMA16 ? 1 : 0;
+    g.w_packed = p.weight_layout == MOE_LAYOUT_TILED ? 1 : 0;
     if (fp8) {
         g.a_scale = a_scale;
         g.a_scale_ld = cap;
@@ -164,7 +165,7 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const void* a, const float* a_
     g.K = p.H;
     g.m_blocks = static_cast<int>(cap / p.block_m);
     g.group_m = kGroupM;
-    g.w_packed = p.weight_layout == MOE_LAYOUT_MFMA16 ? 1 : 0;
+    g.w_packed = p.weight_layout == MOE_LAYOUT_TILED ? 1 : 0;
     g.act = 1;
     g.act_weights = weights;
     g.act_on_input = p.apply_router_weight_on_input ? 1 : 0;
@@ -412,7 +413,7 @@ moe_status_t moe_pack_weights(const moe_problem_t* p, int32_t which, const void*
     const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_packed);
     if (a < b + bytes && b < a + bytes) return MOE_E_INVALID;  // overlapping buffers
     if (a % 16 || b % 16) return MOE_E_INVALID;
-    return hip_status(launch_pack_mfma16(static_cast<const bf16_t*>(w), static_cast<bf16_t*>(w_packed),
+    return hip_status(launch_pack_tiled(static_cast<const bf16_t*>(w), static_cast<bf16_t*>(w_packed),
                                          p->E, N, K, static_cast<hipStream_t>(stream)));
 }
 

@@ -163,30 +163,30 @@ __global__ __launch_bounds__(256) void reduce_kernel(const bf16_t* __restrict__ 
 }
 
 // ------------------------------------------------------------- weight pack --
-// One thread per 16-byte piece of the packed tensor (coalesced writes): piece
-// (e, tile, kf, lane) holds row 16 tile + (lane & 15), columns 32 kf + 8 (lane >> 4)
-// .. + 7 of expert e.
-__global__ __launch_bounds__(256) void pack_mfma16_kernel(const uint4* __restrict__ w,
+// One thread per 16-byte piece of the tiled tensor (coalesced writes): piece q of
+// tile (e, tile, kf) holds row 16 tile + q / 4, columns 32 kf + 8 (q % 4) .. + 7 of
+// expert e.
+__global__ __launch_bounds__(256) void pack_tiled_kernel(const uint4* __restrict__ w,
                                                           uint4* __restrict__ wp, int64_t pieces,
                                                           int N, int K) {
     const int64_t kfs = K / 32, tiles = N / 16;
     for (int64_t d = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; d < pieces;
          d += static_cast<int64_t>(gridDim.x) * 256) {
-        const int lane = static_cast<int>(d & 63);
+        const int q = static_cast<int>(d & 63);
         const int64_t f = d >> 6;
         const int64_t kf = f % kfs, tile = (f / kfs) % tiles, e = f / (kfs * tiles);
-        const int64_t n = tile * 16 + (lane & 15), k = kf * 32 + 8 * (lane >> 4);
+        const int64_t n = tile * 16 + (q >> 2), k = kf * 32 + 8 * (q & 3);
         wp[d] = w[((e * N + n) * K + k) / 8];
     }
 }
 
 }  // namespace
 
-hipError_t launch_pack_mfma16(const bf16_t* w, bf16_t* wp, int64_t E, int N, int K, hipStream_t stream) {
+hipError_t launch_pack_tiled(const bf16_t* w, bf16_t* wp, int64_t E, int N, int K, hipStream_t stream) {
     const int64_t pieces = E * N * K / 8;
     const int64_t blocks = ceil_div(pieces, 256);
     const dim3 grid(static_cast<unsigned>(blocks < 65536 ? blocks : 65536));
-    hipLaunchKernelGGL(pack_mfma16_kernel, grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL(pack_tiled_kernel, grid, dim3(256), 0, stream,
                        reinterpret_cast<const uint4*>(w), reinterpret_cast<uint4*>(wp), pieces, N, K);
     return hipGetLastError();
 }

@@ -33,10 +33,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef DMA128_WIDE
-#define DMA128_WIDE 0
-#endif
-
 namespace {
 
 constexpr int kRowBytes = 128;  // one tile row = 128 bytes of K
@@ -538,6 +534,10 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
         a_src[i] = reinterpret_cast<const uint8_t*>(p.A) + src * p.lda_bytes + chunk * 16;
     }
     const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
+    // Tiled weights (16-row x 32-column tiles, row-major inside, ordered by row block
+    // then column block): a copy's 16 rows x 64 bytes of one stage are one contiguous
+    // 1 KB tile (64-byte rows only), and the next stage's tile follows it directly.
+    const int w_stage_bytes = p.w_packed ? 1024 : C::ROWB;
     int32_t b_off[B_INSTR];
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
@@ -547,7 +547,15 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
         // n0 + 32 * (r / 64) + r % 32; gate rows are w13 rows [0, N), up rows [N, 2N)
         const int wrow = ACT ? ((row >> 5) & 1) * p.N + min(n0 + (row >> 6) * 32 + (row & 31), p.N - 1)
                              : min(n0 + row, p.N - 1);
-        b_off[i] = wrow * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
+        if (p.w_packed) {
+            // the copy's 16 rows are 16 consecutive weight rows from a multiple of 16 (N is
+            // a multiple of 128); past the last row a whole tile is clamped
+            const int wrow0 = ACT ? ((row >> 5) & 1) * p.N + min(n0 + (row >> 6) * 32 + (row & 16), p.N - 16)
+                                  : min(n0 + (row & ~15), p.N - 16);
+            b_off[i] = (wrow0 / 16) * (p.K / 32) * 1024 + (row & 15) * 64 + chunk * 16;
+        } else {
+            b_off[i] = wrow * static_cast<int32_t>(p.ldw_bytes) + chunk * 16;
+        }
     }
     // LDS destinations are wave-uniform: keep them in scalar registers
     const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds_base + wave * A_INSTR * 1024);
@@ -559,7 +567,7 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
         const int64_t k_off = static_cast<int64_t>(sp.chunk) * KT * C::ROWB;
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i) a_src[i] += k_off;
-        w_base += k_off;
+        w_base += static_cast<int64_t>(sp.chunk) * KT * w_stage_bytes;
     }
     // copy group j of K tile kt: groups of 4 (or 2) consecutive 1 KB copies
     constexpr int AG = A_INSTR >= 4 ? 4 : A_INSTR, BG = B_INSTR >= 4 ? 4 : B_INSTR;
@@ -575,9 +583,10 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
             copy_group<AG>(g, a_dst + st + j * AG * 1024);
         } else {
             const int jb = j - A_INSTR / AG;
+            const int64_t woff = static_cast<int64_t>(kt) * w_stage_bytes;
             const uint8_t* g[BG];
 #pragma unroll
-            for (int i = 0; i < BG; ++i) g[i] = w_base + b_off[jb * BG + i] + off;
+            for (int i = 0; i < BG; ++i) g[i] = w_base + b_off[jb * BG + i] + woff;
             copy_group<BG>(g, b_dst + st + jb * BG * 1024);
         }
     };
@@ -1201,14 +1210,13 @@ hipError_t launch_dma_as(const GemmArgs& a, hipStream_t stream) {
 
 template <class C>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
+    if (a.w_packed && C::ROWB != 64) return hipErrorInvalidValue;  // one 16 x 32 tile per copy
     if (a.act) return a.sorted ? launch_dma_as<C, true, true>(a, stream) : hipErrorInvalidValue;
     return a.sorted ? launch_dma_as<C, true, false>(a, stream) : launch_dma_as<C, false, false>(a, stream);
 }
 
 // 128 tokens x 512 weight rows, 64-byte rows, 1 x 8 waves of 128 x 64 (two per SIMD)
 using Dma128 = dma::Cfg<128, 512, 1, 4, 64, 8>;
-// 128 tokens x 256 weight rows, 128-byte rows, 1 x 4 waves of 128 x 64
-using Dma128w = dma::Cfg<128, 256, 1, 3, 128>;
 // 256 tokens x 256 weight rows, 64-byte rows, 2 x 4 waves of 128 x 64 (two per SIMD:
 // one wave's MFMAs cover the other's waits)
 using Dma256 = dma::Cfg<256, 256, 2, 5, 64, 8>;
@@ -1249,7 +1257,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStre
         switch (block_m) {
             case 32: return launch_tile<32, 256, false>(a, stream);
             case 64: return launch_tile<64, 512, false>(a, stream);
-            case 128: return DMA128_WIDE ? launch_dma<Dma128w>(a, stream) : launch_dma<Dma128>(a, stream);
+            case 128: return launch_dma<Dma128>(a, stream);
             case 256: return launch_dma<Dma256>(a, stream);
         }
     } else {

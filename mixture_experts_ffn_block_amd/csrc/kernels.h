@@ -45,8 +45,8 @@ struct GemmArgs {
     int* part_cnt;
     int part_slots;
     int n_cu;                  // workgroups of this kernel that run at once (one per CU)
-    // W in the MFMA16 order (block_m 16 only): each 16-row x 32-column block is the
-    // 1 KB operand of one 16x16x32 step, lane 16q + r holding row r, columns 8q..8q+7
+    // W tiled: 16-row x 32-column tiles of 1 KB, row-major inside, ordered by row
+    // block then column block (bf16; block_m 16, 128 and 256)
     int w_packed;
 };
 
@@ -73,6 +73,6 @@ hipError_t launch_permute_scales(const float* scale, int groups, int topk, int R
                                  float* out, hipStream_t stream);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream);
 int concurrent_tiles();  // workgroups of the LDS-tiled GEMMs that run at once
-hipError_t launch_pack_mfma16(const bf16_t* w, bf16_t* wp, int64_t E, int N, int K, hipStream_t stream);
+hipError_t launch_pack_tiled(const bf16_t* w, bf16_t* wp, int64_t E, int N, int K, hipStream_t stream);
 hipError_t launch_reduce(const bf16_t* o, const int32_t* inv_perm, const float* weights, int64_t M,
                          int k, int H, int use_weights, bf16_t* y, hipStream_t stream);

@@ -50,8 +50,9 @@ def P(**kw):
     (dict(wdtype=7), moe.MOE_E_UNSUPPORTED),
     (dict(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=16), moe.MOE_E_UNSUPPORTED),
     (dict(weight_layout=2), moe.MOE_E_UNSUPPORTED),
-    (dict(weight_layout=moe.MOE_LAYOUT_MFMA16, block_m=128), moe.MOE_E_UNSUPPORTED),
-    (dict(weight_layout=moe.MOE_LAYOUT_MFMA16, block_m=64, wdtype=moe.MOE_W_FP8_E4M3_BLOCK128),
+    (dict(weight_layout=moe.MOE_LAYOUT_TILED, block_m=64), moe.MOE_E_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_TILED, block_m=32), moe.MOE_E_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_TILED, block_m=128, wdtype=moe.MOE_W_FP8_E4M3_BLOCK128),
      moe.MOE_E_UNSUPPORTED),
 ])
 def test_fused_experts_validation(kw, status):
@@ -112,7 +113,7 @@ def test_router_align_quant_validation():
 
 def test_pack_weights_validation():
     L = moe.lib()
-    p = P(weight_layout=moe.MOE_LAYOUT_MFMA16)
+    p = P(weight_layout=moe.MOE_LAYOUT_TILED)
     a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 40)
     assert L.moe_pack_weights(ctypes.byref(p), 3, a, b, None) == moe.MOE_E_INVALID
     assert L.moe_pack_weights(ctypes.byref(p), 1, None, b, None) == moe.MOE_E_INVALID
