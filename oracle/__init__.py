@@ -51,16 +51,16 @@ def lib():
             "oracle_quant_groups_fp8": [_P, _I64, _P, _P],
             "oracle_topk": [_P, _I64, _I32, _I32, _I32, _P, _P],
             "oracle_align_capacity": [_I64, _I32, _I32, _I32],
-            "oracle_align": [_P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P],
+            "oracle_align": [_P, _I64, _I32, _I32, _I32, _I64, _P, _I32, _P, _P, _P, _P],
             "oracle_gemm1_bf16": [_P, _P, _I32, _I32, _P],
             "oracle_act_bf16": [_P, _I32, ctypes.c_double, _P],
             "oracle_gemm2_bf16": [_P, _P, _I32, _I32, _P],
             "oracle_gemm_fp8": [_P, _P, _P, _P, _I32, _I32, _P],
             "oracle_act_fp8": [_P, _I32, ctypes.c_double, _P, _P],
             "oracle_fused_experts_bf16": [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
-                                          _I32, _I64, _I64, _P, _P],
+                                          _I32, _P, _I32, _I64, _I64, _P, _P],
             "oracle_fused_experts_fp8": [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
-                                         _P, _P, _I32, _I64, _I64, _P, _P],
+                                         _P, _P, _I32, _P, _I32, _I64, _I64, _P, _P],
             "oracle_dense_experts_bf16": [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                           _P, _P],
         }
@@ -150,17 +150,28 @@ def align_capacity(M: int, k: int, E: int, B: int) -> int:
     return int(lib().oracle_align_capacity(M, k, E, B))
 
 
-def align(ids: np.ndarray, E: int, B: int, cap: int | None = None):
+def _emap(expert_map):
+    """(pointer-ready map, its length) or (None, 0): ids are local without a map."""
+    if expert_map is None:
+        return None, 0
+    m = _c(expert_map, np.int32)
+    return m, int(m.size)
+
+
+def align(ids: np.ndarray, E: int, B: int, cap: int | None = None, expert_map=None):
+    """With expert_map (global id -> local expert or -1), E is the local expert
+    count and items of remote experts get no row (inv_perm -1)."""
     ids = _c(ids, np.int32)
     M, k = ids.shape
     if cap is None:
         cap = align_capacity(M, k, E, B)
+    emap, eg = _emap(expert_map)
     sorted_ids = np.empty(cap, np.int32)
     expert_ids = np.empty(cap // B, np.int32)
     npp = np.zeros(1, np.int32)
     inv = np.empty((M, k), np.int32)
-    rc = lib().oracle_align(_p(ids), M, k, E, B, cap, _p(sorted_ids), _p(expert_ids), _p(npp),
-                            _p(inv))
+    rc = lib().oracle_align(_p(ids), M, k, E, B, cap, _p(emap) if emap is not None else None, eg,
+                            _p(sorted_ids), _p(expert_ids), _p(npp), _p(inv))
     if rc:
         raise ValueError(f"oracle_align failed ({rc})")
     return sorted_ids, expert_ids, int(npp[0]), inv
@@ -215,8 +226,9 @@ def act_fp8(h: np.ndarray, alpha: float = 1.0):
 # ----------------------------------------------------------------- layer ---
 
 def fused_experts_bf16(x, w13, w2, ids, weights, on_input=False, t0=0, t1=None,
-                       return_acc=False):
-    """y rows [t0, t1) of the layer with bf16 weights (uint16 bit patterns)."""
+                       return_acc=False, expert_map=None):
+    """y rows [t0, t1) of the layer with bf16 weights (uint16 bit patterns).
+    With expert_map, w13/w2 hold the local experts and ids are global."""
     x, w13, w2 = _c(x, np.uint16), _c(w13, np.uint16), _c(w2, np.uint16)
     ids, weights = _c(ids, np.int32), _c(weights, np.float32)
     M, H = x.shape
@@ -225,16 +237,18 @@ def fused_experts_bf16(x, w13, w2, ids, weights, on_input=False, t0=0, t1=None,
     t1 = M if t1 is None else t1
     y = np.zeros((M, H), np.uint16)
     acc = np.zeros((M, H), np.float64) if return_acc else None
+    emap, eg = _emap(expert_map)
     rc = lib().oracle_fused_experts_bf16(M, H, N2 // 2, E, k, _p(x), _p(w13), _p(w2), _p(ids),
-                                         _p(weights), int(on_input), t0, t1, _p(y),
-                                         _p(acc) if acc is not None else None)
+                                         _p(weights), int(on_input),
+                                         _p(emap) if emap is not None else None, eg, t0, t1,
+                                         _p(y), _p(acc) if acc is not None else None)
     if rc:
         raise ValueError("oracle_fused_experts_bf16: expert id out of range")
     return (y[t0:t1], acc[t0:t1]) if return_acc else y[t0:t1]
 
 
 def fused_experts_fp8(x, w13q, w13s, w2q, w2s, ids, weights, on_input=False, t0=0, t1=None,
-                      return_acc=False):
+                      return_acc=False, expert_map=None):
     """y rows [t0, t1) of the layer with e4m3 weights and 128x128 block scales."""
     x = _c(x, np.uint16)
     w13q, w2q = _c(w13q, np.uint8), _c(w2q, np.uint8)
@@ -246,8 +260,10 @@ def fused_experts_fp8(x, w13q, w13s, w2q, w2s, ids, weights, on_input=False, t0=
     t1 = M if t1 is None else t1
     y = np.zeros((M, H), np.uint16)
     acc = np.zeros((M, H), np.float64) if return_acc else None
+    emap, eg = _emap(expert_map)
     rc = lib().oracle_fused_experts_fp8(M, H, N2 // 2, E, k, _p(x), _p(w13q), _p(w13s),
                                         _p(w2q), _p(w2s), _p(ids), _p(weights), int(on_input),
+                                        _p(emap) if emap is not None else None, eg,
                                         t0, t1, _p(y), _p(acc) if acc is not None else None)
     if rc:
         raise ValueError("oracle_fused_experts_fp8: expert id out of range")

@@ -214,11 +214,26 @@ int64_t oracle_align_capacity(int64_t M, int k, int E, int B)
     return (bound + B - 1) / B * B;
 }
 
+/* The expert an item is computed with on this shard ([MK] "expert_map": a
+ * global-to-local table with -1 for experts held by another rank; [DG] 2.6.2
+ * ep_scatter skips items whose expert is not local). Without a map the ids
+ * are local already. Returns -2 for an id outside the routing range. */
+static int local_expert(int id, const int32_t *emap, int E_global, int E)
+{
+    if (!emap) return (id < 0 || id >= E) ? -2 : id;
+    if (id < 0 || id >= E_global) return -2;
+    return emap[id] >= 0 && emap[id] < E ? emap[id] : -1;
+}
+
 /* Routed item r = t*k + j. Items are grouped by expert in ascending expert
  * order; each expert's segment holds its items in ascending r, padded with the
  * sentinel R up to a multiple of B. expert_ids[b] is the expert of block b
- * (-1 past the used blocks); inv_perm[r] is the row that item r landed in. */
+ * (-1 past the used blocks); inv_perm[r] is the row that item r landed in.
+ * With an expert map (emap, E_global entries), ids are global, segments are
+ * those of the local experts, and items of remote experts get no row
+ * (inv_perm = -1). */
 int oracle_align(const int32_t *ids, int64_t M, int k, int E, int B, int64_t cap,
+                 const int32_t *emap, int E_global,
                  int32_t *sorted, int32_t *expert_ids, int32_t *npp, int32_t *inv_perm)
 {
     int64_t R = M * k;
@@ -226,8 +241,9 @@ int oracle_align(const int32_t *ids, int64_t M, int k, int E, int B, int64_t cap
     int64_t *start = calloc((size_t)E + 1, sizeof(int64_t));
     int64_t *fill = calloc((size_t)E, sizeof(int64_t));
     for (int64_t r = 0; r < R; ++r) {
-        if (ids[r] < 0 || ids[r] >= E) { free(count); free(start); free(fill); return 1; }
-        count[ids[r]]++;
+        int e = local_expert(ids[r], emap, E_global, E);
+        if (e == -2) { free(count); free(start); free(fill); return 1; }
+        if (e >= 0) count[e]++;
     }
     start[0] = 0;
     for (int e = 0; e < E; ++e) start[e + 1] = start[e] + (count[e] + B - 1) / B * B;
@@ -235,7 +251,8 @@ int oracle_align(const int32_t *ids, int64_t M, int k, int E, int B, int64_t cap
     for (int64_t pos = 0; pos < cap; ++pos) sorted[pos] = (int32_t)R;
     for (int64_t b = 0; b < cap / B; ++b) expert_ids[b] = -1;
     for (int64_t r = 0; r < R; ++r) {
-        int e = ids[r];
+        int e = local_expert(ids[r], emap, E_global, E);
+        if (e < 0) { inv_perm[r] = -1; continue; }
         int64_t pos = start[e] + fill[e]++;
         sorted[pos] = (int32_t)r;
         inv_perm[r] = (int32_t)pos;
@@ -327,10 +344,13 @@ void oracle_act_fp8(const uint16_t *h, int I, double alpha, uint8_t *zq, float *
 /* ------------------------------------------------------------------------ */
 
 /* bf16 weights. tokens [t0, t1) of y are written; acc (optional, [M, H]) gets
- * the unrounded weighted sums. */
+ * the unrounded weighted sums. With an expert map the weights are the E local
+ * experts' and only slots whose expert is local contribute ([DG] 2.6.5:
+ * ep_gather skips the slots of experts on other ranks). */
 int oracle_fused_experts_bf16(int64_t M, int H, int I, int E, int k,
                               const uint16_t *x, const uint16_t *w13, const uint16_t *w2,
                               const int32_t *ids, const float *weights, int on_input,
+                              const int32_t *emap, int E_global,
                               int64_t t0, int64_t t1, uint16_t *y, double *acc_out)
 {
     (void)M;
@@ -342,12 +362,13 @@ int oracle_fused_experts_bf16(int64_t M, int H, int I, int E, int k,
         uint16_t *o = malloc(sizeof(uint16_t) * (size_t)H);
         double *acc = calloc((size_t)H, sizeof(double));
         for (int j = 0; j < k; ++j) {
-            int e = ids[t * k + j];
-            if (e < 0 || e >= E) {
+            int e = local_expert(ids[t * k + j], emap, E_global, E);
+            if (e == -2) {
 #pragma omp atomic write
                 bad = 1;
                 continue;
             }
+            if (e < 0) continue;  /* computed on another rank */
             double alpha = weights[t * k + j];
             oracle_gemm1_bf16(x + t * H, w13 + (int64_t)e * 2 * I * H, H, I, h);
             oracle_act_bf16(h, I, on_input ? alpha : 1.0, z);
@@ -370,6 +391,7 @@ int oracle_fused_experts_fp8(int64_t M, int H, int I, int E, int k,
                              const uint16_t *x, const uint8_t *w13q, const float *w13s,
                              const uint8_t *w2q, const float *w2s,
                              const int32_t *ids, const float *weights, int on_input,
+                             const int32_t *emap, int E_global,
                              int64_t t0, int64_t t1, uint16_t *y, double *acc_out)
 {
     (void)M;
@@ -388,12 +410,13 @@ int oracle_fused_experts_fp8(int64_t M, int H, int I, int E, int k,
         for (int c = 0; c < H; ++c) xf[c] = (float)oracle_bf16_to_f64(x[t * H + c]);
         oracle_quant_groups_fp8(xf, H, xq, xs);
         for (int j = 0; j < k; ++j) {
-            int e = ids[t * k + j];
-            if (e < 0 || e >= E) {
+            int e = local_expert(ids[t * k + j], emap, E_global, E);
+            if (e == -2) {
 #pragma omp atomic write
                 bad = 1;
                 continue;
             }
+            if (e < 0) continue;  /* computed on another rank */
             double alpha = weights[t * k + j];
             oracle_gemm_fp8(xq, xs, w13q + (int64_t)e * 2 * I * H, w13s + e * s13, 2 * I, H, h);
             oracle_act_fp8(h, I, on_input ? alpha : 1.0, zq, zs);
