@@ -92,7 +92,10 @@ class Step:
         self.moe, self.p, self.d = moe, p, d
         self.fp8 = p.wdtype == "fp8"
         dev = d.x.device
-        M, H, I, E, k, B = p.M, p.H, p.I, p.E, p.topk, p.block_m
+        # an expert-parallel rank holds E / ep_size experts; ids stay global
+        self.emap = d.expert_map
+        G = p.E if self.emap is not None else 0
+        M, H, I, E, k, B = p.M, p.H, p.I, len(p.local_experts), p.topk, p.block_m
         wdt = moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16
         rows = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input)
         packable = not self.fp8 and B in (16, 128, 256)
@@ -100,7 +103,7 @@ class Step:
             raise SystemExit("--weight-layout tiled needs bf16 weights and block_m 16, 128 or 256")
         self.layout = "tiled" if packable and layout in ("auto", "tiled") else "rows"
         self.wl = moe.MOE_LAYOUT_TILED if self.layout == "tiled" else moe.MOE_LAYOUT_ROWS
-        self.prob = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input, self.wl)
+        self.prob = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input, self.wl, G)
         self.ids = torch.empty((M, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((M, k), dtype=torch.float32, device=dev)
         self.y = torch.empty_like(d.x)
@@ -135,7 +138,7 @@ class Step:
         m.moe_topk(d.logits, self.p.topk, out=(self.ids, self.w))
         m.fused_experts(d.x, self.w13, self.w2, self.ids, self.w, self.p.block_m,
                         d.w13s, d.w2s, self.p.apply_router_weight_on_input, out=self.y,
-                        workspace=self.ws, weight_layout=self.wl)
+                        workspace=self.ws, weight_layout=self.wl, expert_map=self.emap)
 
     STAGES = ("router", "quant", "align", "gemm1", "act", "gemm2", "reduce")
 
@@ -153,9 +156,14 @@ class Step:
                                      m._ptr(self.xs), s)
             a1, a1s = self.xq, self.xst
         ev[2].record()
-        lib.moe_align_block_size(m._ptr(self.ids), self.p.M, self.p.topk, self.p.E,
-                                 self.p.block_m, m._ptr(self.sorted), m._ptr(self.expert_ids),
-                                 m._ptr(self.npp), m._ptr(self.inv), s)
+        if self.emap is None:
+            lib.moe_align_block_size(m._ptr(self.ids), self.p.M, self.p.topk, self.p.E,
+                                     self.p.block_m, m._ptr(self.sorted), m._ptr(self.expert_ids),
+                                     m._ptr(self.npp), m._ptr(self.inv), s)
+        else:
+            lib.moe_align_block_size_ep(m._ptr(self.ids), self.p.M, self.p.topk, self.p.E,
+                                        m._ptr(self.emap), p.E, self.p.block_m, m._ptr(self.sorted),
+                                        m._ptr(self.expert_ids), m._ptr(self.npp), m._ptr(self.inv), s)
         if self.fp8:  # the activation scales follow the rows into the sorted order
             m.moe_permute_scales(p, self.xs, self.sorted, self.npp, self.xst)
         ev[3].record()
@@ -176,10 +184,11 @@ class Step:
         ev[7].record()
 
 
-def algorithmic(p: synth.Problem, touched: int, act_fused: bool = False):
+def algorithmic(p: synth.Problem, touched: int, act_fused: bool = False, R: int | None = None):
     """Algorithmic FLOP and HBM bytes of the step and of GEMM1 (padding excluded);
-    with the activation fused into GEMM1 that kernel writes z instead of h."""
-    R = p.M * p.topk
+    with the activation fused into GEMM1 that kernel writes z instead of h. R: the
+    routed items computed here (all M * topk, or an expert-parallel rank's share)."""
+    R = p.M * p.topk if R is None else R
     wb = 1 if p.wdtype == "fp8" else 2
     flops_g1 = 4.0 * R * p.H * p.I
     flops = 6.0 * R * p.H * p.I
@@ -213,14 +222,18 @@ def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.
         return t.cpu().contiguous().view(torch.uint8).numpy()
 
     ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    # experts held here: global id -> row of the weight tensors (an expert-parallel
+    # rank holds a slice; other slots are computed elsewhere and skipped)
+    held = np.full(p.E, -1, np.int64)
+    held[list(p.local_experts)] = np.arange(len(p.local_experts))
 
     def run(T):
         toks = np.arange(T)
-        experts = sorted(set(ids_np[toks].reshape(-1).tolist()))
+        experts = sorted(e for e in set(ids_np[toks].reshape(-1).tolist()) if held[e] >= 0)
         remap = np.full(p.E, -1, np.int32)
         remap[experts] = np.arange(len(experts), dtype=np.int32)
-        sub_ids = remap[ids_np[toks]]
-        sel = torch.tensor(experts, device=d.x.device)
+        sub_ids = ids_np[toks]
+        sel = torch.tensor(held[experts], device=d.x.device)
         x = bits16(d.x[:T])
         if p.wdtype == "fp8":
             args = (x, bits8(d.w13q[sel]), d.w13s[sel].cpu().numpy(), bits8(d.w2q[sel]),
@@ -230,19 +243,20 @@ def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.
             args = (x, bits16(d.w13[sel]), bits16(d.w2[sel]), sub_ids, w_np[toks])
             fn = oracle.fused_experts_bf16
         t0 = time.perf_counter()
-        fn(*args, on_input=p.apply_router_weight_on_input)
-        return time.perf_counter() - t0
+        fn(*args, on_input=p.apply_router_weight_on_input, expert_map=remap)
+        return time.perf_counter() - t0, int((held[ids_np[toks]] >= 0).sum())
 
     T = min(p.M, threads)
-    dt = run(T)
+    dt, items = run(T)
     if dt < target_s / 2 and T < p.M:
         T = int(min(p.M, max(T, round(T * target_s / dt / threads) * threads)))
-        dt = run(T)
-    flops = 6.0 * T * p.topk * p.H * p.I
+        dt, items = run(T)
+    flops = 6.0 * items * p.H * p.I
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "tokens_per_s": round(T / dt, 3), "seconds": round(dt, 3),
             "sample": f"first {T} of {p.M} tokens of the same workload (all their top-{p.topk} "
-                      f"experts), plain C oracle, fp64 accumulation, {threads} OpenMP threads"}
+                      f"experts held here, {items} routed items), plain C oracle, fp64 "
+                      f"accumulation, {threads} OpenMP threads"}
 
 
 def main():
@@ -275,7 +289,11 @@ def main():
         st.fused()
     torch.cuda.synchronize()
     ids_host = st.ids.cpu().numpy()
-    touched = int(np.unique(ids_host).size)
+    # experts touched and routed items computed here (an expert-parallel rank: its share)
+    held = np.zeros(p.E, bool)
+    held[list(p.local_experts)] = True
+    touched = int(np.unique(ids_host[held[ids_host]]).size)
+    items = int(held[ids_host].sum())
 
     # timed region: K steps through the product entry points
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -301,7 +319,7 @@ def main():
                 for j, name in enumerate(Step.STAGES)}
     staged_total = float(np.mean([e[0].elapsed_time(e[7]) for e in evs]))
 
-    alg = algorithmic(p, touched, st.act_fused)
+    alg = algorithmic(p, touched, st.act_fused, items)
     tflops = alg["flops"] / (ms * 1e-3) / 1e12
     tok_s = p.M / (ms * 1e-3)
     dt = "fp8" if p.wdtype == "fp8" else "bf16"
@@ -329,7 +347,9 @@ def main():
         "config": {"workload": args.workload, "M": p.M, "H": p.H, "I": p.I, "E": p.E,
                    "topk": p.topk, "block_m": p.block_m, "weights": p.wdtype,
                    "weight_layout": st.layout,
-                   "experts_touched": touched, "seed": p.seed},
+                   "experts_touched": touched, "seed": p.seed,
+                   **({"ep_size": p.ep_size, "ep_rank": p.ep_rank, "experts_held": len(p.local_experts),
+                       "routed_items_here": items} if p.ep_size > 1 else {})},
         "step_roofline_frac": round(t_star / (ms * 1e-3), 4),
         "roofline": roof,
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},

@@ -32,7 +32,8 @@ extern "C" {
 
 typedef enum {
     MOE_OK = 0,
-    MOE_E_INVALID = 1,     /* null pointer, negative size, topk outside [1, min(E, 32)] */
+    MOE_E_INVALID = 1,     /* null pointer, negative size, topk outside [1, min(E, 32)]
+                              (E: num_global_experts when it is set) */
     MOE_E_UNSUPPORTED = 2, /* E > 256, H or I not a multiple of 128, unknown block_m,
                               dtype or weight layout, fp8 with block_m 16 or 256, the
                               tiled layout other than bf16 with block_m 16, 128 or 256,
@@ -82,6 +83,9 @@ typedef struct {
     int32_t apply_router_weight_on_input; /* 0: weight the expert outputs in the final sum;
                                              1: weight the SiLU-and-mul output instead */
     int32_t weight_layout; /* moe_wlayout_t of w13 and w2 (0: row-major) */
+    int32_t num_global_experts; /* expert-parallel shard: the range of topk_ids,
+                                   E being the experts held here (fused_experts_ep);
+                                   0 otherwise. topk <= num_global_experts */
 } moe_problem_t;
 
 /*
@@ -133,6 +137,19 @@ moe_status_t moe_align_block_size(const int32_t *topk_ids, int64_t M, int32_t to
                                   int32_t *inv_perm, void *stream);
 
 /*
+ * Align on one rank of an expert-parallel shard: topk_ids hold global ids in
+ * [0, num_global_experts); expert_map as for fused_experts_ep. Items of
+ * experts not held here get no row and inv_perm -1; the segments are those of
+ * the E local experts in local order. Sizes and outputs as for
+ * moe_align_block_size (cap = moe_align_capacity(M, topk, E, block_m)).
+ */
+moe_status_t moe_align_block_size_ep(const int32_t *topk_ids, int64_t M, int32_t topk,
+                                     int32_t num_global_experts, const int32_t *expert_map,
+                                     int32_t E, int32_t block_m, int32_t *sorted_token_ids,
+                                     int32_t *expert_ids, int32_t *num_tokens_post_padded,
+                                     int32_t *inv_perm, void *stream);
+
+/*
  * Dynamic fp8 quantisation of activations, per row and per 128 columns
  * ("DeepGEMM FusedMoE on Blackwell", section 2.5 / 1.1 step 4;
  *  "fused_moe.py analysis", "FP8 W8A8").
@@ -172,6 +189,29 @@ moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w1
                            const float *w13_scale, const void *w2, const float *w2_scale,
                            const int32_t *topk_ids, const float *topk_weights, void *y,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The same layer on one rank of an expert-parallel shard ("vLLM
+ * modular_kernel.py notes", the expert_map argument of fused_experts: a table
+ * from global expert ids to this rank's experts, -1 for experts held by other
+ * ranks; "DeepGEMM FusedMoE on Blackwell", 2.6.2 and 2.6.5: ep_scatter and
+ * ep_gather skip the items and slots of remote experts).
+ *   p->num_global_experts  G > 0, the range of topk_ids; p->E the experts held
+ *                 here, whose weights w13 [E, 2I, H] and w2 [E, H, I] are passed
+ *   expert_map    [G] int32: the local index in [0, E) of global expert g, or -1
+ *                 (entries outside [0, E), and ids outside [0, G), count as not
+ *                 held here)
+ *   y[t, :] = bf16( sum over the token's slots j whose expert is held here of
+ *                   alpha_{t,j} * expert output ): this rank's part of the
+ *             layer, which a combine across ranks adds up (not done here).
+ * Everything else as for fused_experts; moe_workspace_bytes(p) sizes the
+ * workspace. p->num_global_experts must be 0 for fused_experts.
+ */
+moe_status_t fused_experts_ep(const moe_problem_t *p, const int32_t *expert_map, const void *x,
+                              const void *w13, const float *w13_scale, const void *w2,
+                              const float *w2_scale, const int32_t *topk_ids,
+                              const float *topk_weights, void *y, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * The stages of fused_experts, for callers that build their own pipeline or

@@ -20,8 +20,9 @@ MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 
-EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_quant_fp8_groups",
-           "moe_workspace_bytes", "fused_experts", "moe_expert_gemm_workspace_bytes",
+EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_align_block_size_ep",
+           "moe_quant_fp8_groups", "moe_workspace_bytes", "fused_experts", "fused_experts_ep",
+           "moe_expert_gemm_workspace_bytes",
            "moe_expert_gemm", "moe_silu_and_mul",
            "moe_expert_gemm_act_supported", "moe_expert_gemm_act", "moe_permute_scales",
            "moe_unpermute_reduce", "moe_pack_weights", "moe_status_string")
@@ -31,7 +32,7 @@ class MoeProblem(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("wdtype", ctypes.c_int32), ("apply_router_weight_on_input", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("num_global_experts", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -55,11 +56,14 @@ def lib() -> ctypes.CDLL:
         L.moe_align_capacity.argtypes = [_I64, _I32, _I32, _I32]
         L.moe_align_capacity.restype = _I64
         L.moe_align_block_size.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P]
+        L.moe_align_block_size_ep.argtypes = [_P, _I64, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P]
         L.moe_quant_fp8_groups.argtypes = [_P, _I64, _I32, _P, _P, _P]
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeProblem)]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.fused_experts.argtypes = [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]
+        L.fused_experts_ep.argtypes = [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, ctypes.c_size_t, _P]
         PP = ctypes.POINTER(MoeProblem)
         L.moe_expert_gemm_workspace_bytes.argtypes = [PP]
         L.moe_expert_gemm_workspace_bytes.restype = ctypes.c_size_t
@@ -73,7 +77,8 @@ def lib() -> ctypes.CDLL:
         L.moe_pack_weights.argtypes = [PP, _I32, _P, _P, _P]
         L.moe_status_string.argtypes = [_I32]
         L.moe_status_string.restype = ctypes.c_char_p
-        for name in ("moe_topk", "moe_align_block_size", "moe_quant_fp8_groups", "fused_experts",
+        for name in ("moe_topk", "moe_align_block_size", "moe_align_block_size_ep",
+                     "moe_quant_fp8_groups", "fused_experts", "fused_experts_ep",
                      "moe_expert_gemm", "moe_silu_and_mul", "moe_permute_scales",
                      "moe_expert_gemm_act", "moe_unpermute_reduce", "moe_pack_weights"):
             getattr(L, name).restype = _I32
@@ -161,6 +166,26 @@ def moe_align_block_size(topk_ids: torch.Tensor, E: int, block_m: int, stream=No
     return sorted_ids, expert_ids, npp, inv
 
 
+def moe_align_block_size_ep(topk_ids: torch.Tensor, expert_map: torch.Tensor, E: int, block_m: int,
+                            stream=None):
+    """Align on one expert-parallel rank: topk_ids are global, expert_map [G] int32 sends
+    them to the E local experts or -1. Same outputs as moe_align_block_size."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(expert_map, torch.int32, "expert_map")
+    M, k = topk_ids.shape
+    cap = moe_align_capacity(M, k, E, block_m)
+    dev = topk_ids.device
+    sorted_ids = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(max(cap, 0) // block_m, dtype=torch.int32, device=dev)
+    npp = torch.zeros(1, dtype=torch.int32, device=dev)
+    inv = torch.empty((M, k), dtype=torch.int32, device=dev)
+    _check(lib().moe_align_block_size_ep(_ptr(topk_ids), M, k, expert_map.numel(), _ptr(expert_map),
+                                         E, block_m, _ptr(sorted_ids), _ptr(expert_ids), _ptr(npp),
+                                         _ptr(inv), _stream(stream)),
+           "moe_align_block_size_ep")
+    return sorted_ids, expert_ids, npp, inv
+
+
 def moe_quant_fp8_groups(x: torch.Tensor, stream=None):
     """Per-row, per-128-column dynamic e4m3 quantisation -> (q, scale)."""
     _need(x, torch.bfloat16, "x")
@@ -173,8 +198,9 @@ def moe_quant_fp8_groups(x: torch.Tensor, stream=None):
 
 
 def make_problem(M, H, I, E, topk, block_m, wdtype=MOE_W_BF16, on_input=False,
-                 weight_layout=MOE_LAYOUT_ROWS) -> MoeProblem:
-    return MoeProblem(M, H, I, E, topk, block_m, wdtype, int(on_input), weight_layout)
+                 weight_layout=MOE_LAYOUT_ROWS, num_global_experts=0) -> MoeProblem:
+    return MoeProblem(M, H, I, E, topk, block_m, wdtype, int(on_input), weight_layout,
+                      num_global_experts)
 
 
 def moe_workspace_bytes(p: MoeProblem) -> int:
@@ -190,10 +216,15 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
                   topk_weights: torch.Tensor, block_m: int, w13_scale: torch.Tensor | None = None,
                   w2_scale: torch.Tensor | None = None, apply_router_weight_on_input=False,
                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                  stream=None, weight_layout=MOE_LAYOUT_ROWS) -> torch.Tensor:
+                  stream=None, weight_layout=MOE_LAYOUT_ROWS,
+                  expert_map: torch.Tensor | None = None) -> torch.Tensor:
     """y = fused MoE expert forward (bf16 [M, H]). `out` may be `x` (in place).
 
-    weight_layout MOE_LAYOUT_TILED: w13 and w2 come from moe_pack_weights (same shapes)."""
+    weight_layout MOE_LAYOUT_TILED: w13 and w2 come from moe_pack_weights (same shapes).
+    expert_map [G] int32 (one expert-parallel rank): topk_ids are global ids in [0, G),
+    w13 / w2 hold this rank's E experts, and y sums only the slots of those experts."""
+    if expert_map is not None:
+        _need(expert_map, torch.int32, "expert_map")
     _need(x, torch.bfloat16, "x")
     fp8 = w13.dtype == torch.float8_e4m3fn
     wdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
@@ -211,15 +242,22 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
         raise ValueError("fused_experts: inconsistent shapes")
     p = make_problem(M, H, N2 // 2, E, topk_ids.shape[1], block_m,
                      MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16, apply_router_weight_on_input,
-                     weight_layout)
+                     weight_layout, 0 if expert_map is None else expert_map.numel())
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
         workspace = workspace_for(p, x.device)
-    _check(lib().fused_experts(ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
-                               _ptr(w2_scale), _ptr(topk_ids), _ptr(topk_weights), _ptr(out),
-                               _ptr(workspace), workspace.numel(), _stream(stream)),
-           "fused_experts")
+    if expert_map is None:
+        _check(lib().fused_experts(ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                   _ptr(w2_scale), _ptr(topk_ids), _ptr(topk_weights), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)),
+               "fused_experts")
+    else:
+        _check(lib().fused_experts_ep(ctypes.byref(p), _ptr(expert_map), _ptr(x), _ptr(w13),
+                                      _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(topk_ids),
+                                      _ptr(topk_weights), _ptr(out), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)),
+               "fused_experts_ep")
     return out
 
 

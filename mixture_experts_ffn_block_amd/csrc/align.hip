@@ -19,6 +19,13 @@
 //      inside a segment.
 // Padding rows and the tail get the sentinel R; blocks past the padded total
 // get expert -1.
+//
+// Expert-parallel shard ("vLLM modular_kernel.py notes", expert_map: global
+// expert id -> this rank's expert, -1 for experts on other ranks; "DeepGEMM
+// FusedMoE on Blackwell", 2.6.2 ep_scatter skips items of remote experts): with
+// a map, each id is looked up first; items whose expert is not local are
+// neither counted nor placed and get inv_perm -1, so the GEMMs never see them
+// and the reduce skips their slots.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,8 +35,16 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / MOE_WAVE;
 constexpr int kMaxE = 256;
 
+// this rank's expert of global id `id`: the id itself without a map; ids outside
+// the routing range and map entries outside [0, E) count as not local (-1)
+__device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ emap, int E_global) {
+    if (emap == nullptr) return id;
+    return static_cast<unsigned>(id) < static_cast<unsigned>(E_global) ? emap[id] : -1;
+}
+
 __global__ __launch_bounds__(kThreads) void align_kernel(
     const int32_t* __restrict__ ids, int64_t R, int E, int B, int64_t cap,
+    const int32_t* __restrict__ emap, int E_global,
     int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids, int32_t* __restrict__ npp_out,
     int32_t* __restrict__ inv_perm) {
     __shared__ int32_t wave_off[kWaves][kMaxE];  // counts, then running offsets
@@ -46,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
 
     // 1. histogram
     for (int64_t r = c0 + lane; r < c1; r += 64) {
-        const int e = ids[r];
+        const int e = local_expert(ids[r], emap, E_global);
         if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&wave_off[wave][e], 1);
     }
     __syncthreads();
@@ -102,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     // 3. stable scatter
     for (int64_t base = c0; base < c1; base += 64) {
         const int64_t r = base + lane;
-        const int e = r < c1 ? ids[r] : -1;
+        const int e = r < c1 ? local_expert(ids[r], emap, E_global) : -1;
         const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
         uint64_t peers = ballot64(valid);
 #pragma unroll
@@ -126,9 +141,9 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
 }  // namespace
 
 hipError_t launch_align(const int32_t* ids, int64_t R, int E, int B, int64_t cap,
-                        int32_t* sorted, int32_t* expert_ids, int32_t* npp, int32_t* inv_perm,
-                        hipStream_t stream) {
-    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), 0, stream, ids, R, E, B, cap,
-                       sorted, expert_ids, npp, inv_perm);
+                        const int32_t* emap, int E_global, int32_t* sorted, int32_t* expert_ids,
+                        int32_t* npp, int32_t* inv_perm, hipStream_t stream) {
+    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), 0, stream, ids, R, E, B, cap, emap,
+                       E_global, sorted, expert_ids, npp, inv_perm);
     return hipGetLastError();
 }

@@ -60,10 +60,17 @@ Layout layout(const moe_problem_t& p) {
     return L;
 }
 
+constexpr int kMaxGlobalE = 1 << 16;  // routing range of an expert map
+
 moe_status_t check_problem(const moe_problem_t* p) {
     if (!p) return MOE_E_INVALID;
     if (p->M < 0 || p->H <= 0 || p->I <= 0 || p->E <= 0 || p->topk <= 0) return MOE_E_INVALID;
-    if (p->topk > p->E || p->topk > kMaxTopk) return MOE_E_INVALID;
+    if (p->num_global_experts < 0) return MOE_E_INVALID;
+    if (p->num_global_experts > kMaxGlobalE) return MOE_E_UNSUPPORTED;
+    // top-k picks distinct experts of the routing range: the global experts under
+    // an expert map, else the E experts held here
+    const int e_route = p->num_global_experts > 0 ? p->num_global_experts : p->E;
+    if (p->topk > e_route || p->topk > kMaxTopk) return MOE_E_INVALID;
     if (p->E > kMaxE || p->H % 128 || p->I % 128) return MOE_E_UNSUPPORTED;
     if (!block_m_ok(p->block_m)) return MOE_E_UNSUPPORTED;
     if (p->wdtype != MOE_W_BF16 && p->wdtype != MOE_W_FP8_E4M3_BLOCK128) return MOE_E_UNSUPPORTED;
@@ -251,8 +258,25 @@ moe_status_t moe_align_block_size(const int32_t* topk_ids, int64_t M, int32_t to
     // with M == 0 only num_tokens_post_padded is written (0); the rest may be null
     if (!num_tokens_post_padded) return MOE_E_INVALID;
     if (M > 0 && (!topk_ids || !sorted_token_ids || !expert_ids || !inv_perm)) return MOE_E_INVALID;
-    return hip_status(launch_align(topk_ids, M * topk, E, block_m, cap, sorted_token_ids,
+    return hip_status(launch_align(topk_ids, M * topk, E, block_m, cap, nullptr, 0, sorted_token_ids,
                                    expert_ids, num_tokens_post_padded, inv_perm,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_align_block_size_ep(const int32_t* topk_ids, int64_t M, int32_t topk,
+                                     int32_t num_global_experts, const int32_t* expert_map,
+                                     int32_t E, int32_t block_m, int32_t* sorted_token_ids,
+                                     int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                                     int32_t* inv_perm, void* stream) {
+    if (M < 0 || E <= 0 || topk <= 0 || block_m <= 0 || num_global_experts <= 0) return MOE_E_INVALID;
+    if (topk > num_global_experts || topk > kMaxTopk) return MOE_E_INVALID;
+    if (E > kMaxE || num_global_experts > kMaxGlobalE || !block_m_ok(block_m)) return MOE_E_UNSUPPORTED;
+    const int64_t cap = moe_align_capacity(M, topk, E, block_m);
+    if (M * topk >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
+    if (!num_tokens_post_padded || !expert_map) return MOE_E_INVALID;
+    if (M > 0 && (!topk_ids || !sorted_token_ids || !expert_ids || !inv_perm)) return MOE_E_INVALID;
+    return hip_status(launch_align(topk_ids, M * topk, E, block_m, cap, expert_map, num_global_experts,
+                                   sorted_token_ids, expert_ids, num_tokens_post_padded, inv_perm,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -272,12 +296,16 @@ size_t moe_workspace_bytes(const moe_problem_t* p) {
     return static_cast<size_t>(layout(*p).total);
 }
 
-moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w13,
-                           const float* w13_scale, const void* w2, const float* w2_scale,
-                           const int32_t* topk_ids, const float* topk_weights, void* y,
-                           void* workspace, size_t workspace_bytes, void* stream) {
-    const moe_status_t st = check_problem(p);
-    if (st != MOE_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// fused_experts and fused_experts_ep: emap is null (ids are local) or holds
+// p->num_global_experts entries
+moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* x, const void* w13,
+                       const float* w13_scale, const void* w2, const float* w2_scale,
+                       const int32_t* topk_ids, const float* topk_weights, void* y,
+                       void* workspace, size_t workspace_bytes, void* stream) {
     if (p->M == 0) return MOE_OK;
     const bool fp8 = p->wdtype == MOE_W_FP8_E4M3_BLOCK128;
     if (!x || !w13 || !w2 || !topk_ids || !topk_weights || !y) return MOE_E_INVALID;
@@ -306,8 +334,8 @@ moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w1
         a1 = ws + L.xq;
         a1_scale = reinterpret_cast<const float*>(ws + L.xst);
     }
-    err = launch_align(topk_ids, M * p->topk, p->E, p->block_m, L.cap, sorted, expert_ids, npp,
-                       inv_perm, s);
+    err = launch_align(topk_ids, M * p->topk, p->E, p->block_m, L.cap, emap, p->num_global_experts,
+                       sorted, expert_ids, npp, inv_perm, s);
     if (err != hipSuccess) return MOE_E_HIP;
     if (fp8) {
         err = permute_stage(*p, reinterpret_cast<const float*>(ws + L.xs), sorted, npp,
@@ -329,6 +357,33 @@ moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w1
                      expert_ids, npp, ho, L.split >= 0 ? ws + L.split : nullptr, s);
     if (err != hipSuccess) return MOE_E_HIP;
     return hip_status(reduce_stage(*p, ho, inv_perm, topk_weights, y, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w13,
+                           const float* w13_scale, const void* w2, const float* w2_scale,
+                           const int32_t* topk_ids, const float* topk_weights, void* y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->num_global_experts != 0) return MOE_E_INVALID;  // global ids need the expert map
+    return run_fused(p, nullptr, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y,
+                     workspace, workspace_bytes, stream);
+}
+
+moe_status_t fused_experts_ep(const moe_problem_t* p, const int32_t* expert_map, const void* x,
+                              const void* w13, const float* w13_scale, const void* w2,
+                              const float* w2_scale, const int32_t* topk_ids,
+                              const float* topk_weights, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->num_global_experts <= 0 || !expert_map) return MOE_E_INVALID;
+    return run_fused(p, expert_map, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y,
+                     workspace, workspace_bytes, stream);
 }
 
 size_t moe_expert_gemm_workspace_bytes(const moe_problem_t* p) {

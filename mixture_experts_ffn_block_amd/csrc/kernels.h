@@ -54,8 +54,10 @@ constexpr int kSplitSlots = 256;  // partial tiles of the split-K workspace
 
 hipError_t launch_topk_softmax(const float* logits, int64_t M, int E, int k, int renormalize,
                                int32_t* ids, float* weights, hipStream_t stream);
-hipError_t launch_align(const int32_t* ids, int64_t R, int E, int B, int64_t cap, int32_t* sorted,
-                        int32_t* expert_ids, int32_t* npp, int32_t* inv_perm, hipStream_t stream);
+// emap: null, or E_global entries mapping global expert ids to [0, E) or -1 (not local)
+hipError_t launch_align(const int32_t* ids, int64_t R, int E, int B, int64_t cap,
+                        const int32_t* emap, int E_global, int32_t* sorted, int32_t* expert_ids,
+                        int32_t* npp, int32_t* inv_perm, hipStream_t stream);
 int gemm_supported_block_m(int bm);
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStream_t stream);
 bool gemm_act_supported(int block_m, bool fp8, int K);  // a fused SiLU-and-mul GEMM1 exists

@@ -23,6 +23,11 @@ generation is chunked):
 * ``w2``      [E, H, I]  ~ N(0, 1/sqrt(I)) -> bf16.
 * fp8 workloads: ``w13q``/``w2q`` float8_e4m3fn with fp32 scales per 128x128
   block, ``scale = amax(block) / 448``, ``q = e4m3(w / scale)``.
+* Expert-parallel workloads (``ep_size`` > 1): the logits cover all E experts
+  (global routing); rank ``ep_rank`` holds the contiguous range of E / ep_size
+  experts starting at ``ep_rank * E / ep_size``, whose weights are the same
+  draws as in the unsharded workload, and ``expert_map`` [E] int32 sends a
+  global expert to its index in that range or to -1.
 
 The second argument of N(.,.) is the standard deviation.
 """
@@ -47,6 +52,12 @@ WORKLOADS = {
                        bias_std=0.0),
     "fp8_block_m4096": dict(M=4096, H=7168, I=2048, E=256, topk=8, wdtype="fp8",
                             block_m=128, bias_std=0.0),
+    # one rank of an 8-way expert-parallel split of the skewed workload: the rank
+    # with the most routed items (13863 of 65536, 20 experts touched) when the
+    # inputs are drawn on the GPU (torch's CPU and GPU generators differ), which
+    # sets the step time of the split layer
+    "dsv3_ep8_rank2_prefill_m8192": dict(M=8192, H=7168, I=2048, E=256, topk=8, wdtype="bf16",
+                                         block_m=128, bias_std=1.5, ep_size=8, ep_rank=2),
 }
 
 _T_X, _T_LOGITS, _T_BIAS, _T_W13, _T_W2 = 1, 2, 3, 4, 5
@@ -66,6 +77,14 @@ class Problem:
     bias_std: float = 0.0
     seed: int = 0
     apply_router_weight_on_input: bool = False
+    ep_size: int = 1              # expert-parallel ranks; E counts the global experts
+    ep_rank: int = 0
+
+    @property
+    def local_experts(self) -> range:
+        """Global ids of the experts this rank holds (all E without expert parallelism)."""
+        n = self.E // self.ep_size
+        return range(self.ep_rank * n, (self.ep_rank + 1) * n)
 
     @staticmethod
     def named(name: str, **overrides) -> "Problem":
@@ -117,6 +136,7 @@ class Inputs:
     w13s: torch.Tensor | None = None  # [E, 2I/128, H/128] fp32
     w2q: torch.Tensor | None = None   # [E, H, I] float8_e4m3fn
     w2s: torch.Tensor | None = None   # [E, H/128, I/128] fp32
+    expert_map: torch.Tensor | None = None  # [E] int32 on expert-parallel ranks, else None
 
 
 def make_inputs(p: Problem, device="cpu") -> Inputs:
@@ -126,23 +146,30 @@ def make_inputs(p: Problem, device="cpu") -> Inputs:
     logits = _randn((M, E), device, p.seed, _T_LOGITS)
     if p.bias_std:
         logits += _randn((E,), device, p.seed, _T_BIAS, std=p.bias_std)[None, :]
+    held = p.local_experts
+    emap = None
+    if p.ep_size > 1:
+        emap = torch.full((E,), -1, dtype=torch.int32)
+        emap[held.start:held.stop] = torch.arange(len(held), dtype=torch.int32)
+        emap = emap.to(device)
+    EL = len(held)
     if p.wdtype == "bf16":
-        w13 = torch.empty((E, 2 * I, H), dtype=torch.bfloat16, device=device)
-        w2 = torch.empty((E, H, I), dtype=torch.bfloat16, device=device)
-        for e in range(E):
-            w13[e] = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H))
-            w2[e] = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I))
-        return Inputs(x, logits, w13, w2)
+        w13 = torch.empty((EL, 2 * I, H), dtype=torch.bfloat16, device=device)
+        w2 = torch.empty((EL, H, I), dtype=torch.bfloat16, device=device)
+        for i, e in enumerate(held):
+            w13[i] = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H))
+            w2[i] = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I))
+        return Inputs(x, logits, w13, w2, expert_map=emap)
     if p.wdtype == "fp8":
-        w13q = torch.empty((E, 2 * I, H), dtype=torch.float8_e4m3fn, device=device)
-        w2q = torch.empty((E, H, I), dtype=torch.float8_e4m3fn, device=device)
-        w13s = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
-        w2s = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=device)
-        for e in range(E):
+        w13q = torch.empty((EL, 2 * I, H), dtype=torch.float8_e4m3fn, device=device)
+        w2q = torch.empty((EL, H, I), dtype=torch.float8_e4m3fn, device=device)
+        w13s = torch.empty((EL, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
+        w2s = torch.empty((EL, H // 128, I // 128), dtype=torch.float32, device=device)
+        for i, e in enumerate(held):
             m13 = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H)).to(torch.bfloat16)
-            w13q[e], w13s[e] = block_quant_fp8(m13)
+            w13q[i], w13s[i] = block_quant_fp8(m13)
             m2 = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I)).to(torch.bfloat16)
-            w2q[e], w2s[e] = block_quant_fp8(m2)
-        return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s)
+            w2q[i], w2s[i] = block_quant_fp8(m2)
+        return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s, expert_map=emap)
     raise ValueError(f"unknown weight dtype {p.wdtype!r}")
 

@@ -138,3 +138,31 @@ def test_problem_struct_matches_header():
     assert names == [f[0] for f in moe.MoeProblem._fields_]
     kinds = [k for k, decl in fields for _ in decl.split(",")]
     assert [ctypes.sizeof(f[1]) for f in moe.MoeProblem._fields_] == [8 if k == "int64_t" else 4 for k in kinds]
+
+
+def test_expert_parallel_validation():
+    L = moe.lib()
+    d = ctypes.c_void_p(1 << 20)
+    # an expert-parallel problem: 256 global experts, 4 held here, top-8 over the global range
+    p = P(M=64, E=4, topk=8, num_global_experts=256, block_m=128)
+    need = moe.moe_workspace_bytes(p)
+    assert need > 0
+    assert L.fused_experts(ctypes.byref(p), d, d, None, d, None, d, d, d, d, need, None) == moe.MOE_E_INVALID
+    assert L.fused_experts_ep(ctypes.byref(p), None, d, d, None, d, None, d, d, d, d, need, None) \
+        == moe.MOE_E_INVALID
+    assert L.fused_experts_ep(ctypes.byref(p), d, d, d, None, d, None, d, d, d, d, need - 1, None) \
+        == moe.MOE_E_WORKSPACE
+    plain = P()
+    assert L.fused_experts_ep(ctypes.byref(plain), d, d, d, None, d, None, d, d, d, d, 1 << 30, None) \
+        == moe.MOE_E_INVALID                                       # no global range given
+    assert moe.moe_workspace_bytes(P(E=4, topk=8)) == 0            # top-8 of 4 local experts
+    assert moe.moe_workspace_bytes(P(num_global_experts=-1)) == 0
+    assert moe.moe_workspace_bytes(P(num_global_experts=1 << 17)) == 0
+    assert L.fused_experts_ep(ctypes.byref(P(M=0, E=4, topk=8, num_global_experts=256)), d, None, None,
+                              None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
+    A = L.moe_align_block_size_ep
+    assert A(d, 4, 8, 4, d, 4, 16, d, d, d, d, None) == moe.MOE_E_INVALID     # topk > global experts
+    assert A(d, 4, 2, 256, None, 4, 16, d, d, d, d, None) == moe.MOE_E_INVALID
+    assert A(d, 4, 2, 256, d, 300, 16, d, d, d, d, None) == moe.MOE_E_UNSUPPORTED
+    assert A(d, 4, 2, 256, d, 4, 24, d, d, d, d, None) == moe.MOE_E_UNSUPPORTED
+    assert A(None, 4, 2, 256, d, 4, 16, d, d, d, d, None) == moe.MOE_E_INVALID

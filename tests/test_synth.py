@@ -45,3 +45,18 @@ def test_fp8_block_quant_recipe():
     # e4m3 half-ulp of the block amax
     q = inp.w13q.float().view(2, 2, 128, 2, 128)
     assert torch.all(q.abs().amax(dim=(2, 4)) == 448.0)
+
+
+def test_expert_parallel_rank_holds_its_slice_of_the_same_weights():
+    full = synth.make_inputs(synth.Problem(M=8, H=128, I=128, E=8, topk=2), "cpu")
+    for wdtype in ("bf16", "fp8"):
+        p = synth.Problem(M=8, H=128, I=128, E=8, topk=2, wdtype=wdtype, ep_size=4, ep_rank=2)
+        r = synth.make_inputs(p, "cpu")
+        assert list(p.local_experts) == [4, 5]
+        assert r.expert_map.tolist() == [-1, -1, -1, -1, 0, 1, -1, -1]
+        assert torch.equal(r.x, full.x) and torch.equal(r.logits, full.logits)  # global routing
+        if wdtype == "bf16":
+            assert torch.equal(r.w13, full.w13[4:6]) and torch.equal(r.w2, full.w2[4:6])
+        else:
+            assert r.w13q.shape[0] == 2 and r.w2s.shape[0] == 2
+    assert synth.make_inputs(synth.Problem(M=2, H=128, I=128, E=4, topk=1), "cpu").expert_map is None
