@@ -63,6 +63,8 @@ def lib():
                                          _P, _P, _I32, _P, _I32, _I64, _I64, _P, _P],
             "oracle_dense_experts_bf16": [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                           _P, _P],
+            "oracle_batched_experts_bf16": [_I32, _I64, _I32, _I32, _P, _P, _P, _P, _P],
+            "oracle_batched_experts_fp8": [_I32, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -282,3 +284,32 @@ def dense_experts_bf16(x, w13, w2, ids, weights, return_acc=False):
     lib().oracle_dense_experts_bf16(M, H, N2 // 2, E, k, _p(x), _p(w13), _p(w2), _p(ids),
                                     _p(weights), _p(y), _p(acc))
     return (y, acc) if return_acc else y
+
+
+# ---------------------------------------------------------- batched form ---
+
+def batched_experts_bf16(a, counts, w13, w2):
+    """out [E, max_M, H] (uint16 bf16 bits): expert e applied, unweighted, to rows
+    i < counts[e] of its batch a[e]; other rows 0."""
+    a, w13, w2 = _c(a, np.uint16), _c(w13, np.uint16), _c(w2, np.uint16)
+    counts = _c(counts, np.int32)
+    E, max_M, H = a.shape
+    I = w13.shape[1] // 2
+    out = np.empty((E, max_M, H), np.uint16)
+    if lib().oracle_batched_experts_bf16(E, max_M, H, I, _p(a), _p(counts), _p(w13), _p(w2), _p(out)):
+        raise ValueError("oracle_batched_experts_bf16: negative count")
+    return out
+
+
+def batched_experts_fp8(a, counts, w13q, w13s, w2q, w2s):
+    """The batched form with e4m3 weights and 128x128 block scales."""
+    a, counts = _c(a, np.uint16), _c(counts, np.int32)
+    w13q, w2q = _c(w13q, np.uint8), _c(w2q, np.uint8)
+    w13s, w2s = _c(w13s, np.float32), _c(w2s, np.float32)
+    E, max_M, H = a.shape
+    I = w13q.shape[1] // 2
+    out = np.empty((E, max_M, H), np.uint16)
+    if lib().oracle_batched_experts_fp8(E, max_M, H, I, _p(a), _p(counts), _p(w13q), _p(w13s),
+                                        _p(w2q), _p(w2s), _p(out)):
+        raise ValueError("oracle_batched_experts_fp8: negative count")
+    return out

@@ -464,3 +464,73 @@ int oracle_dense_experts_bf16(int64_t M, int H, int I, int E, int k,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Batched-experts form ([MK] 6.x, 7.1: after a low-latency dispatch the      */
+/* activations arrive as [E, max_M, K], one batch per local expert, with the  */
+/* per-expert token counts; [DG] 2.5: the masked grouped GEMM computes only   */
+/* the first count rows of each batch, and the combine applies the weights).  */
+/* ------------------------------------------------------------------------ */
+
+/* out[e, i] = W2_e(SiLU(G_e a[e, i]) * U_e a[e, i]) in bf16 for i < counts[e]
+ * (clamped to max_M), unweighted; other rows are set to 0. Returns 1 if a
+ * count is negative. */
+int oracle_batched_experts_bf16(int E, int64_t max_M, int H, int I, const uint16_t *a,
+                                const int32_t *counts, const uint16_t *w13, const uint16_t *w2,
+                                uint16_t *out)
+{
+    for (int e = 0; e < E; ++e)
+        if (counts[e] < 0) return 1;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int e = 0; e < E; ++e) {
+        for (int64_t i = 0; i < max_M; ++i) {
+            uint16_t *row = out + ((int64_t)e * max_M + i) * H;
+            if (i >= counts[e]) {
+                for (int n = 0; n < H; ++n) row[n] = 0;
+                continue;
+            }
+            uint16_t *h = malloc(sizeof(uint16_t) * 2 * (size_t)I);
+            uint16_t *z = malloc(sizeof(uint16_t) * (size_t)I);
+            oracle_gemm1_bf16(a + ((int64_t)e * max_M + i) * H, w13 + (int64_t)e * 2 * I * H, H, I, h);
+            oracle_act_bf16(h, I, 1.0, z);
+            oracle_gemm2_bf16(z, w2 + (int64_t)e * H * I, H, I, row);
+            free(h); free(z);
+        }
+    }
+    return 0;
+}
+
+/* The same with e4m3 weights and 128x128 block scales: each row is quantised
+ * per 128 columns, and z again after SiLU-and-mul (as in the routed form). */
+int oracle_batched_experts_fp8(int E, int64_t max_M, int H, int I, const uint16_t *a,
+                               const int32_t *counts, const uint8_t *w13q, const float *w13s,
+                               const uint8_t *w2q, const float *w2s, uint16_t *out)
+{
+    for (int e = 0; e < E; ++e)
+        if (counts[e] < 0) return 1;
+    int64_t s13 = (int64_t)(2 * I / 128) * (H / 128), s2 = (int64_t)(H / 128) * (I / 128);
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int e = 0; e < E; ++e) {
+        for (int64_t i = 0; i < max_M; ++i) {
+            uint16_t *row = out + ((int64_t)e * max_M + i) * H;
+            if (i >= counts[e]) {
+                for (int n = 0; n < H; ++n) row[n] = 0;
+                continue;
+            }
+            const uint16_t *x = a + ((int64_t)e * max_M + i) * H;
+            float *xf = malloc(sizeof(float) * (size_t)H);
+            uint8_t *xq = malloc((size_t)H);
+            float *xs = malloc(sizeof(float) * (size_t)(H / 128));
+            uint16_t *h = malloc(sizeof(uint16_t) * 2 * (size_t)I);
+            uint8_t *zq = malloc((size_t)I);
+            float *zs = malloc(sizeof(float) * (size_t)(I / 128));
+            for (int c = 0; c < H; ++c) xf[c] = (float)oracle_bf16_to_f64(x[c]);
+            oracle_quant_groups_fp8(xf, H, xq, xs);
+            oracle_gemm_fp8(xq, xs, w13q + (int64_t)e * 2 * I * H, w13s + e * s13, 2 * I, H, h);
+            oracle_act_fp8(h, I, 1.0, zq, zs);
+            oracle_gemm_fp8(zq, zs, w2q + (int64_t)e * H * I, w2s + e * s2, H, I, row);
+            free(xf); free(xq); free(xs); free(h); free(zq); free(zs);
+        }
+    }
+    return 0;
+}
