@@ -184,6 +184,83 @@ class Step:
         ev[7].record()
 
 
+class BatchedStep(Step):
+    """The batched-experts form: the router's items of the workload, presented as one
+    batch of up to M rows per expert (built once, outside every timed region, as a
+    low-latency dispatch would deliver them), then moe_batched_experts. The staged
+    run launches the same kernels as the equivalent top-1 routed problem over the
+    E * M batch rows."""
+
+    STAGES = Step.STAGES
+
+    def __init__(self, p: synth.Problem, d: synth.Inputs, layout: str = "auto"):
+        super().__init__(p, d, layout)
+        if self.fp8 or self.emap is not None:
+            raise SystemExit("the batched workload is bf16 on all experts")
+        m, dev = self.moe, d.x.device
+        E, M, k, H, I, B = p.E, p.M, p.topk, p.H, p.I, p.block_m
+        m.moe_topk(d.logits, k, out=(self.ids, self.w))
+        flat = self.ids.reshape(-1).long()
+        order = torch.argsort(flat, stable=True)            # items by expert, tokens ascending
+        counts = torch.bincount(flat, minlength=E)
+        e_sorted = flat[order]
+        pos = torch.arange(flat.numel(), device=dev) - (torch.cumsum(counts, 0) - counts)[e_sorted]
+        self.a = torch.zeros((E, M, H), dtype=torch.bfloat16, device=dev)
+        self.a[e_sorted, pos] = d.x[order // k]
+        self.counts = counts.to(torch.int32)
+        self.out = torch.empty_like(self.a)
+        self.pb = m.make_problem(M, H, I, E, 1, B, m.MOE_W_BF16, False, self.wl)
+        self.bws = torch.empty(max(m.moe_batched_workspace_bytes(self.pb), 256), dtype=torch.uint8,
+                               device=dev)
+        # the equivalent routed top-1 problem, for the staged run
+        r = torch.arange(M, device=dev)
+        self.qids = torch.where(r[None, :] < counts[:, None], torch.arange(E, device=dev)[:, None],
+                                torch.full_like(r[None, :], -1)).to(torch.int32).reshape(E * M, 1).contiguous()
+        self.q = m.make_problem(E * M, H, I, E, 1, B, m.MOE_W_BF16, False, self.wl)
+        cap = m.moe_align_capacity(E * M, 1, E, B)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.sorted_q = torch.empty(cap, **i32)
+        self.expert_ids_q = torch.empty(cap // B, **i32)
+        self.npp_q = torch.zeros(1, **i32)
+        self.inv_q = torch.empty((E * M, 1), **i32)
+        self.z_q = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
+        self.h_q = torch.empty((cap, 2 * I), dtype=torch.bfloat16, device=dev)
+        self.o_q = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        self.ones_q = torch.ones((E * M, 1), dtype=torch.float32, device=dev)
+        self.act_fused = m.moe_expert_gemm_act_supported(self.q)
+        self.gws = m.gemm_workspace_for(self.q, dev)
+
+    def fused(self):
+        self.moe.moe_batched_experts(self.a, self.counts, self.w13, self.w2, self.p.block_m,
+                                     out=self.out, workspace=self.bws, weight_layout=self.wl)
+
+    def staged(self, ev):
+        m, q = self.moe, self.q
+        E, M = self.p.E, self.p.M
+        a = self.a.view(E * M, self.p.H)
+        ev[0].record()
+        ev[1].record()
+        ev[2].record()
+        m.lib().moe_align_block_size(m._ptr(self.qids), E * M, 1, E, self.p.block_m, m._ptr(self.sorted_q),
+                                     m._ptr(self.expert_ids_q), m._ptr(self.npp_q), m._ptr(self.inv_q),
+                                     m._stream())
+        ev[3].record()
+        if self.act_fused:
+            m.moe_expert_gemm_act(q, a, None, self.w13, None, self.sorted_q, self.expert_ids_q, self.npp_q,
+                                  self.ones_q, self.z_q)
+            ev[4].record()
+        else:
+            m.moe_expert_gemm(q, 1, a, self.w13, self.sorted_q, self.expert_ids_q, self.npp_q, self.h_q)
+            ev[4].record()
+            m.moe_silu_and_mul(q, self.h_q, self.sorted_q, self.ones_q, self.npp_q, self.z_q)
+        ev[5].record()
+        m.moe_expert_gemm(q, 2, self.z_q, self.w2, None, self.expert_ids_q, self.npp_q, self.o_q,
+                          workspace=self.gws)
+        ev[6].record()
+        m.moe_unpermute_reduce(q, self.o_q, self.inv_q, self.ones_q, self.out.view(E * M, self.p.H))
+        ev[7].record()
+
+
 def algorithmic(p: synth.Problem, touched: int, act_fused: bool = False, R: int | None = None):
     """Algorithmic FLOP and HBM bytes of the step and of GEMM1 (padding excluded);
     with the activation fused into GEMM1 that kernel writes z instead of h. R: the
@@ -259,6 +336,31 @@ def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.
                       f"accumulation, {threads} OpenMP threads"}
 
 
+def cpu_baseline_batched(p: synth.Problem, d: synth.Inputs, st: "BatchedStep", target_s: float):
+    """The CPU oracle of the batched form on the batches of the first experts."""
+    import oracle
+    threads = oracle.threads()
+    bits16 = lambda t: t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    counts = st.counts.cpu().numpy()
+
+    def run(n):
+        sel = slice(0, n)
+        t0 = time.perf_counter()
+        oracle.batched_experts_bf16(bits16(st.a[sel]), counts[sel], bits16(d.w13[sel]), bits16(d.w2[sel]))
+        return time.perf_counter() - t0
+
+    n = min(p.E, 4)
+    dt = run(n)
+    if dt < target_s / 2 and n < p.E:
+        n = int(min(p.E, max(n, round(n * target_s / dt))))
+        dt = run(n)
+    items = int(np.clip(counts[:n], 0, p.M).sum())
+    return {"value": round(6.0 * items * p.H * p.I / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the batches of the first {n} of {p.E} experts ({items} rows), plain C oracle, "
+                      f"fp64 accumulation, {threads} OpenMP threads"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -275,7 +377,7 @@ def main():
     p = synth.Problem.named(args.workload, **over)
     print(f"# workload {args.workload}: {p}", file=sys.stderr, flush=True)
     d = synth.make_inputs(p, "cuda")
-    st = Step(p, d, args.weight_layout)
+    st = (BatchedStep if p.batched else Step)(p, d, args.weight_layout)
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -349,7 +451,10 @@ def main():
                    "weight_layout": st.layout,
                    "experts_touched": touched, "seed": p.seed,
                    **({"ep_size": p.ep_size, "ep_rank": p.ep_rank, "experts_held": len(p.local_experts),
-                       "routed_items_here": items} if p.ep_size > 1 else {})},
+                       "routed_items_here": items} if p.ep_size > 1 else {}),
+                   **({"form": "batched experts [E, M, H] (the timed step is moe_batched_experts; "
+                               "router and dispatch precede it)", "batch_rows_max": p.M}
+                      if p.batched else {})},
         "step_roofline_frac": round(t_star / (ms * 1e-3), 4),
         "roofline": roof,
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
@@ -358,7 +463,8 @@ def main():
     }
     if args.cpu_seconds > 0:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(p, d, st.ids, st.w, args.cpu_seconds)
+        line["cpu_baseline"] = (cpu_baseline_batched(p, d, st, args.cpu_seconds) if p.batched
+                                else cpu_baseline(p, d, st.ids, st.w, args.cpu_seconds))
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -214,6 +214,34 @@ moe_status_t fused_experts_ep(const moe_problem_t *p, const int32_t *expert_map,
                               size_t workspace_bytes, void *stream);
 
 /*
+ * Batched-experts form ("vLLM modular_kernel.py notes", 6.x and 7.1: after a
+ * low-latency dispatch the activations of a rank arrive as one batch of up to
+ * max_M rows per local expert, [E, max_M, H], with per-expert token counts;
+ * "DeepGEMM FusedMoE on Blackwell", 2.5: the masked grouped GEMM computes only
+ * the first count rows of each batch, and the combine applies the router
+ * weights):
+ *   out[e, i, :] = bf16( W2_e ( SiLU(G_e a[e, i]) * (U_e a[e, i]) ) )
+ *                  for i < expert_num_tokens[e], unweighted; 0 for the other rows.
+ *   p             M = max_M (rows per batch), E = experts (batches), topk = 1,
+ *                 apply_router_weight_on_input = 0, num_global_experts = 0;
+ *                 H, I, block_m, wdtype and weight_layout as for fused_experts
+ *   a             [E, max_M, H] bf16; rows past a count are not read
+ *   expert_num_tokens [E] int32 (device); values above max_M act as max_M,
+ *                 negative ones as 0
+ *   w13, w13_scale, w2, w2_scale as for fused_experts
+ *   out           [E, max_M, H] bf16 out (must not overlap a)
+ *   workspace     at least moe_batched_workspace_bytes(p) bytes, 256-aligned
+ * The rows run through the same kernels as fused_experts with top-1 routing
+ * (row e * max_M + i routed to expert e when it is counted, else nowhere).
+ * M == 0 returns MOE_OK and launches nothing.
+ */
+size_t moe_batched_workspace_bytes(const moe_problem_t *p);  /* host, pure; 0 if invalid */
+moe_status_t moe_batched_experts(const moe_problem_t *p, const void *a,
+                                 const int32_t *expert_num_tokens, const void *w13,
+                                 const float *w13_scale, const void *w2, const float *w2_scale,
+                                 void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The stages of fused_experts, for callers that build their own pipeline or
  * time the stages one by one. fused_experts launches exactly these kernels:
  * for fp8, moe_quant_fp8_groups(x) and moe_permute_scales after the align;

@@ -25,7 +25,8 @@ EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_align_
            "moe_expert_gemm_workspace_bytes",
            "moe_expert_gemm", "moe_silu_and_mul",
            "moe_expert_gemm_act_supported", "moe_expert_gemm_act", "moe_permute_scales",
-           "moe_unpermute_reduce", "moe_pack_weights", "moe_status_string")
+           "moe_unpermute_reduce", "moe_pack_weights", "moe_batched_workspace_bytes",
+           "moe_batched_experts", "moe_status_string")
 
 
 class MoeProblem(ctypes.Structure):
@@ -75,12 +76,16 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_gemm_act.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_unpermute_reduce.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_pack_weights.argtypes = [PP, _I32, _P, _P, _P]
+        L.moe_batched_workspace_bytes.argtypes = [PP]
+        L.moe_batched_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_batched_experts.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_status_string.argtypes = [_I32]
         L.moe_status_string.restype = ctypes.c_char_p
         for name in ("moe_topk", "moe_align_block_size", "moe_align_block_size_ep",
                      "moe_quant_fp8_groups", "fused_experts", "fused_experts_ep",
                      "moe_expert_gemm", "moe_silu_and_mul", "moe_permute_scales",
-                     "moe_expert_gemm_act", "moe_unpermute_reduce", "moe_pack_weights"):
+                     "moe_expert_gemm_act", "moe_unpermute_reduce", "moe_pack_weights",
+                     "moe_batched_experts"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -390,3 +395,42 @@ def moe_pack_weights(p: MoeProblem, which: int, w: torch.Tensor, out: torch.Tens
     _check(lib().moe_pack_weights(ctypes.byref(p), which, _ptr(w), _ptr(out), _stream(stream)),
            "moe_pack_weights")
     return out
+
+
+def moe_batched_experts(a: torch.Tensor, expert_num_tokens: torch.Tensor, w13: torch.Tensor,
+                        w2: torch.Tensor, block_m: int, w13_scale: torch.Tensor | None = None,
+                        w2_scale: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None,
+                        weight_layout=MOE_LAYOUT_ROWS) -> torch.Tensor:
+    """Batched-experts form: a [E, max_M, H] bf16 (one batch per expert), expert_num_tokens
+    [E] int32 -> out [E, max_M, H] bf16, rows past a count 0, unweighted."""
+    _need(a, torch.bfloat16, "a")
+    _need(expert_num_tokens, torch.int32, "expert_num_tokens")
+    fp8 = w13.dtype == torch.float8_e4m3fn
+    wdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    _need(w13, wdt, "w13")
+    _need(w2, wdt, "w2")
+    E, max_M, H = a.shape
+    E2, N2, H2 = w13.shape
+    if E2 != E or H2 != H or tuple(w2.shape) != (E, H, N2 // 2) or expert_num_tokens.numel() != E:
+        raise ValueError("moe_batched_experts: inconsistent shapes")
+    if fp8:
+        _need(w13_scale, torch.float32, "w13_scale")
+        _need(w2_scale, torch.float32, "w2_scale")
+    p = make_problem(max_M, H, N2 // 2, E, 1, block_m,
+                     MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16, False, weight_layout)
+    if out is None:
+        out = torch.empty_like(a)
+    _need(out, torch.bfloat16, "out")
+    if workspace is None:
+        n = moe_batched_workspace_bytes(p)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=a.device)
+    _check(lib().moe_batched_experts(ctypes.byref(p), _ptr(a), _ptr(expert_num_tokens), _ptr(w13),
+                                     _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(out),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_batched_experts")
+    return out
+
+
+def moe_batched_workspace_bytes(p: MoeProblem) -> int:
+    return int(lib().moe_batched_workspace_bytes(ctypes.byref(p)))

@@ -138,7 +138,26 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     }
 }
 
+// batched form ("vLLM modular_kernel.py notes", BatchedExperts: E batches of
+// max_M rows with per-expert counts): one top-1 id per row, -1 past the count
+__global__ __launch_bounds__(256) void batched_ids_kernel(const int32_t* __restrict__ counts, int E,
+                                                          int64_t max_M, int32_t* __restrict__ ids) {
+    const int64_t n = E * max_M;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; r < n;
+         r += static_cast<int64_t>(gridDim.x) * 256) {
+        const int e = static_cast<int>(r / max_M);
+        ids[r] = r - e * max_M < counts[e] ? e : -1;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_batched_ids(const int32_t* counts, int E, int64_t max_M, int32_t* ids, hipStream_t stream) {
+    const int64_t blocks = ceil_div(E * max_M, 256);
+    const dim3 grid(static_cast<unsigned>(blocks < 4096 ? blocks : 4096));
+    hipLaunchKernelGGL(batched_ids_kernel, grid, dim3(256), 0, stream, counts, E, max_M, ids);
+    return hipGetLastError();
+}
 
 hipError_t launch_align(const int32_t* ids, int64_t R, int E, int B, int64_t cap,
                         const int32_t* emap, int E_global, int32_t* sorted, int32_t* expert_ids,

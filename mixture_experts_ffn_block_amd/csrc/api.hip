@@ -24,6 +24,24 @@ int64_t up(int64_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 
 bool block_m_ok(int bm) { return bm == 16 || gemm_supported_block_m(bm); }
 
+// Row geometry of an expert-sorted layout: cap rows, R routed items (entries of
+// sorted_token_ids >= R are padding), item r belonging to token r / topk. The
+// routed form takes the align capacity; the batched form has E batches of M
+// rows, each row its own item (top-1).
+struct Rows {
+    int64_t cap, R;
+    int topk;
+};
+
+Rows routed_rows(const moe_problem_t& p) {
+    return {moe_align_capacity(p.M, p.topk, p.E, p.block_m), p.M * p.topk, p.topk};
+}
+
+Rows batched_rows(const moe_problem_t& p) {
+    const int64_t n = static_cast<int64_t>(p.E) * p.M;
+    return {n, n, 1};
+}
+
 struct Layout {
     int64_t cap, R;
     int64_t sorted, expert_ids, npp, inv_perm, xq, xs, xst, ho, z, zs, split, total;
@@ -37,17 +55,17 @@ int64_t split_bytes(const moe_problem_t& p) {
     return kSplitSlots * kTileOutputs * 4 + kSplitSlots * 4;
 }
 
-Layout layout(const moe_problem_t& p) {
+Layout layout(const moe_problem_t& p, const Rows& rows) {
     Layout L{};
-    L.R = p.M * p.topk;
-    L.cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
+    L.R = rows.R;
+    L.cap = rows.cap;
     const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
     int64_t off = 0;
     auto take = [&](int64_t bytes) { const int64_t o = off; off += up(bytes); return o; };
     L.sorted = take(L.cap * 4);
     L.expert_ids = take(L.cap / p.block_m * 4);
     L.npp = take(4);
-    L.inv_perm = take(L.R * 4);
+    L.inv_perm = take(L.R * 4);  // (unused by the batched form)
     L.xq = fp8 ? take(p.M * p.H) : -1;
     L.xs = fp8 ? take(p.M * (p.H / 128) * 4) : -1;
     L.xst = fp8 ? take(L.cap * (p.H / 128) * 4) : -1;  // GEMM1 scales by sorted position
@@ -97,21 +115,21 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_
 
 // which == 1: C[pos, :2I] = A[token(pos)] w13[e]^T, A rows gathered through sorted
 // which == 2: C[pos, :H]  = A[pos] w2[e]^T
-hipError_t gemm_stage(const moe_problem_t& p, int which, const void* a, const float* a_scale,
-                      const void* w, const float* w_scale, const int32_t* sorted,
-                      const int32_t* expert_ids, const int32_t* npp, void* c, void* split_ws,
-                      hipStream_t s) {
+hipError_t gemm_stage(const moe_problem_t& p, const Rows& rows, int which, const void* a,
+                      const float* a_scale, const void* w, const float* w_scale,
+                      const int32_t* sorted, const int32_t* expert_ids, const int32_t* npp,
+                      void* c, void* split_ws, hipStream_t s) {
     const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
     const int esz = fp8 ? 1 : 2;  // bytes per weight / activation element
-    const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
+    const int64_t cap = rows.cap;
     const int N = which == 1 ? 2 * p.I : p.H;
     const int K = which == 1 ? p.H : p.I;
     GemmArgs g{};
     g.A = a;
     g.lda_bytes = static_cast<int64_t>(K) * esz;
     g.sorted = which == 1 ? sorted : nullptr;
-    g.topk = p.topk;
-    g.R = static_cast<int>(p.M * p.topk);
+    g.topk = rows.topk;
+    g.R = static_cast<int>(rows.R);
     g.W = w;
     g.w_expert_bytes = static_cast<int64_t>(N) * K * esz;
     g.ldw_bytes = static_cast<int64_t>(K) * esz;
@@ -148,19 +166,19 @@ bool act_fused(const moe_problem_t& p) {
     return gemm_act_supported(p.block_m, p.wdtype == MOE_W_FP8_E4M3_BLOCK128, p.H);
 }
 
-hipError_t gemm_act_stage(const moe_problem_t& p, const void* a, const float* a_scale,
-                          const void* w13, const float* w13_scale, const int32_t* sorted,
-                          const int32_t* expert_ids, const int32_t* npp, const float* weights,
-                          void* z, float* z_scale, hipStream_t s) {
+hipError_t gemm_act_stage(const moe_problem_t& p, const Rows& rows, const void* a,
+                          const float* a_scale, const void* w13, const float* w13_scale,
+                          const int32_t* sorted, const int32_t* expert_ids, const int32_t* npp,
+                          const float* weights, void* z, float* z_scale, hipStream_t s) {
     const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
     const int esz = fp8 ? 1 : 2;
-    const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
+    const int64_t cap = rows.cap;
     GemmArgs g{};
     g.A = a;
     g.lda_bytes = static_cast<int64_t>(p.H) * esz;
     g.sorted = sorted;
-    g.topk = p.topk;
-    g.R = static_cast<int>(p.M * p.topk);
+    g.topk = rows.topk;
+    g.R = static_cast<int>(rows.R);
     g.W = w13;
     g.w_expert_bytes = static_cast<int64_t>(2) * p.I * p.H * esz;
     g.ldw_bytes = static_cast<int64_t>(p.H) * esz;
@@ -188,11 +206,11 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const void* a, const float* a_
     return p.block_m == 16 ? launch_stream_gemm(g, s) : launch_grouped_gemm(g, p.block_m, fp8, s);
 }
 
-hipError_t act_stage(const moe_problem_t& p, const void* h, const int32_t* sorted,
+hipError_t act_stage(const moe_problem_t& p, const Rows& rows, const void* h, const int32_t* sorted,
                      const float* weights, const int32_t* npp, void* z, float* z_scale,
                      hipStream_t s) {
-    const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
-    const int R = static_cast<int>(p.M * p.topk);
+    const int64_t cap = rows.cap;
+    const int R = static_cast<int>(rows.R);
     const int on_input = p.apply_router_weight_on_input ? 1 : 0;
     if (p.wdtype == MOE_W_FP8_E4M3_BLOCK128)
         return launch_silu_mul_fp8(static_cast<const bf16_t*>(h), static_cast<uint8_t*>(z),
@@ -201,17 +219,20 @@ hipError_t act_stage(const moe_problem_t& p, const void* h, const int32_t* sorte
                                 weights, R, p.I, cap, npp, on_input, s);
 }
 
-hipError_t permute_stage(const moe_problem_t& p, const float* scale, const int32_t* sorted,
-                         const int32_t* npp, float* out, hipStream_t s) {
-    const int64_t cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m);
-    return launch_permute_scales(scale, p.H / 128, p.topk, static_cast<int>(p.M * p.topk), sorted,
+hipError_t permute_stage(const moe_problem_t& p, const Rows& rows, const float* scale,
+                         const int32_t* sorted, const int32_t* npp, float* out, hipStream_t s) {
+    const int64_t cap = rows.cap;
+    return launch_permute_scales(scale, p.H / 128, rows.topk, static_cast<int>(rows.R), sorted,
                                  npp, cap, out, s);
 }
 
+// weights are applied unless the router weight went onto the SiLU-and-mul input
+// or the caller's combine applies them (unweighted, the batched form)
 hipError_t reduce_stage(const moe_problem_t& p, const void* o, const int32_t* inv_perm,
-                        const float* weights, void* y, hipStream_t s) {
+                        const float* weights, void* y, hipStream_t s, bool unweighted = false) {
     return launch_reduce(static_cast<const bf16_t*>(o), inv_perm, weights, p.M, p.topk, p.H,
-                         p.apply_router_weight_on_input ? 0 : 1, static_cast<bf16_t*>(y), s);
+                         (p.apply_router_weight_on_input || unweighted) ? 0 : 1,
+                         static_cast<bf16_t*>(y), s);
 }
 
 }  // namespace
@@ -293,7 +314,7 @@ moe_status_t moe_quant_fp8_groups(const void* x, int64_t rows, int32_t cols, voi
 
 size_t moe_workspace_bytes(const moe_problem_t* p) {
     if (check_problem(p) != MOE_OK || p->M == 0) return 0;
-    return static_cast<size_t>(layout(*p).total);
+    return static_cast<size_t>(layout(*p, routed_rows(*p)).total);
 }
 
 }  // extern "C"
@@ -301,16 +322,19 @@ size_t moe_workspace_bytes(const moe_problem_t* p) {
 namespace {
 
 // fused_experts and fused_experts_ep: emap is null (ids are local) or holds
-// p->num_global_experts entries
+// p->num_global_experts entries. unweighted (the batched form): every slot enters
+// the sum with weight 1 and topk_weights is not read.
 moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* x, const void* w13,
                        const float* w13_scale, const void* w2, const float* w2_scale,
                        const int32_t* topk_ids, const float* topk_weights, void* y,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       bool unweighted = false) {
     if (p->M == 0) return MOE_OK;
     const bool fp8 = p->wdtype == MOE_W_FP8_E4M3_BLOCK128;
-    if (!x || !w13 || !w2 || !topk_ids || !topk_weights || !y) return MOE_E_INVALID;
+    if (!x || !w13 || !w2 || !topk_ids || !y || (!topk_weights && !unweighted)) return MOE_E_INVALID;
     if (fp8 && (!w13_scale || !w2_scale)) return MOE_E_INVALID;
-    const Layout L = layout(*p);
+    const Rows rows = routed_rows(*p);
+    const Layout L = layout(*p, rows);
     if (!workspace || workspace_bytes < static_cast<size_t>(L.total)) return MOE_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return MOE_E_INVALID;
 
@@ -338,25 +362,47 @@ moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* 
                        sorted, expert_ids, npp, inv_perm, s);
     if (err != hipSuccess) return MOE_E_HIP;
     if (fp8) {
-        err = permute_stage(*p, reinterpret_cast<const float*>(ws + L.xs), sorted, npp,
+        err = permute_stage(*p, rows, reinterpret_cast<const float*>(ws + L.xs), sorted, npp,
                             reinterpret_cast<float*>(ws + L.xst), s);
         if (err != hipSuccess) return MOE_E_HIP;
     }
     float* zs = fp8 ? reinterpret_cast<float*>(ws + L.zs) : nullptr;
     if (act_fused(*p)) {
-        err = gemm_act_stage(*p, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp,
+        err = gemm_act_stage(*p, rows, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp,
                              topk_weights, z, zs, s);
         if (err != hipSuccess) return MOE_E_HIP;
     } else {
-        err = gemm_stage(*p, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, nullptr, s);
+        err = gemm_stage(*p, rows, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, nullptr, s);
         if (err != hipSuccess) return MOE_E_HIP;
-        err = act_stage(*p, ho, sorted, topk_weights, npp, z, zs, s);
+        err = act_stage(*p, rows, ho, sorted, topk_weights, npp, z, zs, s);
         if (err != hipSuccess) return MOE_E_HIP;
     }
-    err = gemm_stage(*p, 2, z, reinterpret_cast<const float*>(ws + L.zs), w2, w2_scale, sorted,
+    err = gemm_stage(*p, rows, 2, z, reinterpret_cast<const float*>(ws + L.zs), w2, w2_scale, sorted,
                      expert_ids, npp, ho, L.split >= 0 ? ws + L.split : nullptr, s);
     if (err != hipSuccess) return MOE_E_HIP;
-    return hip_status(reduce_stage(*p, ho, inv_perm, topk_weights, y, s));
+    return hip_status(reduce_stage(*p, ho, inv_perm, topk_weights, y, s, unweighted));
+}
+
+// The batched form as a routed top-1 problem: batch row e * max_M + i is item r
+// of its own token, routed to expert e if i < expert_num_tokens[e], else to no
+// expert (skipped by align, so its output row reduces to 0).
+moe_problem_t batched_as_routed(const moe_problem_t& p) {
+    moe_problem_t q = p;
+    q.M = static_cast<int64_t>(p.E) * p.M;
+    q.topk = 1;
+    return q;
+}
+
+int64_t batched_ids_bytes(const moe_problem_t& p) { return up(static_cast<int64_t>(p.E) * p.M * 4); }
+
+moe_status_t check_batched(const moe_problem_t* p) {
+    if (!p) return MOE_E_INVALID;
+    if (p->topk != 1 || p->apply_router_weight_on_input || p->num_global_experts != 0)
+        return MOE_E_INVALID;  // one expert per row, unweighted, local experts
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    const moe_problem_t q = batched_as_routed(*p);
+    return check_problem(&q);
 }
 
 }  // namespace
@@ -386,6 +432,32 @@ moe_status_t fused_experts_ep(const moe_problem_t* p, const int32_t* expert_map,
                      workspace, workspace_bytes, stream);
 }
 
+size_t moe_batched_workspace_bytes(const moe_problem_t* p) {
+    if (check_batched(p) != MOE_OK || p->M == 0) return 0;
+    const moe_problem_t q = batched_as_routed(*p);
+    return static_cast<size_t>(batched_ids_bytes(*p) + layout(q, routed_rows(q)).total);
+}
+
+moe_status_t moe_batched_experts(const moe_problem_t* p, const void* a, const int32_t* expert_num_tokens,
+                                 const void* w13, const float* w13_scale, const void* w2,
+                                 const float* w2_scale, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    const moe_status_t st = check_batched(p);
+    if (st != MOE_OK) return st;
+    if (p->M == 0) return MOE_OK;
+    if (!a || !expert_num_tokens || !out) return MOE_E_INVALID;
+    if (!workspace || workspace_bytes < moe_batched_workspace_bytes(p)) return MOE_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return MOE_E_INVALID;
+    const moe_problem_t q = batched_as_routed(*p);
+    int32_t* ids = static_cast<int32_t*>(workspace);
+    const hipError_t err = launch_batched_ids(expert_num_tokens, p->E, p->M, ids,
+                                              static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return MOE_E_HIP;
+    const int64_t off = batched_ids_bytes(*p);
+    return run_fused(&q, nullptr, a, w13, w13_scale, w2, w2_scale, ids, nullptr, out,
+                     static_cast<uint8_t*>(workspace) + off, workspace_bytes - off, stream, true);
+}
+
 size_t moe_expert_gemm_workspace_bytes(const moe_problem_t* p) {
     if (check_problem(p) != MOE_OK) return 0;
     return static_cast<size_t>(split_bytes(*p));
@@ -405,7 +477,7 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, int32_t which, const void* 
     if (which == 1 && !sorted_token_ids) return MOE_E_INVALID;
     if (fp8 && (!a_scale || !w_scale)) return MOE_E_INVALID;
     if (workspace != nullptr && workspace_bytes < static_cast<size_t>(split_bytes(*p))) return MOE_E_WORKSPACE;
-    return hip_status(gemm_stage(*p, which, a, a_scale, w, w_scale, sorted_token_ids, expert_ids,
+    return hip_status(gemm_stage(*p, routed_rows(*p), which, a, a_scale, w, w_scale, sorted_token_ids, expert_ids,
                                  num_tokens_post_padded, c, workspace, static_cast<hipStream_t>(stream)));
 }
 
@@ -426,7 +498,7 @@ moe_status_t moe_expert_gemm_act(const moe_problem_t* p, const void* x, const fl
     if (!x || !w13 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !topk_weights || !z)
         return MOE_E_INVALID;
     if (fp8 && (!x_scale || !w13_scale || !z_scale)) return MOE_E_INVALID;
-    return hip_status(gemm_act_stage(*p, x, x_scale, w13, w13_scale, sorted_token_ids, expert_ids,
+    return hip_status(gemm_act_stage(*p, routed_rows(*p), x, x_scale, w13, w13_scale, sorted_token_ids, expert_ids,
                                      num_tokens_post_padded, topk_weights, z, z_scale,
                                      static_cast<hipStream_t>(stream)));
 }
@@ -441,7 +513,7 @@ moe_status_t moe_silu_and_mul(const moe_problem_t* p, const void* h,
     if (!h || !sorted_token_ids || !topk_weights || !num_tokens_post_padded || !z)
         return MOE_E_INVALID;
     if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && !z_scale) return MOE_E_INVALID;
-    return hip_status(act_stage(*p, h, sorted_token_ids, topk_weights, num_tokens_post_padded, z,
+    return hip_status(act_stage(*p, routed_rows(*p), h, sorted_token_ids, topk_weights, num_tokens_post_padded, z,
                                 z_scale, static_cast<hipStream_t>(stream)));
 }
 
@@ -452,7 +524,7 @@ moe_status_t moe_permute_scales(const moe_problem_t* p, const float* scale,
     if (st != MOE_OK) return st;
     if (p->M == 0) return MOE_OK;
     if (!scale || !sorted_token_ids || !num_tokens_post_padded || !out) return MOE_E_INVALID;
-    return hip_status(permute_stage(*p, scale, sorted_token_ids, num_tokens_post_padded, out,
+    return hip_status(permute_stage(*p, routed_rows(*p), scale, sorted_token_ids, num_tokens_post_padded, out,
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -52,6 +52,10 @@ WORKLOADS = {
                        bias_std=0.0),
     "fp8_block_m4096": dict(M=4096, H=7168, I=2048, E=256, topk=8, wdtype="fp8",
                             block_m=128, bias_std=0.0),
+    # the decode routing presented in the batched-experts form: one batch of up to
+    # M rows per expert (a token sends at most one item to an expert)
+    "decode_batched_m32": dict(M=32, H=2048, I=768, E=128, topk=8, wdtype="bf16", block_m=16,
+                               bias_std=0.0, batched=True),
     # one rank of an 8-way expert-parallel split of the skewed workload: the rank
     # with the most routed items (13863 of 65536, 20 experts touched) when the
     # inputs are drawn on the GPU (torch's CPU and GPU generators differ), which
@@ -79,6 +83,7 @@ class Problem:
     apply_router_weight_on_input: bool = False
     ep_size: int = 1              # expert-parallel ranks; E counts the global experts
     ep_rank: int = 0
+    batched: bool = False         # the expert layer takes the batched-experts form
 
     @property
     def local_experts(self) -> range:

@@ -166,3 +166,24 @@ def test_expert_parallel_validation():
     assert A(d, 4, 2, 256, d, 300, 16, d, d, d, d, None) == moe.MOE_E_UNSUPPORTED
     assert A(d, 4, 2, 256, d, 4, 24, d, d, d, d, None) == moe.MOE_E_UNSUPPORTED
     assert A(None, 4, 2, 256, d, 4, 16, d, d, d, d, None) == moe.MOE_E_INVALID
+
+
+def test_batched_validation():
+    L = moe.lib()
+    d = ctypes.c_void_p(1 << 20)
+    p = P(M=32, E=8, topk=1)
+    need = moe.moe_batched_workspace_bytes(p)
+    assert need > 0
+    for bad in (P(M=32, E=8, topk=2), P(M=32, E=8, topk=1, on_input=True),
+                P(M=32, E=8, topk=1, num_global_experts=16)):
+        assert moe.moe_batched_workspace_bytes(bad) == 0
+        assert L.moe_batched_experts(ctypes.byref(bad), d, d, d, None, d, None, d, d, need, None) \
+            == moe.MOE_E_INVALID
+    assert L.moe_batched_experts(ctypes.byref(p), d, None, d, None, d, None, d, d, need, None) \
+        == moe.MOE_E_INVALID
+    assert L.moe_batched_experts(ctypes.byref(p), d, d, d, None, d, None, d, d, need - 1, None) \
+        == moe.MOE_E_WORKSPACE
+    assert L.moe_batched_experts(ctypes.byref(P(M=32, E=8, topk=1, block_m=48)), d, d, d, None, d, None,
+                                 d, d, need, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_batched_experts(ctypes.byref(P(M=0, E=8, topk=1)), None, None, None, None, None, None,
+                                 None, None, 0, None) == moe.MOE_OK
