@@ -50,6 +50,8 @@ def lib():
             "oracle_f32_to_e4m3_n": [_P, _I64, _P],
             "oracle_quant_groups_fp8": [_P, _I64, _P, _P],
             "oracle_topk": [_P, _I64, _I32, _I32, _I32, _P, _P],
+            "oracle_topk_grouped": [_P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                                    ctypes.c_float, _P, _P],
             "oracle_align_capacity": [_I64, _I32, _I32, _I32],
             "oracle_align": [_P, _I64, _I32, _I32, _I32, _I64, _P, _I32, _P, _P, _P, _P],
             "oracle_gemm1_bf16": [_P, _P, _I32, _I32, _P],
@@ -143,6 +145,24 @@ def topk(logits: np.ndarray, k: int, renormalize: bool = True):
     rc = lib().oracle_topk(_p(logits), M, E, k, int(renormalize), _p(ids), _p(w))
     if rc:
         raise ValueError("oracle_topk: invalid arguments")
+    return ids, w
+
+
+def topk_grouped(logits: np.ndarray, k: int, scoring: str = "softmax", renormalize: bool = True,
+                 num_expert_group: int = 1, topk_group: int = 1, bias: np.ndarray | None = None,
+                 routed_scaling_factor: float = 1.0):
+    """Grouped / sigmoid router -> (ids int32 [M, k], weights fp32 [M, k])."""
+    logits = _c(logits, np.float32)
+    M, E = logits.shape
+    ids = np.empty((M, k), np.int32)
+    w = np.empty((M, k), np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    rc = lib().oracle_topk_grouped(_p(logits), M, E, k, {"softmax": 0, "sigmoid": 1}[scoring],
+                                   int(renormalize), num_expert_group, topk_group,
+                                   _p(b) if b is not None else None, float(routed_scaling_factor),
+                                   _p(ids), _p(w))
+    if rc:
+        raise ValueError("oracle_topk_grouped: invalid arguments")
     return ids, w
 
 

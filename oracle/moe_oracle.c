@@ -201,6 +201,77 @@ int oracle_topk(const float *logits, int64_t M, int E, int k, int renormalize,
     return 0;
 }
 
+/* Grouped / sigmoid router ([MK] section 3, fused_topk scoring_func softmax or
+ * sigmoid; [MK] 11.x apply_monolithic: num_expert_group, topk_group,
+ * e_score_correction_bias, routed_scaling_factor). The pages name the knobs;
+ * the steps follow their plain meaning:
+ *   1. score u_e: softmax over the E logits, or sigmoid(s_e);
+ *   2. selection key: the logit itself (both scores increase with it), or with
+ *      a correction bias (sigmoid only) the fp32 sum u_e + b_e, u_e being the
+ *      sigmoid evaluated in double and rounded to fp32;
+ *   3. groups of E / G consecutive experts; a group's score is its largest key,
+ *      or with a bias the fp32 sum of its two largest keys; the topk_group
+ *      best groups are kept (ties to the lower group index);
+ *   4. the k largest keys among the kept groups' experts, in descending order
+ *      (ties to the lower expert index);
+ *   5. weights are the unbiased scores u (softmax over all E, or sigmoid),
+ *      divided by their sum over the k chosen when `renormalize` is set, then
+ *      multiplied by routed_scaling_factor.
+ * G = 1 (or topk_group = G) is plain top-k. */
+static float sigmoid_f32(float s) { return (float)(1.0 / (1.0 + exp(-(double)s))); }
+
+int oracle_topk_grouped(const float *logits, int64_t M, int E, int k, int scoring,
+                        int renormalize, int G, int topk_group, const float *bias,
+                        float scale, int32_t *ids, float *weights)
+{
+    if (k < 1 || E > 1024 || k > 64 || G < 1 || E % G || topk_group < 1 || topk_group > G) return 1;
+    int gs = E / G;
+    if (k > topk_group * gs || (bias && (scoring != 1 || gs < 2))) return 1;
+    for (int64_t t = 0; t < M; ++t) {
+        const float *s = logits + t * E;
+        float key[1024];
+        for (int e = 0; e < E; ++e) key[e] = bias ? sigmoid_f32(s[e]) + bias[e] : s[e];
+        char allowed[1024];
+        memset(allowed, 0, sizeof allowed);
+        char gtaken[1024];
+        memset(gtaken, 0, sizeof gtaken);
+        for (int r = 0; r < topk_group; ++r) {
+            int bg = -1;
+            float bscore = 0.0f;
+            for (int g = 0; g < G; ++g) {
+                if (gtaken[g]) continue;
+                float m1 = -INFINITY, m2 = -INFINITY;   /* two largest keys of group g */
+                for (int e = g * gs; e < (g + 1) * gs; ++e) {
+                    if (key[e] > m1) { m2 = m1; m1 = key[e]; }
+                    else if (key[e] > m2) m2 = key[e];
+                }
+                float score = bias ? m1 + m2 : m1;
+                if (bg < 0 || score > bscore) { bg = g; bscore = score; }
+            }
+            gtaken[bg] = 1;
+            for (int e = bg * gs; e < (bg + 1) * gs; ++e) allowed[e] = 1;
+        }
+        double smax = -INFINITY;
+        for (int e = 0; e < E; ++e)
+            if (s[e] > smax) smax = s[e];
+        double denom = 0.0;
+        for (int e = 0; e < E; ++e) denom += exp((double)s[e] - smax);
+        double u[64], usum = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (allowed[e] && (best < 0 || key[e] > key[best])) best = e;
+            allowed[best] = 0;
+            ids[t * k + j] = best;
+            u[j] = scoring == 1 ? (double)sigmoid_f32(s[best]) : exp((double)s[best] - smax) / denom;
+            usum += u[j];
+        }
+        for (int j = 0; j < k; ++j)
+            weights[t * k + j] = (float)((renormalize ? u[j] / usum : u[j]) * (double)scale);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Align ([FG] "moe_align_block_size"; [DG] 2.6.1, 2.6.2).                     */
 /* ------------------------------------------------------------------------ */
