@@ -133,9 +133,18 @@ class Step:
             self.w13 = moe.moe_pack_weights(rows, 1, d.w13)
             self.w2 = moe.moe_pack_weights(rows, 2, d.w2)
 
+    def route(self):
+        """The workload's router: softmax top-k, or the grouped / sigmoid router."""
+        m, d, p = self.moe, self.d, self.p
+        if p.scoring == "softmax" and p.n_group == 1 and d.score_bias is None and p.routed_scale == 1.0:
+            m.moe_topk(d.logits, p.topk, out=(self.ids, self.w))
+        else:
+            m.moe_topk_grouped(d.logits, p.topk, p.scoring, True, p.n_group, p.topk_group, d.score_bias,
+                               p.routed_scale, out=(self.ids, self.w))
+
     def fused(self):
         m, d = self.moe, self.d
-        m.moe_topk(d.logits, self.p.topk, out=(self.ids, self.w))
+        self.route()
         m.fused_experts(d.x, self.w13, self.w2, self.ids, self.w, self.p.block_m,
                         d.w13s, d.w2s, self.p.apply_router_weight_on_input, out=self.y,
                         workspace=self.ws, weight_layout=self.wl, expert_map=self.emap)
@@ -148,7 +157,7 @@ class Step:
         lib = m.lib()
         s = m._stream()
         ev[0].record()
-        m.moe_topk(d.logits, self.p.topk, out=(self.ids, self.w))
+        self.route()
         ev[1].record()
         a1, a1s = d.x, None
         if self.fp8:
@@ -199,7 +208,7 @@ class BatchedStep(Step):
             raise SystemExit("the batched workload is bf16 on all experts")
         m, dev = self.moe, d.x.device
         E, M, k, H, I, B = p.E, p.M, p.topk, p.H, p.I, p.block_m
-        m.moe_topk(d.logits, k, out=(self.ids, self.w))
+        self.route()
         flat = self.ids.reshape(-1).long()
         order = torch.argsort(flat, stable=True)            # items by expert, tokens ascending
         counts = torch.bincount(flat, minlength=E)

@@ -67,6 +67,11 @@ typedef enum {
  *     moe_pack_weights; results are bit-identical to MOE_LAYOUT_ROWS.
  */
 typedef enum {
+    MOE_SCORING_SOFTMAX = 0,
+    MOE_SCORING_SIGMOID = 1
+} moe_scoring_t;
+
+typedef enum {
     MOE_LAYOUT_ROWS = 0,
     MOE_LAYOUT_TILED = 1
 } moe_wlayout_t;
@@ -103,6 +108,35 @@ typedef struct {
 moe_status_t moe_topk(const float *logits, int64_t M, int32_t E, int32_t topk,
                       int32_t renormalize, int32_t *topk_ids, float *topk_weights,
                       void *stream);
+
+/*
+ * Grouped / sigmoid router ("vLLM modular_kernel.py notes", section 3:
+ * fused_topk with scoring_func "softmax" or "sigmoid"; the grouped routing
+ * arguments of apply_monolithic: num_expert_group, topk_group,
+ * e_score_correction_bias, routed_scaling_factor). Per token:
+ *   score u_e   softmax over the E logits, or sigmoid(s_e)
+ *   key         the logit s_e; with a correction bias (sigmoid only),
+ *               fp32( sigmoid(s_e) evaluated in double ) + bias[e] in fp32
+ *   groups      num_expert_group groups of E / G consecutive experts; a group
+ *               scores its largest key, or with a bias the sum of its two
+ *               largest keys; the topk_group best groups are kept (lower group
+ *               index on ties)
+ *   selection   the topk largest keys among the kept groups' experts, slots in
+ *               descending key order (lower expert index on ties)
+ *   weights     u of the chosen (the bias never enters a weight), divided by
+ *               their sum when `renormalize`, times routed_scaling_factor
+ *   logits [M, E] fp32; e_score_correction_bias [E] fp32 or NULL;
+ *   topk_ids [M, topk] int32 out; topk_weights [M, topk] fp32 out.
+ * num_expert_group = topk_group (e.g. 1, 1) is plain top-k over all experts.
+ * MOE_E_INVALID: G or topk_group outside [1, E] with E % G == 0 and
+ * topk_group <= G, topk above topk_group * E / G or 32, a bias with softmax
+ * scoring or with groups of one expert; MOE_E_UNSUPPORTED: E > 256 or G > 64.
+ */
+moe_status_t moe_topk_grouped(const float *logits, int64_t M, int32_t E, int32_t topk,
+                              int32_t scoring, int32_t renormalize, int32_t num_expert_group,
+                              int32_t topk_group, const float *e_score_correction_bias,
+                              float routed_scaling_factor, int32_t *topk_ids, float *topk_weights,
+                              void *stream);
 
 /*
  * Host-only, pure: the number of rows the expert-sorted layout may need,

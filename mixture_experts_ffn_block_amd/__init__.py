@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
+MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
 
-EXPORTS = ("moe_topk", "moe_align_capacity", "moe_align_block_size", "moe_align_block_size_ep",
+EXPORTS = ("moe_topk", "moe_topk_grouped", "moe_align_capacity", "moe_align_block_size", "moe_align_block_size_ep",
            "moe_quant_fp8_groups", "moe_workspace_bytes", "fused_experts", "fused_experts_ep",
            "moe_expert_gemm_workspace_bytes",
            "moe_expert_gemm", "moe_silu_and_mul",
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         L.moe_topk.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P]
+        L.moe_topk_grouped.argtypes = [_P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                                       ctypes.c_float, _P, _P, _P]
         L.moe_align_capacity.argtypes = [_I64, _I32, _I32, _I32]
         L.moe_align_capacity.restype = _I64
         L.moe_align_block_size.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P]
@@ -81,7 +84,7 @@ def lib() -> ctypes.CDLL:
         L.moe_batched_experts.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_status_string.argtypes = [_I32]
         L.moe_status_string.restype = ctypes.c_char_p
-        for name in ("moe_topk", "moe_align_block_size", "moe_align_block_size_ep",
+        for name in ("moe_topk", "moe_topk_grouped", "moe_align_block_size", "moe_align_block_size_ep",
                      "moe_quant_fp8_groups", "fused_experts", "fused_experts_ep",
                      "moe_expert_gemm", "moe_silu_and_mul", "moe_permute_scales",
                      "moe_expert_gemm_act", "moe_unpermute_reduce", "moe_pack_weights",
@@ -147,6 +150,28 @@ def moe_topk(logits: torch.Tensor, topk: int, renormalize: bool = True, stream=N
         ids, w = out
     _check(lib().moe_topk(_ptr(logits), M, E, topk, int(renormalize), _ptr(ids), _ptr(w),
                           _stream(stream)), "moe_topk")
+    return ids, w
+
+
+def moe_topk_grouped(logits: torch.Tensor, topk: int, scoring: str = "softmax", renormalize: bool = True,
+                     num_expert_group: int = 1, topk_group: int = 1,
+                     e_score_correction_bias: torch.Tensor | None = None,
+                     routed_scaling_factor: float = 1.0, stream=None,
+                     out: tuple[torch.Tensor, torch.Tensor] | None = None):
+    """Grouped / sigmoid router -> (topk_ids int32 [M, k], topk_weights fp32 [M, k])."""
+    _need(logits, torch.float32, "logits")
+    if e_score_correction_bias is not None:
+        _need(e_score_correction_bias, torch.float32, "e_score_correction_bias")
+    M, E = logits.shape
+    if out is None:
+        ids = torch.empty((M, topk), dtype=torch.int32, device=logits.device)
+        w = torch.empty((M, topk), dtype=torch.float32, device=logits.device)
+    else:
+        ids, w = out
+    sc = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}[scoring]
+    _check(lib().moe_topk_grouped(_ptr(logits), M, E, topk, sc, int(renormalize), num_expert_group,
+                                  topk_group, _ptr(e_score_correction_bias), float(routed_scaling_factor),
+                                  _ptr(ids), _ptr(w), _stream(stream)), "moe_topk_grouped")
     return ids, w
 
 

@@ -267,6 +267,25 @@ moe_status_t moe_topk(const float* logits, int64_t M, int32_t E, int32_t topk, i
                                           static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_topk_grouped(const float* logits, int64_t M, int32_t E, int32_t topk, int32_t scoring,
+                              int32_t renormalize, int32_t num_expert_group, int32_t topk_group,
+                              const float* e_score_correction_bias, float routed_scaling_factor,
+                              int32_t* topk_ids, float* topk_weights, void* stream) {
+    if (M < 0 || E <= 0 || topk <= 0 || topk > kMaxTopk) return MOE_E_INVALID;
+    if (scoring != MOE_SCORING_SOFTMAX && scoring != MOE_SCORING_SIGMOID) return MOE_E_INVALID;
+    const int G = num_expert_group, TG = topk_group;
+    if (G < 1 || TG < 1 || TG > G || E % G) return MOE_E_INVALID;
+    if (topk > TG * (E / G)) return MOE_E_INVALID;  // not enough experts in the kept groups
+    if (e_score_correction_bias && (scoring != MOE_SCORING_SIGMOID || E / G < 2)) return MOE_E_INVALID;
+    if (E > kMaxE || G > 64) return MOE_E_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_E_INVALID;
+    return hip_status(launch_topk_grouped(logits, M, E, topk, scoring == MOE_SCORING_SIGMOID ? 1 : 0,
+                                          renormalize, G, TG, e_score_correction_bias,
+                                          routed_scaling_factor, topk_ids, topk_weights,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_align_block_size(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E,
                                   int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
                                   int32_t* num_tokens_post_padded, int32_t* inv_perm,

@@ -57,6 +57,9 @@ hipError_t launch_topk_softmax(const float* logits, int64_t M, int E, int k, int
 // top-1 ids of the batched form: row e * max_M + i goes to expert e if i < counts[e]
 hipError_t launch_batched_ids(const int32_t* counts, int E, int64_t max_M, int32_t* ids, hipStream_t stream);
 // emap: null, or E_global entries mapping global expert ids to [0, E) or -1 (not local)
+hipError_t launch_topk_grouped(const float* logits, int64_t M, int E, int k, int sigmoid,
+                               int renormalize, int G, int TG, const float* bias, float scale,
+                               int32_t* ids, float* weights, hipStream_t stream);
 hipError_t launch_align(const int32_t* ids, int64_t R, int E, int B, int64_t cap,
                         const int32_t* emap, int E_global, int32_t* sorted, int32_t* expert_ids,
                         int32_t* npp, int32_t* inv_perm, hipStream_t stream);

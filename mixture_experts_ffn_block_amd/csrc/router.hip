@@ -80,7 +80,160 @@ __global__ __launch_bounds__(kTokensPerBlock * MOE_WAVE) void topk_softmax_kerne
     }
 }
 
+// ------------------------------------------------------------ grouped router --
+// "vLLM modular_kernel.py notes", section 3 (fused_topk, scoring softmax or
+// sigmoid) and the grouped routing arguments of apply_monolithic
+// (num_expert_group, topk_group, e_score_correction_bias,
+// routed_scaling_factor). Keys: the logits (both scores increase with them),
+// or with a correction bias the fp32 sum sigmoid + bias, the sigmoid evaluated
+// in double and rounded to fp32 so that the kept experts do not depend on an
+// exp approximation. A group of E / G consecutive experts scores its largest
+// key, or with a bias the sum of its two largest; the topk_group best groups
+// (lower index on ties) are kept, then the k largest keys among their experts.
+// Weights are the unbiased scores, renormalised over the k chosen if asked,
+// times routed_scaling_factor.
+//
+// Same wave layout as above; the score of group g ends in lane g (G <= 64),
+// found by a butterfly that merges (largest, second largest) pairs.
+__device__ __forceinline__ float sigmoid_f32(float s) {
+    return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(s))));
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kTokensPerBlock * MOE_WAVE) void topk_grouped_kernel(
+    const float* __restrict__ logits, int64_t M, int E, int k, int sigmoid, int renormalize, int G,
+    int TG, const float* __restrict__ bias, float scale, int32_t* __restrict__ ids,
+    float* __restrict__ weights) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + (threadIdx.x >> 6);
+    if (t >= M) return;
+    const float* row = logits + t * E;
+    const int gs = E / G;
+
+    float v[EPL], key[EPL];
+    uint32_t alive = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? row[e] : -INFINITY;
+        key[i] = v[i];
+        if (e < E) {
+            alive |= 1u << i;
+            if (bias) key[i] = sigmoid_f32(v[i]) + bias[e];
+        }
+    }
+
+    if (TG < G) {
+        float gscore = -INFINITY;  // lane g: score of group g
+        for (int g = 0; g < G; ++g) {
+            float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (((alive >> i) & 1u) && (lane + 64 * i) / gs == g) {
+                    if (key[i] > m1) { m2 = m1; m1 = key[i]; }
+                    else if (key[i] > m2) m2 = key[i];
+                }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float o1 = __shfl_xor(m1, o, 64), o2 = __shfl_xor(m2, o, 64);
+                const float hi = fmaxf(m1, o1), lo = fminf(m1, o1);
+                m2 = fmaxf(lo, fmaxf(m2, o2));
+                m1 = hi;
+            }
+            if (lane == g) gscore = bias ? m1 + m2 : m1;
+        }
+        uint64_t kept = 0;
+        for (int r = 0; r < TG; ++r) {
+            float bv = lane < G && !((kept >> lane) & 1ull) ? gscore : -INFINITY;
+            int bg = lane < G && !((kept >> lane) & 1ull) ? lane : 0x7fffffff;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int og = __shfl_xor(bg, o, 64);
+                if (better(ov, og, bv, bg)) { bv = ov; bg = og; }
+            }
+            kept |= 1ull << bg;
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;  // e < E: its group index is below G <= 64
+            if (e < E && !((kept >> (e / gs)) & 1ull)) alive &= ~(1u << i);
+        }
+    }
+
+    int my_id = 0;
+    float my_logit = 0.0f, top = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if ((alive >> i) & 1u) {
+                const int e = lane + 64 * i;
+                if (better(key[i], e, bv, be)) { bv = key[i]; be = e; }
+            }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oe = __shfl_xor(be, o, 64);
+            if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
+        }
+        if ((be & 63) == lane) alive &= ~(1u << (be >> 6));
+        // the chosen expert's logit, from the lane that holds it
+        float lg = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (lane + 64 * i == be) lg = v[i];
+        lg = __shfl(lg, be & 63, 64);
+        if (j == 0) top = lg;
+        if (lane == j) { my_id = be; my_logit = lg; }
+    }
+
+    float u = 0.0f;
+    if (sigmoid) {
+        u = lane < k ? sigmoid_f32(my_logit) : 0.0f;
+        if (renormalize) u /= wave_sum(u);
+    } else if (renormalize) {
+        // the chosen have the largest logits among the kept groups: top is their maximum
+        u = lane < k ? expf(my_logit - top) : 0.0f;
+        u /= wave_sum(u);
+    } else {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) mx = fmaxf(mx, v[i]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (lane + 64 * i < E) sum += expf(v[i] - mx);
+        u = lane < k ? expf(my_logit - mx) : 0.0f;
+        u /= wave_sum(sum);
+    }
+    if (lane < k) {
+        ids[t * k + lane] = my_id;
+        weights[t * k + lane] = u * scale;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_topk_grouped(const float* logits, int64_t M, int E, int k, int sigmoid,
+                               int renormalize, int G, int TG, const float* bias, float scale,
+                               int32_t* ids, float* weights, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(M, kTokensPerBlock)));
+    const dim3 block(kTokensPerBlock * MOE_WAVE);
+    if (E <= 64)
+        hipLaunchKernelGGL(topk_grouped_kernel<1>, grid, block, 0, stream, logits, M, E, k, sigmoid,
+                           renormalize, G, TG, bias, scale, ids, weights);
+    else if (E <= 128)
+        hipLaunchKernelGGL(topk_grouped_kernel<2>, grid, block, 0, stream, logits, M, E, k, sigmoid,
+                           renormalize, G, TG, bias, scale, ids, weights);
+    else
+        hipLaunchKernelGGL(topk_grouped_kernel<4>, grid, block, 0, stream, logits, M, E, k, sigmoid,
+                           renormalize, G, TG, bias, scale, ids, weights);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk_softmax(const float* logits, int64_t M, int E, int k, int renormalize,
                                int32_t* ids, float* weights, hipStream_t stream) {

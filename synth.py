@@ -18,6 +18,8 @@ generation is chunked):
 * ``x``       [M, H]  ~ N(0, 1) in fp32, rounded to bf16 (round-to-nearest-even).
 * ``logits``  [M, E]  ~ N(0, 1) fp32, plus a per-expert bias ~ N(0, bias_std)
   when the workload asks for skewed routing.
+* ``score_bias`` [E] ~ N(0, score_bias_std) fp32: the router's correction bias
+  (grouped sigmoid routing), when the workload has one.
 * ``w13``     [E, 2I, H] ~ N(0, 1/sqrt(H)) -> bf16; rows [0, I) are the gate
   projection, rows [I, 2I) the up projection.
 * ``w2``      [E, H, I]  ~ N(0, 1/sqrt(I)) -> bf16.
@@ -52,6 +54,11 @@ WORKLOADS = {
                        bias_std=0.0),
     "fp8_block_m4096": dict(M=4096, H=7168, I=2048, E=256, topk=8, wdtype="fp8",
                             block_m=128, bias_std=0.0),
+    # DeepSeek-V3-style routing on the DSV3 shape: sigmoid scores, 8 groups of 32
+    # experts of which 4 are kept, a correction bias, weights scaled by 2.5
+    "dsv3_grouped_prefill_m8192": dict(M=8192, H=7168, I=2048, E=256, topk=8, wdtype="bf16",
+                                       block_m=128, scoring="sigmoid", n_group=8, topk_group=4,
+                                       score_bias_std=0.05, routed_scale=2.5),
     # the decode routing presented in the batched-experts form: one batch of up to
     # M rows per expert (a token sends at most one item to an expert)
     "decode_batched_m32": dict(M=32, H=2048, I=768, E=128, topk=8, wdtype="bf16", block_m=16,
@@ -64,7 +71,7 @@ WORKLOADS = {
                                          block_m=128, bias_std=1.5, ep_size=8, ep_rank=2),
 }
 
-_T_X, _T_LOGITS, _T_BIAS, _T_W13, _T_W2 = 1, 2, 3, 4, 5
+_T_X, _T_LOGITS, _T_BIAS, _T_W13, _T_W2, _T_SCORE_BIAS = 1, 2, 3, 4, 5, 6
 
 
 @dataclasses.dataclass
@@ -84,6 +91,13 @@ class Problem:
     ep_size: int = 1              # expert-parallel ranks; E counts the global experts
     ep_rank: int = 0
     batched: bool = False         # the expert layer takes the batched-experts form
+    # router: scoring "softmax" or "sigmoid", groups (1 = none), kept groups, the
+    # correction bias's standard deviation (0 = none), the routed scaling factor
+    scoring: str = "softmax"
+    n_group: int = 1
+    topk_group: int = 1
+    score_bias_std: float = 0.0
+    routed_scale: float = 1.0
 
     @property
     def local_experts(self) -> range:
@@ -142,6 +156,7 @@ class Inputs:
     w2q: torch.Tensor | None = None   # [E, H, I] float8_e4m3fn
     w2s: torch.Tensor | None = None   # [E, H/128, I/128] fp32
     expert_map: torch.Tensor | None = None  # [E] int32 on expert-parallel ranks, else None
+    score_bias: torch.Tensor | None = None  # [E] fp32 router correction bias, else None
 
 
 def make_inputs(p: Problem, device="cpu") -> Inputs:
@@ -151,6 +166,7 @@ def make_inputs(p: Problem, device="cpu") -> Inputs:
     logits = _randn((M, E), device, p.seed, _T_LOGITS)
     if p.bias_std:
         logits += _randn((E,), device, p.seed, _T_BIAS, std=p.bias_std)[None, :]
+    sbias = _randn((E,), device, p.seed, _T_SCORE_BIAS, std=p.score_bias_std) if p.score_bias_std else None
     held = p.local_experts
     emap = None
     if p.ep_size > 1:
@@ -164,7 +180,7 @@ def make_inputs(p: Problem, device="cpu") -> Inputs:
         for i, e in enumerate(held):
             w13[i] = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H))
             w2[i] = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I))
-        return Inputs(x, logits, w13, w2, expert_map=emap)
+        return Inputs(x, logits, w13, w2, expert_map=emap, score_bias=sbias)
     if p.wdtype == "fp8":
         w13q = torch.empty((EL, 2 * I, H), dtype=torch.float8_e4m3fn, device=device)
         w2q = torch.empty((EL, H, I), dtype=torch.float8_e4m3fn, device=device)
@@ -175,6 +191,6 @@ def make_inputs(p: Problem, device="cpu") -> Inputs:
             w13q[i], w13s[i] = block_quant_fp8(m13)
             m2 = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I)).to(torch.bfloat16)
             w2q[i], w2s[i] = block_quant_fp8(m2)
-        return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s, expert_map=emap)
+        return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s, expert_map=emap, score_bias=sbias)
     raise ValueError(f"unknown weight dtype {p.wdtype!r}")
 

@@ -187,3 +187,21 @@ def test_batched_validation():
                                  d, d, need, None) == moe.MOE_E_UNSUPPORTED
     assert L.moe_batched_experts(ctypes.byref(P(M=0, E=8, topk=1)), None, None, None, None, None, None,
                                  None, None, 0, None) == moe.MOE_OK
+
+
+def test_grouped_router_validation():
+    L = moe.lib()
+    d = ctypes.c_void_p(1 << 20)
+    T = L.moe_topk_grouped
+    S, G = moe.MOE_SCORING_SOFTMAX, moe.MOE_SCORING_SIGMOID
+    assert T(d, 4, 256, 8, 2, 1, 8, 4, None, 1.0, d, d, None) == moe.MOE_E_INVALID   # unknown scoring
+    assert T(d, 4, 256, 8, S, 1, 7, 4, None, 1.0, d, d, None) == moe.MOE_E_INVALID   # 256 % 7
+    assert T(d, 4, 256, 8, S, 1, 8, 9, None, 1.0, d, d, None) == moe.MOE_E_INVALID   # topk_group > G
+    assert T(d, 4, 256, 40, S, 1, 8, 1, None, 1.0, d, d, None) == moe.MOE_E_INVALID  # 40 > 32
+    assert T(d, 4, 64, 9, S, 1, 8, 1, None, 1.0, d, d, None) == moe.MOE_E_INVALID   # 9 > 1 * 8
+    assert T(d, 4, 256, 8, S, 1, 8, 4, d, 1.0, d, d, None) == moe.MOE_E_INVALID     # bias with softmax
+    assert T(d, 4, 64, 8, G, 1, 64, 64, d, 1.0, d, d, None) == moe.MOE_E_INVALID    # groups of one + bias
+    assert T(d, 4, 384, 8, G, 1, 8, 4, d, 1.0, d, d, None) == moe.MOE_E_UNSUPPORTED
+    assert T(d, 4, 256, 8, G, 1, 128, 64, None, 1.0, d, d, None) == moe.MOE_E_UNSUPPORTED  # G > 64
+    assert T(None, 4, 256, 8, G, 1, 8, 4, d, 2.5, d, d, None) == moe.MOE_E_INVALID
+    assert T(None, 0, 256, 8, G, 1, 8, 4, None, 2.5, None, None, None) == moe.MOE_OK

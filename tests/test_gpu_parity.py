@@ -39,6 +39,29 @@ def to_dev(inp: synth.Inputs) -> synth.Inputs:
         inp.x, inp.logits, inp.w13, inp.w2, inp.w13q, inp.w13s, inp.w2q, inp.w2s)])
 
 
+def route_gpu(p: synth.Problem, logits, score_bias):
+    """The workload's router on the GPU: softmax top-k or the grouped / sigmoid router."""
+    if p.scoring == "softmax" and p.n_group == 1 and score_bias is None and p.routed_scale == 1.0:
+        return moe.moe_topk(logits, p.topk)
+    return moe.moe_topk_grouped(logits, p.topk, p.scoring, True, p.n_group, p.topk_group, score_bias,
+                                p.routed_scale)
+
+
+def route_oracle(p: synth.Problem, logits: np.ndarray, score_bias):
+    if p.scoring == "softmax" and p.n_group == 1 and score_bias is None and p.routed_scale == 1.0:
+        return oracle.topk(logits, p.topk)
+    return oracle.topk_grouped(logits, p.topk, p.scoring, True, p.n_group, p.topk_group,
+                               None if score_bias is None else score_bias.cpu().numpy(), p.routed_scale)
+
+
+def router_inputs(p: synth.Problem):
+    """The workload's logits and correction bias, drawn with small H and I (the same draws)."""
+    small = synth.Problem(M=p.M, H=128, I=128, E=p.E, topk=p.topk, bias_std=p.bias_std, seed=p.seed,
+                          score_bias_std=p.score_bias_std)
+    inp = synth.make_inputs(small, "cpu")
+    return inp.logits, inp.score_bias
+
+
 def run_layer(p: synth.Problem, d: synth.Inputs, ids, w, out=None):
     if p.wdtype == "fp8":
         return moe.fused_experts(d.x, d.w13q, d.w2q, ids, w, p.block_m, d.w13s, d.w2s,
@@ -74,12 +97,11 @@ def assert_close(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float, what: str):
 def test_router_bit_exact(name):
     p = synth.Problem.named(name)
     log(f"router {name}")
-    logits = synth.make_inputs(synth.Problem(M=p.M, H=128, I=128, E=p.E, topk=p.topk,
-                                             bias_std=p.bias_std, seed=p.seed), "cpu").logits
-    ids, w = moe.moe_topk(logits.to(DEV), p.topk)
-    ids_ref, w_ref = oracle.topk(logits.numpy(), p.topk)
+    logits, sb = router_inputs(p)
+    ids, w = route_gpu(p, logits.to(DEV), None if sb is None else sb.to(DEV))
+    ids_ref, w_ref = route_oracle(p, logits.numpy(), sb)
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
-    assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6 * max(1.0, p.routed_scale)
 
 
 def test_router_ties_and_unnormalised():
@@ -110,9 +132,8 @@ def check_align(ids_np: np.ndarray, E: int, B: int):
 def test_align_bit_exact_workloads(name):
     p = synth.Problem.named(name)
     log(f"align {name}")
-    logits = synth.make_inputs(synth.Problem(M=p.M, H=128, I=128, E=p.E, topk=p.topk,
-                                             bias_std=p.bias_std, seed=p.seed), "cpu").logits
-    ids, _ = oracle.topk(logits.numpy(), p.topk)
+    logits, sb = router_inputs(p)
+    ids, _ = route_oracle(p, logits.numpy(), sb)
     for B in sorted({p.block_m, 16, 64, 128, 256}):
         check_align(ids, p.E, B)
 
@@ -373,11 +394,11 @@ def sampled_check(name, n_samples=6):
     p = synth.Problem.named(name)
     log(f"full-size {name}: generating inputs on the device")
     d = synth.make_inputs(p, DEV)
-    ids, w = moe.moe_topk(d.logits, p.topk)
+    ids, w = route_gpu(p, d.logits, d.score_bias)
     y = run_layer(p, d, ids, w)
     torch.cuda.synchronize()
     ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
-    ids_ref, _ = oracle.topk(d.logits.cpu().numpy(), p.topk)
+    ids_ref, _ = route_oracle(p, d.logits.cpu().numpy(), d.score_bias)
     assert np.array_equal(ids_np, ids_ref)
     # samples: first, last, and tokens routed to the busiest expert
     counts = np.bincount(ids_np.reshape(-1), minlength=p.E)
@@ -403,6 +424,6 @@ def sampled_check(name, n_samples=6):
 
 
 @pytest.mark.parametrize("name", ["mixtral_prefill_m4096", "dsv3_skewed_prefill_m8192",
-                                  "fp8_block_m4096"])
+                                  "fp8_block_m4096", "dsv3_grouped_prefill_m8192"])
 def test_layer_full_size_sampled(name):
     sampled_check(name)
