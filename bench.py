@@ -17,6 +17,7 @@ Printed JSON line (rank 0):
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -87,7 +88,7 @@ def parse():
 class Step:
     """Device buffers and the two ways of running one step."""
 
-    def __init__(self, p: synth.Problem, d: synth.Inputs, layout: str = "auto"):
+    def __init__(self, p: synth.Problem, d: synth.Inputs, layout: str = "auto", weights=None):
         import mixture_experts_ffn_block_amd as moe
         self.moe, self.p, self.d = moe, p, d
         self.fp8 = p.wdtype == "fp8"
@@ -129,7 +130,9 @@ class Step:
         self.gws = moe.gemm_workspace_for(self.prob, dev)  # split-K tail of the second GEMM
         self.w13 = d.w13q if self.fp8 else d.w13
         self.w2 = d.w2q if self.fp8 else d.w2
-        if self.layout == "tiled":  # weight preparation, once, outside every timed region
+        if weights is not None:  # prepared by another Step of the same workload
+            self.w13, self.w2 = weights
+        elif self.layout == "tiled":  # weight preparation, once, outside every timed region
             self.w13 = moe.moe_pack_weights(rows, 1, d.w13)
             self.w2 = moe.moe_pack_weights(rows, 2, d.w2)
 
@@ -147,7 +150,8 @@ class Step:
         self.route()
         m.fused_experts(d.x, self.w13, self.w2, self.ids, self.w, self.p.block_m,
                         d.w13s, d.w2s, self.p.apply_router_weight_on_input, out=self.y,
-                        workspace=self.ws, weight_layout=self.wl, expert_map=self.emap)
+                        workspace=self.ws, weight_layout=self.wl, expert_map=self.emap,
+                        chunk_tokens=self.p.chunk_tokens)
 
     STAGES = ("router", "quant", "align", "gemm1", "act", "gemm2", "reduce")
 
@@ -387,6 +391,15 @@ def main():
     print(f"# workload {args.workload}: {p}", file=sys.stderr, flush=True)
     d = synth.make_inputs(p, "cuda")
     st = (BatchedStep if p.batched else Step)(p, d, args.weight_layout)
+    # a chunked layer launches its kernels once per chunk: the staged breakdown (and the
+    # roofline of GEMM1 per launch) runs the first chunk
+    chunked = 0 < p.chunk_tokens < p.M
+    if chunked:
+        pc = dataclasses.replace(p, M=p.chunk_tokens, chunk_tokens=0)
+        dc = dataclasses.replace(d, x=d.x[:pc.M], logits=d.logits[:pc.M])
+        sst = Step(pc, dc, args.weight_layout, weights=(st.w13, st.w2))
+    else:
+        pc, sst = p, st
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -421,11 +434,14 @@ def main():
     # stage breakdown: the same kernels stage by stage, HIP events on the same stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
     for _ in range(2):
-        st.staged([torch.cuda.Event(enable_timing=True) for _ in range(8)])
+        sst.staged([torch.cuda.Event(enable_timing=True) for _ in range(8)])
     torch.cuda.synchronize()
     for i in range(args.steps):
-        st.staged(evs[i])
+        sst.staged(evs[i])
     torch.cuda.synchronize()
+    ids_stage = sst.ids.cpu().numpy()
+    alg_stage = algorithmic(pc, int(np.unique(ids_stage[held[ids_stage]]).size), sst.act_fused,
+                            int(held[ids_stage].sum()))
     stage_ms = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
                 for j, name in enumerate(Step.STAGES)}
     staged_total = float(np.mean([e[0].elapsed_time(e[7]) for e in evs]))
@@ -435,13 +451,13 @@ def main():
     tok_s = p.M / (ms * 1e-3)
     dt = "fp8" if p.wdtype == "fp8" else "bf16"
     g1_s = stage_ms["gemm1"] * 1e-3
-    t_mfma = alg["flops_g1"] / (PEAK_TFLOPS[dt] * 1e12)
-    t_hbm = alg["bytes_g1"] / (PEAK_HBM_GBS * 1e9)
+    t_mfma = alg_stage["flops_g1"] / (PEAK_TFLOPS[dt] * 1e12)
+    t_hbm = alg_stage["bytes_g1"] / (PEAK_HBM_GBS * 1e9)
     if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": round(alg["flops_g1"] / g1_s / 1e12, 2),
+        roof = {"bound": "mfma", "achieved": round(alg_stage["flops_g1"] / g1_s / 1e12, 2),
                 "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
     else:
-        roof = {"bound": "hbm", "achieved": round(alg["bytes_g1"] / g1_s / 1e9, 1),
+        roof = {"bound": "hbm", "achieved": round(alg_stage["bytes_g1"] / g1_s / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(args.workload)
@@ -463,7 +479,9 @@ def main():
                        "routed_items_here": items} if p.ep_size > 1 else {}),
                    **({"form": "batched experts [E, M, H] (the timed step is moe_batched_experts; "
                                "router and dispatch precede it)", "batch_rows_max": p.M}
-                      if p.batched else {})},
+                      if p.batched else {}),
+                   **({"chunk_tokens": p.chunk_tokens, "stage_scope": f"first chunk of {pc.M} tokens"}
+                      if chunked else {})},
         "step_roofline_frac": round(t_star / (ms * 1e-3), 4),
         "roofline": roof,
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},

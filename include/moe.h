@@ -91,6 +91,11 @@ typedef struct {
     int32_t num_global_experts; /* expert-parallel shard: the range of topk_ids,
                                    E being the experts held here (fused_experts_ep);
                                    0 otherwise. topk <= num_global_experts */
+    int32_t chunk_tokens; /* > 0: fused_experts(_ep) runs the layer on chunks of this
+                             many tokens, one after another on the stream, and the
+                             workspace is sized for one chunk ("fused_moe.py
+                             analysis", section 6: 16K-token chunks bound the
+                             intermediate buffers); 0: one pass over all M tokens */
 } moe_problem_t;
 
 /*

@@ -34,7 +34,8 @@ class MoeProblem(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("wdtype", ctypes.c_int32), ("apply_router_weight_on_input", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32), ("num_global_experts", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("num_global_experts", ctypes.c_int32),
+                ("chunk_tokens", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -228,9 +229,9 @@ def moe_quant_fp8_groups(x: torch.Tensor, stream=None):
 
 
 def make_problem(M, H, I, E, topk, block_m, wdtype=MOE_W_BF16, on_input=False,
-                 weight_layout=MOE_LAYOUT_ROWS, num_global_experts=0) -> MoeProblem:
+                 weight_layout=MOE_LAYOUT_ROWS, num_global_experts=0, chunk_tokens=0) -> MoeProblem:
     return MoeProblem(M, H, I, E, topk, block_m, wdtype, int(on_input), weight_layout,
-                      num_global_experts)
+                      num_global_experts, chunk_tokens)
 
 
 def moe_workspace_bytes(p: MoeProblem) -> int:
@@ -247,12 +248,13 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
                   w2_scale: torch.Tensor | None = None, apply_router_weight_on_input=False,
                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                   stream=None, weight_layout=MOE_LAYOUT_ROWS,
-                  expert_map: torch.Tensor | None = None) -> torch.Tensor:
+                  expert_map: torch.Tensor | None = None, chunk_tokens: int = 0) -> torch.Tensor:
     """y = fused MoE expert forward (bf16 [M, H]). `out` may be `x` (in place).
 
     weight_layout MOE_LAYOUT_TILED: w13 and w2 come from moe_pack_weights (same shapes).
     expert_map [G] int32 (one expert-parallel rank): topk_ids are global ids in [0, G),
-    w13 / w2 hold this rank's E experts, and y sums only the slots of those experts."""
+    w13 / w2 hold this rank's E experts, and y sums only the slots of those experts.
+    chunk_tokens > 0: the layer runs on chunks of that many tokens (workspace for one chunk)."""
     if expert_map is not None:
         _need(expert_map, torch.int32, "expert_map")
     _need(x, torch.bfloat16, "x")
@@ -272,7 +274,7 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
         raise ValueError("fused_experts: inconsistent shapes")
     p = make_problem(M, H, N2 // 2, E, topk_ids.shape[1], block_m,
                      MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16, apply_router_weight_on_input,
-                     weight_layout, 0 if expert_map is None else expert_map.numel())
+                     weight_layout, 0 if expert_map is None else expert_map.numel(), chunk_tokens)
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:

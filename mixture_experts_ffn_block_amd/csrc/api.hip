@@ -42,6 +42,17 @@ Rows batched_rows(const moe_problem_t& p) {
     return {n, n, 1};
 }
 
+// the problem one chunk of at most chunk_tokens tokens runs as
+moe_problem_t chunk_problem(const moe_problem_t& p, int64_t tokens) {
+    moe_problem_t q = p;
+    q.M = tokens;
+    return q;
+}
+
+int64_t chunk_of(const moe_problem_t& p) {
+    return p.chunk_tokens > 0 && p.chunk_tokens < p.M ? p.chunk_tokens : p.M;
+}
+
 struct Layout {
     int64_t cap, R;
     int64_t sorted, expert_ids, npp, inv_perm, xq, xs, xst, ho, z, zs, split, total;
@@ -83,7 +94,7 @@ constexpr int kMaxGlobalE = 1 << 16;  // routing range of an expert map
 moe_status_t check_problem(const moe_problem_t* p) {
     if (!p) return MOE_E_INVALID;
     if (p->M < 0 || p->H <= 0 || p->I <= 0 || p->E <= 0 || p->topk <= 0) return MOE_E_INVALID;
-    if (p->num_global_experts < 0) return MOE_E_INVALID;
+    if (p->num_global_experts < 0 || p->chunk_tokens < 0) return MOE_E_INVALID;
     if (p->num_global_experts > kMaxGlobalE) return MOE_E_UNSUPPORTED;
     // top-k picks distinct experts of the routing range: the global experts under
     // an expert map, else the E experts held here
@@ -333,7 +344,8 @@ moe_status_t moe_quant_fp8_groups(const void* x, int64_t rows, int32_t cols, voi
 
 size_t moe_workspace_bytes(const moe_problem_t* p) {
     if (check_problem(p) != MOE_OK || p->M == 0) return 0;
-    return static_cast<size_t>(layout(*p, routed_rows(*p)).total);
+    const moe_problem_t q = chunk_problem(*p, chunk_of(*p));
+    return static_cast<size_t>(layout(q, routed_rows(q)).total);
 }
 
 }  // extern "C"
@@ -424,6 +436,29 @@ moe_status_t check_batched(const moe_problem_t* p) {
     return check_problem(&q);
 }
 
+// the layer over chunks of tokens, one after another on the stream, each reusing
+// the whole workspace (a chunk's kernels are enqueued after the previous chunk's)
+moe_status_t run_chunked(const moe_problem_t* p, const int32_t* emap, const void* x, const void* w13,
+                         const float* w13_scale, const void* w2, const float* w2_scale,
+                         const int32_t* topk_ids, const float* topk_weights, void* y,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    const int64_t chunk = chunk_of(*p);
+    if (chunk == p->M)
+        return run_fused(p, emap, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y,
+                         workspace, workspace_bytes, stream);
+    if (!x || !topk_ids || !topk_weights || !y) return MOE_E_INVALID;
+    const int64_t row = static_cast<int64_t>(p->H) * 2;  // bytes of one x / y row
+    for (int64_t t0 = 0; t0 < p->M; t0 += chunk) {
+        const moe_problem_t q = chunk_problem(*p, p->M - t0 < chunk ? p->M - t0 : chunk);
+        const moe_status_t st = run_fused(
+            &q, emap, static_cast<const uint8_t*>(x) + t0 * row, w13, w13_scale, w2, w2_scale,
+            topk_ids + t0 * p->topk, topk_weights + t0 * p->topk, static_cast<uint8_t*>(y) + t0 * row,
+            workspace, workspace_bytes, stream);
+        if (st != MOE_OK) return st;
+    }
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -435,8 +470,8 @@ moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w1
     const moe_status_t st = check_problem(p);
     if (st != MOE_OK) return st;
     if (p->num_global_experts != 0) return MOE_E_INVALID;  // global ids need the expert map
-    return run_fused(p, nullptr, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y,
-                     workspace, workspace_bytes, stream);
+    return run_chunked(p, nullptr, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y,
+                       workspace, workspace_bytes, stream);
 }
 
 moe_status_t fused_experts_ep(const moe_problem_t* p, const int32_t* expert_map, const void* x,
@@ -447,8 +482,8 @@ moe_status_t fused_experts_ep(const moe_problem_t* p, const int32_t* expert_map,
     const moe_status_t st = check_problem(p);
     if (st != MOE_OK) return st;
     if (p->num_global_experts <= 0 || !expert_map) return MOE_E_INVALID;
-    return run_fused(p, expert_map, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y,
-                     workspace, workspace_bytes, stream);
+    return run_chunked(p, expert_map, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y,
+                       workspace, workspace_bytes, stream);
 }
 
 size_t moe_batched_workspace_bytes(const moe_problem_t* p) {

@@ -54,6 +54,9 @@ WORKLOADS = {
                        bias_std=0.0),
     "fp8_block_m4096": dict(M=4096, H=7168, I=2048, E=256, topk=8, wdtype="fp8",
                             block_m=128, bias_std=0.0),
+    # a long prefill on the Mixtral shape, run in two chunks of 16K tokens
+    "mixtral_prefill_m32768_chunk16k": dict(M=32768, H=4096, I=14336, E=8, topk=2, wdtype="bf16",
+                                            block_m=256, chunk_tokens=16384),
     # DeepSeek-V3-style routing on the DSV3 shape: sigmoid scores, 8 groups of 32
     # experts of which 4 are kept, a correction bias, weights scaled by 2.5
     "dsv3_grouped_prefill_m8192": dict(M=8192, H=7168, I=2048, E=256, topk=8, wdtype="bf16",
@@ -98,6 +101,7 @@ class Problem:
     topk_group: int = 1
     score_bias_std: float = 0.0
     routed_scale: float = 1.0
+    chunk_tokens: int = 0         # > 0: the layer runs on chunks of this many tokens
 
     @property
     def local_experts(self) -> range:

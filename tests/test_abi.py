@@ -205,3 +205,11 @@ def test_grouped_router_validation():
     assert T(d, 4, 256, 8, G, 1, 128, 64, None, 1.0, d, d, None) == moe.MOE_E_UNSUPPORTED  # G > 64
     assert T(None, 4, 256, 8, G, 1, 8, 4, d, 2.5, d, d, None) == moe.MOE_E_INVALID
     assert T(None, 0, 256, 8, G, 1, 8, 4, None, 2.5, None, None, None) == moe.MOE_OK
+
+
+def test_chunked_workspace():
+    full = moe.moe_workspace_bytes(P(M=1000, block_m=64))
+    chunked = moe.moe_workspace_bytes(P(M=1000, block_m=64, chunk_tokens=256))
+    assert chunked == moe.moe_workspace_bytes(P(M=256, block_m=64)) and chunked < full
+    assert moe.moe_workspace_bytes(P(M=100, block_m=64, chunk_tokens=256)) == moe.moe_workspace_bytes(P(M=100, block_m=64))
+    assert moe.moe_workspace_bytes(P(chunk_tokens=-1)) == 0

@@ -66,9 +66,10 @@ def run_layer(p: synth.Problem, d: synth.Inputs, ids, w, out=None):
     if p.wdtype == "fp8":
         return moe.fused_experts(d.x, d.w13q, d.w2q, ids, w, p.block_m, d.w13s, d.w2s,
                                  apply_router_weight_on_input=p.apply_router_weight_on_input,
-                                 out=out)
+                                 out=out, chunk_tokens=p.chunk_tokens)
     return moe.fused_experts(d.x, d.w13, d.w2, ids, w, p.block_m,
-                             apply_router_weight_on_input=p.apply_router_weight_on_input, out=out)
+                             apply_router_weight_on_input=p.apply_router_weight_on_input, out=out,
+                             chunk_tokens=p.chunk_tokens)
 
 
 def oracle_layer(p, inp_cpu, ids, w, t0=0, t1=None):
@@ -424,6 +425,41 @@ def sampled_check(name, n_samples=6):
 
 
 @pytest.mark.parametrize("name", ["mixtral_prefill_m4096", "dsv3_skewed_prefill_m8192",
-                                  "fp8_block_m4096", "dsv3_grouped_prefill_m8192"])
+                                  "fp8_block_m4096", "dsv3_grouped_prefill_m8192",
+                                  "mixtral_prefill_m32768_chunk16k"])
 def test_layer_full_size_sampled(name):
     sampled_check(name)
+
+
+# ------------------------------------------------------------- chunking ---
+
+CHUNKED = [
+    dict(M=1000, H=256, I=256, E=8, topk=2, block_m=64, chunk_tokens=256),          # ragged last chunk
+    dict(M=700, H=512, I=256, E=7, topk=3, block_m=128, wdtype="fp8", chunk_tokens=300),
+    dict(M=333, H=384, I=256, E=6, topk=2, block_m=16, chunk_tokens=100,
+         apply_router_weight_on_input=True),
+    dict(M=600, H=512, I=384, E=3, topk=2, block_m=256, chunk_tokens=512),
+    dict(M=64, H=256, I=512, E=8, topk=2, block_m=16, chunk_tokens=64),             # one chunk
+]
+
+
+@pytest.mark.parametrize("cfg", CHUNKED, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_layer_chunked(cfg):
+    # chunks run the layer on token ranges one after another: each token's result is
+    # the oracle's (within tolerance) and close to the one-pass result; in place too
+    p = synth.Problem(**cfg)
+    log(f"chunked {cfg}")
+    inp = synth.make_inputs(p, "cpu")
+    d = to_dev(inp)
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    y = run_layer(p, d, ids, w)
+    one = run_layer(synth.Problem(**dict(cfg, chunk_tokens=0)), d, ids, w)
+    x_copy = d.x.clone()
+    y_in = run_layer(p, d, ids, w, out=d.x)
+    torch.cuda.synchronize()
+    assert torch.equal(y_in, y) and not torch.equal(d.x, x_copy)
+    y_ref = oracle_layer(p, inp, ids.cpu().numpy(), w.cpu().numpy())
+    assert_close(bits16(y), y_ref, TOL[p.wdtype], str(cfg))
+    assert_close(bits16(y), bits16(one), TOL[p.wdtype], "chunked vs one pass")
+    if p.chunk_tokens >= p.M:
+        assert torch.equal(y, one)
