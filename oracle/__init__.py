@@ -50,6 +50,14 @@ def lib():
             "oracle_f32_to_e4m3_n": [_P, _I64, _P],
             "oracle_quant_groups_fp8": [_P, _I64, _P, _P],
             "oracle_topk": [_P, _I64, _I32, _I32, _I32, _P, _P],
+            "oracle_e8m0_to_f64": [ctypes.c_uint8],
+            "oracle_e2m1_to_f64": [ctypes.c_uint8],
+            "oracle_f32_to_e2m1": [ctypes.c_float],
+            "oracle_quant_mx_fp8": [_P, _I64, _P, _P],
+            "oracle_quant_mx_fp4": [_P, _I64, _P, _P],
+            "oracle_gemm_mx": [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _P],
+            "oracle_fused_experts_mx": [_I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                        _I32, _I64, _I64, _P, _P],
             "oracle_topk_grouped": [_P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                     ctypes.c_float, _P, _P],
             "oracle_align_capacity": [_I64, _I32, _I32, _I32],
@@ -72,6 +80,9 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
         L.oracle_align_capacity.restype = _I64
+        L.oracle_e8m0_to_f64.restype = ctypes.c_double
+        L.oracle_e2m1_to_f64.restype = ctypes.c_double
+        L.oracle_f32_to_e2m1.restype = ctypes.c_uint8
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = _I32
         _lib = L
@@ -333,3 +344,69 @@ def batched_experts_fp8(a, counts, w13q, w13s, w2q, w2s):
                                         _p(w2q), _p(w2s), _p(out)):
         raise ValueError("oracle_batched_experts_fp8: negative count")
     return out
+
+
+# ------------------------------------------------------------- MX formats ---
+
+def e8m0_to_f64(c: int) -> float:
+    return float(lib().oracle_e8m0_to_f64(int(c)))
+
+
+def e2m1_to_f64(c: int) -> float:
+    return float(lib().oracle_e2m1_to_f64(int(c)))
+
+
+def f32_to_e2m1(v: float) -> int:
+    return int(lib().oracle_f32_to_e2m1(float(v)))
+
+
+def quant_mx_fp8(v: np.ndarray):
+    """[.., K] values -> (E4M3 codes [.., K] uint8, E8M0 codes [.., K/32] uint8), per 32 columns."""
+    v = _c(v, np.float32)
+    q = np.empty(v.shape, np.uint8)
+    sc = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    lib().oracle_quant_mx_fp8(_p(v), v.size, _p(q), _p(sc))
+    return q, sc
+
+
+def quant_mx_fp4(v: np.ndarray):
+    """[.., K] values -> (E2M1 codes [.., K/2] uint8, two per byte, element 2i low, E8M0 [.., K/32])."""
+    v = _c(v, np.float32)
+    q = np.empty(v.shape[:-1] + (v.shape[-1] // 2,), np.uint8)
+    sc = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    lib().oracle_quant_mx_fp4(_p(v), v.size, _p(q), _p(sc))
+    return q, sc
+
+
+def gemm_mx(qa, sa, qw, sw, fmt_w="e4m3"):
+    """bf16 [N] = MX GEMM of one activation row (E4M3 + E8M0 [K/32] or fp32 [K/128]) with
+    weights (E4M3 [N, K] or E2M1 [N, K/2]) and their E8M0 scales [N, K/32]."""
+    qa, qw, sw = _c(qa, np.uint8), _c(qw, np.uint8), _c(sw, np.uint8)
+    mx_a = sa.dtype == np.uint8
+    sa = _c(sa, np.uint8 if mx_a else np.float32)
+    N, K = sw.shape[0], sw.shape[1] * 32
+    out = np.empty(N, np.uint16)
+    lib().oracle_gemm_mx(_p(qa), _p(sa), int(mx_a), _p(qw), _p(sw), 0 if fmt_w == "e4m3" else 1, N, K, _p(out))
+    return out
+
+
+def fused_experts_mx(x, w13q, w13e, w2q, w2e, ids, weights, w4=False, on_input=False, t0=0, t1=None,
+                     return_acc=False):
+    """y rows [t0, t1): MXFP8 layer (w4=False: E4M3 weights, MXFP8 activations and z) or
+    W4A8 (w4=True: E2M1 weights [E, N, K/2], FP8 activations and z with fp32 per-128 scales);
+    weight scales E8M0 [E, N, K/32] in both."""
+    x = _c(x, np.uint16)
+    w13q, w13e, w2q, w2e = (_c(a, np.uint8) for a in (w13q, w13e, w2q, w2e))
+    ids, weights = _c(ids, np.int32), _c(weights, np.float32)
+    M, H = x.shape
+    E, N2 = w13e.shape[0], w13e.shape[1]
+    k = ids.shape[1]
+    t1 = M if t1 is None else t1
+    y = np.zeros((M, H), np.uint16)
+    acc = np.zeros((M, H), np.float64) if return_acc else None
+    rc = lib().oracle_fused_experts_mx(M, H, N2 // 2, E, k, int(w4), _p(x), _p(w13q), _p(w13e), _p(w2q),
+                                       _p(w2e), _p(ids), _p(weights), int(on_input), t0, t1, _p(y),
+                                       _p(acc) if acc is not None else None)
+    if rc:
+        raise ValueError("oracle_fused_experts_mx: expert id out of range")
+    return (y[t0:t1], acc[t0:t1]) if return_acc else y[t0:t1]

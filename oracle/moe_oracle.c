@@ -165,6 +165,170 @@ void oracle_quant_groups_fp8(const float *v, int64_t n, uint8_t *q, float *scale
 }
 
 /* ------------------------------------------------------------------------ */
+/* MX block scaling ([DG] TL;DR and section 4: MXFP8 1x32 with E8M0 scales on */
+/* weights and dynamic activations; W4A8: E2M1 weights with E8M0/32 scales;  */
+/* the "UE8M0" / "CEIL_UE8M0" scale formats). E8M0 code c means 2^(c - 127); */
+/* 255 is NaN. A block of 32 values takes the smallest power-of-two scale s  */
+/* with max|v| <= fmax * s (fmax 448 for E4M3, 6 for E2M1), clamped to the   */
+/* E8M0 range; the codes are the element format's RNE(v / s). An all-zero   */
+/* block gets code 0 and zero elements.                                      */
+/* ------------------------------------------------------------------------ */
+
+static double silu(double g);
+
+double oracle_e8m0_to_f64(uint8_t c) { return c == 255 ? NAN : ldexp(1.0, (int)c - 127); }
+
+/* E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double oracle_e2m1_to_f64(uint8_t c)
+{
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double v = mag[c & 7];
+    return (c & 8) ? -v : v;
+}
+
+/* nearest E2M1 value, ties to the even code (mantissa bit 0), saturating at 6 */
+uint8_t oracle_f32_to_e2m1(float f)
+{
+    uint8_t sign = signbit(f) ? 8 : 0;
+    double a = fabs((double)f);
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(a - oracle_e2m1_to_f64((uint8_t)c)), db = fabs(a - oracle_e2m1_to_f64((uint8_t)best));
+        if (d < db || (d == db && (c & 1) == 0)) best = c;
+    }
+    return sign | (uint8_t)best;
+}
+
+/* the E8M0 code of the smallest s = 2^e with a <= fmax * s */
+static uint8_t mx_scale_code(double a, double fmax)
+{
+    if (a == 0.0) return 0;
+    int e;
+    frexp(a / fmax, &e);            /* a / fmax in [2^(e-1), 2^e): the answer is e-1 or e */
+    while (e > -127 && a <= fmax * ldexp(1.0, e - 1)) --e;
+    while (a > fmax * ldexp(1.0, e)) ++e;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (uint8_t)(e + 127);
+}
+
+/* n values (n a multiple of 32) -> E4M3 codes q[n] and E8M0 codes sc[n / 32] */
+void oracle_quant_mx_fp8(const float *v, int64_t n, uint8_t *q, uint8_t *sc)
+{
+    for (int64_t b = 0; b < n / 32; ++b) {
+        double a = 0.0;
+        for (int i = 0; i < 32; ++i) a = fmax(a, fabs((double)v[b * 32 + i]));
+        sc[b] = mx_scale_code(a, 448.0);
+        double s = oracle_e8m0_to_f64(sc[b]);
+        for (int i = 0; i < 32; ++i)
+            q[b * 32 + i] = a == 0.0 ? 0 : oracle_f32_to_e4m3((float)(v[b * 32 + i] / s));
+    }
+}
+
+/* n values -> E2M1 codes, two per byte (element 2i in the low nibble), and E8M0 scales */
+void oracle_quant_mx_fp4(const float *v, int64_t n, uint8_t *q, uint8_t *sc)
+{
+    for (int64_t b = 0; b < n / 32; ++b) {
+        double a = 0.0;
+        for (int i = 0; i < 32; ++i) a = fmax(a, fabs((double)v[b * 32 + i]));
+        sc[b] = mx_scale_code(a, 6.0);
+        double s = oracle_e8m0_to_f64(sc[b]);
+        for (int i = 0; i < 32; i += 2) {
+            uint8_t lo = a == 0.0 ? 0 : oracle_f32_to_e2m1((float)(v[b * 32 + i] / s));
+            uint8_t hi = a == 0.0 ? 0 : oracle_f32_to_e2m1((float)(v[b * 32 + i + 1] / s));
+            q[(b * 32 + i) / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+/* out[n] = bf16( sum over 32-blocks b of (sum_{c in b} qa_c * qw[n, c]) * sa_b * sw[n, b] ),
+ * fp64 accumulation. fmt_w 0: E4M3 weights [N, K]; 1: E2M1 weights [N, K/2]. The
+ * activation side is E4M3 with E8M0 scales (mx_a = 1), or with one fp32 scale per
+ * 128 columns (mx_a = 0, sa holds K/128 floats; W4A8's FP8 activations). */
+void oracle_gemm_mx(const uint8_t *qa, const void *sa, int mx_a, const uint8_t *qw, const uint8_t *sw,
+                    int fmt_w, int N, int K, uint16_t *out)
+{
+    for (int n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int b = 0; b < K / 32; ++b) {
+            double part = 0.0;
+            for (int c = b * 32; c < b * 32 + 32; ++c) {
+                double w = fmt_w == 0 ? oracle_e4m3_to_f64(qw[(int64_t)n * K + c])
+                                      : oracle_e2m1_to_f64((qw[((int64_t)n * K + c) / 2] >> (4 * (c & 1))) & 15);
+                part += oracle_e4m3_to_f64(qa[c]) * w;
+            }
+            double a_scale = mx_a ? oracle_e8m0_to_f64(((const uint8_t *)sa)[b])
+                                  : (double)((const float *)sa)[b / 4];
+            acc += part * a_scale * oracle_e8m0_to_f64(sw[(int64_t)n * (K / 32) + b]);
+        }
+        out[n] = oracle_f64_to_bf16(acc);
+    }
+}
+
+/* MXFP8 layer: activations and z quantised to MXFP8 per 32 columns; weights E4M3
+ * with E8M0 scales [E, N, K/32] ([DG] TL;DR: MXFP8 (1x32), weights and dynamic
+ * activations). W4A8 layer (mx_w4 = 1): weights E2M1 [E, N, K/2] with E8M0
+ * scales, activations and z as in the FP8 block recipe (E4M3, fp32 scale per
+ * 128 columns) ([DG] TL;DR: MXFP4 weights x FP8 activations (128)). */
+int oracle_fused_experts_mx(int64_t M, int H, int I, int E, int k, int mx_w4,
+                            const uint16_t *x, const uint8_t *w13q, const uint8_t *w13e,
+                            const uint8_t *w2q, const uint8_t *w2e,
+                            const int32_t *ids, const float *weights, int on_input,
+                            int64_t t0, int64_t t1, uint16_t *y, double *acc_out)
+{
+    (void)M;
+    int bad = 0;
+    int64_t wb13 = mx_w4 ? (int64_t)I * H : (int64_t)2 * I * H;   /* bytes per expert */
+    int64_t wb2 = mx_w4 ? (int64_t)H * I / 2 : (int64_t)H * I;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = t0; t < t1; ++t) {
+        float *xf = malloc(sizeof(float) * (size_t)H);
+        uint8_t *xq = malloc((size_t)H);
+        uint8_t *xs8 = malloc((size_t)(H / 32));
+        float *xs = malloc(sizeof(float) * (size_t)(H / 128));
+        uint16_t *h = malloc(sizeof(uint16_t) * 2 * (size_t)I);
+        float *zf = malloc(sizeof(float) * (size_t)I);
+        uint8_t *zq = malloc((size_t)I);
+        uint8_t *zs8 = malloc((size_t)(I / 32));
+        float *zs = malloc(sizeof(float) * (size_t)(I / 128));
+        uint16_t *o = malloc(sizeof(uint16_t) * (size_t)H);
+        double *acc = calloc((size_t)H, sizeof(double));
+        for (int c = 0; c < H; ++c) xf[c] = (float)oracle_bf16_to_f64(x[t * H + c]);
+        if (mx_w4) oracle_quant_groups_fp8(xf, H, xq, xs);
+        else oracle_quant_mx_fp8(xf, H, xq, xs8);
+        for (int j = 0; j < k; ++j) {
+            int e = ids[t * k + j];
+            if (e < 0 || e >= E) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            double alpha = weights[t * k + j];
+            oracle_gemm_mx(xq, mx_w4 ? (const void *)xs : (const void *)xs8, !mx_w4, w13q + e * wb13,
+                           w13e + (int64_t)e * 2 * I * (H / 32), mx_w4, 2 * I, H, h);
+            double a1 = on_input ? alpha : 1.0;
+            for (int i = 0; i < I; ++i) {
+                double g = oracle_bf16_to_f64(h[i]), u = oracle_bf16_to_f64(h[I + i]);
+                zf[i] = (float)(a1 * silu(g) * u);
+            }
+            if (mx_w4) oracle_quant_groups_fp8(zf, I, zq, zs);
+            else oracle_quant_mx_fp8(zf, I, zq, zs8);
+            oracle_gemm_mx(zq, mx_w4 ? (const void *)zs : (const void *)zs8, !mx_w4, w2q + e * wb2,
+                           w2e + (int64_t)e * H * (I / 32), mx_w4, H, I, o);
+            double a2 = on_input ? 1.0 : alpha;
+            for (int n = 0; n < H; ++n) acc[n] += a2 * oracle_bf16_to_f64(o[n]);
+        }
+        for (int n = 0; n < H; ++n) {
+            y[t * H + n] = oracle_f64_to_bf16(acc[n]);
+            if (acc_out) acc_out[t * H + n] = acc[n];
+        }
+        free(xf); free(xq); free(xs8); free(xs); free(h); free(zf); free(zq); free(zs8); free(zs);
+        free(o); free(acc);
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Router ([MK] section 3; [FG] 1.1): p = softmax(s) over all E experts,       */
 /* S = TopK(p, k), weights renormalised over S when `renormalize` is set.     */
 /* ------------------------------------------------------------------------ */

@@ -25,6 +25,11 @@ generation is chunked):
 * ``w2``      [E, H, I]  ~ N(0, 1/sqrt(I)) -> bf16.
 * fp8 workloads: ``w13q``/``w2q`` float8_e4m3fn with fp32 scales per 128x128
   block, ``scale = amax(block) / 448``, ``q = e4m3(w / scale)``.
+* MX workloads (offline weight preparation as well, [DG] TL;DR: MXFP8 1x32 and
+  W4A8 MXFP4): ``wdtype="mxfp8"`` gives E4M3 weights and ``"w4a8"`` E2M1 weights
+  (two per byte, element 2i in the low nibble), each 32 columns of a row
+  sharing one E8M0 scale 2^ceil(log2(amax / fmax)) (fmax 448 or 6), stored
+  [E, N, K/32] uint8; E2M1 takes the nearest grid value (ties to the smaller).
 * Expert-parallel workloads (``ep_size`` > 1): the logits cover all E experts
   (global routing); rank ``ep_rank`` holds the contiguous range of E / ep_size
   experts starting at ``ep_rank * E / ep_size``, whose weights are the same
@@ -149,14 +154,40 @@ def block_quant_fp8(w: torch.Tensor):
     return q.view(N, K), scale
 
 
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def mx_quant(w: torch.Tensor, fmt: str):
+    """1x32 MX quantisation of a bf16 [N, K] matrix (offline weight prep).
+
+    Returns (codes, scales): E4M3 float8_e4m3fn [N, K] or packed E2M1 uint8 [N, K/2],
+    and E8M0 codes uint8 [N, K/32].
+    """
+    N, K = w.shape
+    wf = w.float().view(N, K // 32, 32)
+    amax = wf.abs().amax(-1)
+    fmax = 448.0 if fmt == "e4m3" else 6.0
+    safe = torch.where(amax > 0, amax, torch.full_like(amax, fmax))
+    e = torch.ceil(torch.log2(safe / fmax)).clamp_(-127, 127)
+    e = torch.where(amax > 0, e, torch.full_like(e, -127))
+    v = wf / torch.exp2(e)[..., None]
+    sc = (e + 127).to(torch.uint8)
+    if fmt == "e4m3":
+        return v.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(N, K), sc
+    mags = torch.tensor(_E2M1, device=w.device)
+    idx = (v.abs().clamp(max=6.0)[..., None] - mags).abs().argmin(-1).to(torch.uint8)
+    codes = (idx | (v < 0).to(torch.uint8) << 3).view(N, K)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous(), sc
+
+
 @dataclasses.dataclass
 class Inputs:
     x: torch.Tensor                   # [M, H] bf16
     logits: torch.Tensor              # [M, E] fp32
     w13: torch.Tensor | None          # [E, 2I, H] bf16 (bf16 workloads)
     w2: torch.Tensor | None           # [E, H, I] bf16
-    w13q: torch.Tensor | None = None  # [E, 2I, H] float8_e4m3fn (fp8 workloads)
-    w13s: torch.Tensor | None = None  # [E, 2I/128, H/128] fp32
+    w13q: torch.Tensor | None = None  # [E, 2I, H] float8_e4m3fn (fp8, mxfp8), [E, 2I, H/2] uint8 (w4a8)
+    w13s: torch.Tensor | None = None  # [E, 2I/128, H/128] fp32 (fp8), [E, 2I, H/32] uint8 E8M0 (MX)
     w2q: torch.Tensor | None = None   # [E, H, I] float8_e4m3fn
     w2s: torch.Tensor | None = None   # [E, H/128, I/128] fp32
     expert_map: torch.Tensor | None = None  # [E] int32 on expert-parallel ranks, else None
@@ -195,6 +226,20 @@ def make_inputs(p: Problem, device="cpu") -> Inputs:
             w13q[i], w13s[i] = block_quant_fp8(m13)
             m2 = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I)).to(torch.bfloat16)
             w2q[i], w2s[i] = block_quant_fp8(m2)
+        return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s, expert_map=emap, score_bias=sbias)
+    if p.wdtype in ("mxfp8", "w4a8"):
+        fmt = "e4m3" if p.wdtype == "mxfp8" else "e2m1"
+        div = 1 if fmt == "e4m3" else 2
+        dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.uint8
+        w13q = torch.empty((EL, 2 * I, H // div), dtype=dt, device=device)
+        w2q = torch.empty((EL, H, I // div), dtype=dt, device=device)
+        w13s = torch.empty((EL, 2 * I, H // 32), dtype=torch.uint8, device=device)
+        w2s = torch.empty((EL, H, I // 32), dtype=torch.uint8, device=device)
+        for i, e in enumerate(held):
+            m13 = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H)).to(torch.bfloat16)
+            w13q[i], w13s[i] = mx_quant(m13, fmt)
+            m2 = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I)).to(torch.bfloat16)
+            w2q[i], w2s[i] = mx_quant(m2, fmt)
         return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s, expert_map=emap, score_bias=sbias)
     raise ValueError(f"unknown weight dtype {p.wdtype!r}")
 
