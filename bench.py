@@ -91,13 +91,14 @@ class Step:
     def __init__(self, p: synth.Problem, d: synth.Inputs, layout: str = "auto", weights=None):
         import mixture_experts_ffn_block_amd as moe
         self.moe, self.p, self.d = moe, p, d
-        self.fp8 = p.wdtype == "fp8"
+        self.fp8 = p.wdtype in ("fp8", "mxfp8")   # 8-bit weights and activations
+        self.mx = p.wdtype == "mxfp8"              # E8M0 scales per 32 values
         dev = d.x.device
         # an expert-parallel rank holds E / ep_size experts; ids stay global
         self.emap = d.expert_map
         G = p.E if self.emap is not None else 0
         M, H, I, E, k, B = p.M, p.H, p.I, len(p.local_experts), p.topk, p.block_m
-        wdt = moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16
+        wdt = moe.MOE_W_MXFP8 if self.mx else moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16
         rows = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input)
         packable = not self.fp8 and B in (16, 128, 256)
         if layout == "tiled" and not packable:
@@ -121,15 +122,20 @@ class Step:
         self.o = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
         adt = torch.float8_e4m3fn if self.fp8 else torch.bfloat16
         self.z = torch.empty((cap, I), dtype=adt, device=dev)
-        self.zs = torch.empty((I // 128, cap), dtype=torch.float32, device=dev) if self.fp8 else None
+        sdt = torch.int32 if self.mx else torch.float32  # MX: four E8M0 bytes per word
+        self.zs = torch.empty((I // 128, cap), dtype=sdt, device=dev) if self.fp8 else None
         if self.fp8:
             self.xq = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
-            self.xs = torch.empty((M, H // 128), dtype=torch.float32, device=dev)
-            self.xst = torch.empty((H // 128, cap), dtype=torch.float32, device=dev)
+            self.xs = torch.empty((M, H // 128), dtype=sdt, device=dev)
+            self.xst = torch.empty((H // 128, cap), dtype=sdt, device=dev)
         self.act_fused = moe.moe_expert_gemm_act_supported(self.prob)
         self.gws = moe.gemm_workspace_for(self.prob, dev)  # split-K tail of the second GEMM
         self.w13 = d.w13q if self.fp8 else d.w13
         self.w2 = d.w2q if self.fp8 else d.w2
+        self.w13s, self.w2s = d.w13s, d.w2s
+        if self.mx:  # weight-scale preparation, once, outside every timed region
+            self.w13s = moe.moe_pack_mx_scales(rows, 1, d.w13s)
+            self.w2s = moe.moe_pack_mx_scales(rows, 2, d.w2s)
         if weights is not None:  # prepared by another Step of the same workload
             self.w13, self.w2 = weights
         elif self.layout == "tiled":  # weight preparation, once, outside every timed region
@@ -149,7 +155,7 @@ class Step:
         m, d = self.moe, self.d
         self.route()
         m.fused_experts(d.x, self.w13, self.w2, self.ids, self.w, self.p.block_m,
-                        d.w13s, d.w2s, self.p.apply_router_weight_on_input, out=self.y,
+                        self.w13s, self.w2s, self.p.apply_router_weight_on_input, out=self.y,
                         workspace=self.ws, weight_layout=self.wl, expert_map=self.emap,
                         chunk_tokens=self.p.chunk_tokens)
 
@@ -165,8 +171,8 @@ class Step:
         ev[1].record()
         a1, a1s = d.x, None
         if self.fp8:
-            lib.moe_quant_fp8_groups(m._ptr(d.x), self.p.M, self.p.H, m._ptr(self.xq),
-                                     m._ptr(self.xs), s)
+            quant = lib.moe_quant_mx_groups if self.mx else lib.moe_quant_fp8_groups
+            quant(m._ptr(d.x), self.p.M, self.p.H, m._ptr(self.xq), m._ptr(self.xs), s)
             a1, a1s = self.xq, self.xst
         ev[2].record()
         if self.emap is None:
@@ -181,17 +187,17 @@ class Step:
             m.moe_permute_scales(p, self.xs, self.sorted, self.npp, self.xst)
         ev[3].record()
         if self.act_fused:  # GEMM1 with the activation in its epilogue; no separate act stage
-            m.moe_expert_gemm_act(p, a1, a1s, self.w13, d.w13s, self.sorted, self.expert_ids,
+            m.moe_expert_gemm_act(p, a1, a1s, self.w13, self.w13s, self.sorted, self.expert_ids,
                                   self.npp, self.w, self.z, self.zs)
             ev[4].record()
         else:
             m.moe_expert_gemm(p, 1, a1, self.w13, self.sorted, self.expert_ids, self.npp, self.h,
-                              a1s, d.w13s)
+                              a1s, self.w13s)
             ev[4].record()
             m.moe_silu_and_mul(p, self.h, self.sorted, self.w, self.npp, self.z, self.zs)
         ev[5].record()
         m.moe_expert_gemm(p, 2, self.z, self.w2, None, self.expert_ids, self.npp, self.o,
-                          self.zs, d.w2s, workspace=self.gws)
+                          self.zs, self.w2s, workspace=self.gws)
         ev[6].record()
         m.moe_unpermute_reduce(p, self.o, self.inv, self.w, self.y)
         ev[7].record()
@@ -279,20 +285,25 @@ def algorithmic(p: synth.Problem, touched: int, act_fused: bool = False, R: int 
     with the activation fused into GEMM1 that kernel writes z instead of h. R: the
     routed items computed here (all M * topk, or an expert-parallel rank's share)."""
     R = p.M * p.topk if R is None else R
-    wb = 1 if p.wdtype == "fp8" else 2
+    q8 = p.wdtype in ("fp8", "mxfp8")
+    wb = 1 if q8 else 2
+    # scale bytes per K value: fp32 per 128x128 block (weights) or per 128 (activations),
+    # or one E8M0 byte per 32 values (MX)
+    ws_per = 1.0 / 32 if p.wdtype == "mxfp8" else 4.0 / (128 * 128)
+    as_per = 1.0 / 32 if p.wdtype == "mxfp8" else 4.0 / 128
     flops_g1 = 4.0 * R * p.H * p.I
     flops = 6.0 * R * p.H * p.I
     w13_b = touched * 2 * p.I * p.H * wb
     w2_b = touched * p.H * p.I * wb
-    if p.wdtype == "fp8":
-        w13_b += touched * (2 * p.I // 128) * (p.H // 128) * 4
-        w2_b += touched * (p.H // 128) * (p.I // 128) * 4
+    if q8:
+        w13_b += touched * 2 * p.I * p.H * ws_per
+        w2_b += touched * p.H * p.I * ws_per
     x_b = p.M * p.H * 2
     y_b = p.M * p.H * 2
     logits_b = p.M * p.E * 4
-    xin_g1 = p.M * p.H * wb + (p.M * (p.H // 128) * 4 if p.wdtype == "fp8" else 0)
+    xin_g1 = p.M * p.H * wb + (p.M * p.H * as_per if q8 else 0)
     if act_fused:
-        out_g1 = R * p.I * wb + (R * (p.I // 128) * 4 if p.wdtype == "fp8" else 0)
+        out_g1 = R * p.I * wb + (R * p.I * as_per if q8 else 0)
     else:
         out_g1 = R * 2 * p.I * 2
     return dict(flops=flops, bytes=w13_b + w2_b + x_b + y_b + logits_b,
@@ -325,6 +336,12 @@ def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.
         sub_ids = ids_np[toks]
         sel = torch.tensor(held[experts], device=d.x.device)
         x = bits16(d.x[:T])
+        if p.wdtype == "mxfp8":  # (no expert map: every expert is held)
+            t0 = time.perf_counter()
+            oracle.fused_experts_mx(x, bits8(d.w13q[sel]), d.w13s[sel].cpu().numpy(), bits8(d.w2q[sel]),
+                                    d.w2s[sel].cpu().numpy(), remap[sub_ids], w_np[toks],
+                                    on_input=p.apply_router_weight_on_input)
+            return time.perf_counter() - t0, int((held[ids_np[toks]] >= 0).sum())
         if p.wdtype == "fp8":
             args = (x, bits8(d.w13q[sel]), d.w13s[sel].cpu().numpy(), bits8(d.w2q[sel]),
                     d.w2s[sel].cpu().numpy(), sub_ids, w_np[toks])
@@ -449,7 +466,7 @@ def main():
     alg = algorithmic(p, touched, st.act_fused, items)
     tflops = alg["flops"] / (ms * 1e-3) / 1e12
     tok_s = p.M / (ms * 1e-3)
-    dt = "fp8" if p.wdtype == "fp8" else "bf16"
+    dt = "fp8" if p.wdtype in ("fp8", "mxfp8") else "bf16"
     g1_s = stage_ms["gemm1"] * 1e-3
     t_mfma = alg_stage["flops_g1"] / (PEAK_TFLOPS[dt] * 1e12)
     t_hbm = alg_stage["bytes_g1"] / (PEAK_HBM_GBS * 1e9)
@@ -470,7 +487,8 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s",
         "tokens_per_s": round(tok_s, 1), "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8" if p.wdtype == "mxfp8" else dt,
+        "data": "synthetic",
         "config": {"workload": args.workload, "M": p.M, "H": p.H, "I": p.I, "E": p.E,
                    "topk": p.topk, "block_m": p.block_m, "weights": p.wdtype,
                    "weight_layout": st.layout,

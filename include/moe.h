@@ -35,7 +35,8 @@ typedef enum {
     MOE_E_INVALID = 1,     /* null pointer, negative size, topk outside [1, min(E, 32)]
                               (E: num_global_experts when it is set) */
     MOE_E_UNSUPPORTED = 2, /* E > 256, H or I not a multiple of 128, unknown block_m,
-                              dtype or weight layout, fp8 with block_m 16 or 256, the
+                              dtype or weight layout, fp8 with block_m 16 or 256, MXFP8
+                              other than block_m 128 with H, I >= 256, the
                               tiled layout other than bf16 with block_m 16, 128 or 256,
                               more than 2^31 routed rows, one expert's w13 of 2 GiB
                               or more */
@@ -45,8 +46,14 @@ typedef enum {
 
 typedef enum {
     MOE_W_BF16 = 0,              /* bf16 weights, bf16 activations, fp32 accumulate */
-    MOE_W_FP8_E4M3_BLOCK128 = 1  /* e4m3 weights with one fp32 scale per 128x128 block;
+    MOE_W_FP8_E4M3_BLOCK128 = 1, /* e4m3 weights with one fp32 scale per 128x128 block;
                                     activations quantised per token per 128 columns */
+    MOE_W_MXFP8 = 2              /* MXFP8 ("DeepGEMM FusedMoE on Blackwell", MXFP8 1x32):
+                                    e4m3 weights and activations, one E8M0 scale (2^(c-127))
+                                    per 32 K values, the smallest power of two s with
+                                    amax <= 448 s; z is requantised the same way. Weight
+                                    scales as packed words from moe_pack_mx_scales;
+                                    block_m 128 with H, I >= 256 */
 } moe_wdtype_t;
 
 /*
@@ -201,6 +208,29 @@ moe_status_t moe_align_block_size_ep(const int32_t *topk_ids, int64_t M, int32_t
 moe_status_t moe_quant_fp8_groups(const void *x, int64_t rows, int32_t cols, void *q,
                                   float *scale, void *stream);
 
+/*
+ * MXFP8 activations ("DeepGEMM FusedMoE on Blackwell", MXFP8 1x32, dynamic
+ * activations): per row, each 32 columns share one E8M0 scale code c (the
+ * smallest power of two s = 2^(c-127) with amax <= 448 s; 0 for an all-zero
+ * block) and the codes are e4m3(v / s), round to nearest even.
+ *   x [rows, cols] bf16; q [rows, cols] e4m3 out; scale [rows, cols / 32] uint8 out
+ * cols must be a multiple of 128.
+ */
+moe_status_t moe_quant_mx_groups(const void *x, int64_t rows, int32_t cols, void *q, void *scale,
+                                 void *stream);
+
+/*
+ * MXFP8 weight scales into the order the kernels read ("DeepGEMM FusedMoE on
+ * Blackwell", 2.8 (c): scales are post-processed after loading into the
+ * kernel's packed, MN-major layout, four E8M0 exponents to a 32-bit word):
+ *   which = 1: scale [E, 2I, H/32] uint8 -> scale_packed [E, H/128, 2I] uint32
+ *   which = 2: scale [E, H, I/32]  uint8 -> scale_packed [E, I/128, H]  uint32
+ * byte b of word (e, j, n) holds the scale of K block 4 j + b of row n.
+ * Requires p->wdtype == MOE_W_MXFP8; buffers 4-byte aligned and distinct.
+ */
+moe_status_t moe_pack_mx_scales(const moe_problem_t *p, int32_t which, const void *scale,
+                                void *scale_packed, void *stream);
+
 /* Host-only, pure: bytes of device workspace fused_experts needs for `p`
  * (0 when M == 0). */
 size_t moe_workspace_bytes(const moe_problem_t *p);
@@ -214,7 +244,9 @@ size_t moe_workspace_bytes(const moe_problem_t *p);
  *   x             [M, H] bf16
  *   w13           [E, 2I, H] bf16 or e4m3 (per p->wdtype); rows [0, I) gate,
  *                 [I, 2I) up
- *   w13_scale     [E, 2I/128, H/128] fp32 for fp8 (NULL is MOE_E_INVALID), ignored for bf16
+ *   w13_scale     [E, 2I/128, H/128] fp32 for fp8 (NULL is MOE_E_INVALID), ignored for bf16;
+ *                 for MXFP8 the packed words [E, H/128, 2I] uint32 of moe_pack_mx_scales
+ *                 (w2_scale: [E, I/128, H]), passed through the same pointer
  *   w2            [E, H, I] bf16 or e4m3
  *   w2_scale      [E, H/128, I/128] fp32 for fp8 (NULL is MOE_E_INVALID), ignored for bf16
  *                 (w13 and w2 in the element order p->weight_layout names)
@@ -361,7 +393,9 @@ moe_status_t moe_expert_gemm_act(const moe_problem_t *p, const void *x, const fl
  * The fp8 GEMM1 activation scales in the expert-sorted row order
  * ("DeepGEMM FusedMoE on Blackwell", 2.5 and 2.6.2: the per-token group
  * scales travel with the permuted rows, stored column-major for the GEMM):
- *   scale  [M, H/128] fp32, as from moe_quant_fp8_groups(x)
+ *   scale  [M, H/128] fp32, as from moe_quant_fp8_groups(x); for MXFP8 the
+ *          [M, H/32] E8M0 bytes of moe_quant_mx_groups, read as [M, H/128]
+ *          32-bit words (moved as bit patterns)
  *   out    [H/128, cap] fp32 out: out[g * cap + pos] = scale[sorted_token_ids[pos] / topk, g]
  *          for pos < num_tokens_post_padded, 0 at padding positions; later
  *          positions are not written

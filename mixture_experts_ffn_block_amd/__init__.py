@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
-MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128 = 0, 1
+MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8 = 0, 1, 2
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
 
@@ -27,7 +27,7 @@ EXPORTS = ("moe_topk", "moe_topk_grouped", "moe_align_capacity", "moe_align_bloc
            "moe_expert_gemm", "moe_silu_and_mul",
            "moe_expert_gemm_act_supported", "moe_expert_gemm_act", "moe_permute_scales",
            "moe_unpermute_reduce", "moe_pack_weights", "moe_batched_workspace_bytes",
-           "moe_batched_experts", "moe_status_string")
+           "moe_batched_experts", "moe_quant_mx_groups", "moe_pack_mx_scales", "moe_status_string")
 
 
 class MoeProblem(ctypes.Structure):
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_gemm_act.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_unpermute_reduce.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_pack_weights.argtypes = [PP, _I32, _P, _P, _P]
+        L.moe_quant_mx_groups.argtypes = [_P, _I64, _I32, _P, _P, _P]
+        L.moe_pack_mx_scales.argtypes = [PP, _I32, _P, _P, _P]
         L.moe_batched_workspace_bytes.argtypes = [PP]
         L.moe_batched_workspace_bytes.restype = ctypes.c_size_t
         L.moe_batched_experts.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -89,7 +91,7 @@ def lib() -> ctypes.CDLL:
                      "moe_quant_fp8_groups", "fused_experts", "fused_experts_ep",
                      "moe_expert_gemm", "moe_silu_and_mul", "moe_permute_scales",
                      "moe_expert_gemm_act", "moe_unpermute_reduce", "moe_pack_weights",
-                     "moe_batched_experts"):
+                     "moe_batched_experts", "moe_quant_mx_groups", "moe_pack_mx_scales"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -259,22 +261,25 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
         _need(expert_map, torch.int32, "expert_map")
     _need(x, torch.bfloat16, "x")
     fp8 = w13.dtype == torch.float8_e4m3fn
+    # e4m3 weights: fp32 128x128 block scales, or packed MX words (int32) from moe_pack_mx_scales
+    mx = fp8 and w13_scale is not None and w13_scale.dtype == torch.int32
     wdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
     _need(w13, wdt, "w13")
     _need(w2, wdt, "w2")
     _need(topk_ids, torch.int32, "topk_ids")
     _need(topk_weights, torch.float32, "topk_weights")
     if fp8:
-        _need(w13_scale, torch.float32, "w13_scale")
-        _need(w2_scale, torch.float32, "w2_scale")
+        _need(w13_scale, torch.int32 if mx else torch.float32, "w13_scale")
+        _need(w2_scale, torch.int32 if mx else torch.float32, "w2_scale")
     M, H = x.shape
     E, N2, H2 = w13.shape
     if H2 != H or tuple(w2.shape) != (E, H, N2 // 2) or topk_ids.shape != topk_weights.shape \
             or topk_ids.shape[0] != M:
         raise ValueError("fused_experts: inconsistent shapes")
     p = make_problem(M, H, N2 // 2, E, topk_ids.shape[1], block_m,
-                     MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16, apply_router_weight_on_input,
-                     weight_layout, 0 if expert_map is None else expert_map.numel(), chunk_tokens)
+                     MOE_W_MXFP8 if mx else MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16,
+                     apply_router_weight_on_input, weight_layout,
+                     0 if expert_map is None else expert_map.numel(), chunk_tokens)
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
@@ -304,7 +309,8 @@ def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
 
     workspace (from gemm_workspace_for) enables the split-K tail of the second GEMM, as
     fused_experts runs it."""
-    fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128
+    fp8 = p.wdtype in (MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8)
+    mx = p.wdtype == MOE_W_MXFP8   # scales: packed E8M0 words (int32) instead of fp32
     cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
     N, K = (2 * p.I, p.H) if which == 1 else (p.H, p.I)
     _need_size(a, _F8 if fp8 else _BF, (p.M if which == 1 else cap) * K, "a")
@@ -315,8 +321,8 @@ def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
     if which == 1:
         _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
     if fp8:
-        _need_size(a_scale, _F32, (K // 128) * cap, "a_scale [K/128, cap]")
-        _need_size(w_scale, _F32, p.E * (N // 128) * (K // 128), "w_scale")
+        _need_size(a_scale, _I32T if mx else _F32, (K // 128) * cap, "a_scale [K/128, cap]")
+        _need_size(w_scale, _I32T if mx else _F32, p.E * (N if mx else N // 128) * (K // 128), "w_scale")
     _check(lib().moe_expert_gemm(ctypes.byref(p), which, _ptr(a), _ptr(a_scale), _ptr(w),
                                  _ptr(w_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
                                  _ptr(num_tokens_post_padded), _ptr(c), _ptr(workspace),
@@ -363,7 +369,8 @@ def moe_expert_gemm_act(p: MoeProblem, x: torch.Tensor, x_scale: torch.Tensor | 
 
     bf16 weights (block_m 128 or 256): z [cap, I] bf16, the scales are unused.
     fp8 weights (block_m 128): z [cap, I] e4m3 with z_scale [I/128, cap]."""
-    fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128
+    fp8 = p.wdtype in (MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8)
+    mx = p.wdtype == MOE_W_MXFP8
     cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
     _need_size(x, _F8 if fp8 else _BF, p.M * p.H, "x")
     _need_size(w13, _F8 if fp8 else _BF, p.E * 2 * p.I * p.H, "w13")
@@ -373,9 +380,10 @@ def moe_expert_gemm_act(p: MoeProblem, x: torch.Tensor, x_scale: torch.Tensor | 
     _need_size(topk_weights, _F32, p.M * p.topk, "topk_weights")
     _need_size(z, _F8 if fp8 else _BF, cap * p.I, "z")
     if fp8:
-        _need_size(x_scale, _F32, (p.H // 128) * cap, "x_scale [H/128, cap]")
-        _need_size(w13_scale, _F32, p.E * (2 * p.I // 128) * (p.H // 128), "w13_scale")
-        _need_size(z_scale, _F32, (p.I // 128) * cap, "z_scale [I/128, cap]")
+        sd = _I32T if mx else _F32
+        _need_size(x_scale, sd, (p.H // 128) * cap, "x_scale [H/128, cap]")
+        _need_size(w13_scale, sd, p.E * (2 * p.I if mx else 2 * p.I // 128) * (p.H // 128), "w13_scale")
+        _need_size(z_scale, sd, (p.I // 128) * cap, "z_scale [I/128, cap]")
     _check(lib().moe_expert_gemm_act(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(w13),
                                      _ptr(w13_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
                                      _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(z),
@@ -385,12 +393,13 @@ def moe_expert_gemm_act(p: MoeProblem, x: torch.Tensor, x_scale: torch.Tensor | 
 
 def moe_permute_scales(p: MoeProblem, scale: torch.Tensor, sorted_token_ids: torch.Tensor,
                        num_tokens_post_padded: torch.Tensor, out: torch.Tensor, stream=None):
-    """Per-token fp8 group scales [M, H/128] -> group-major, sorted-order [H/128, cap]."""
+    """Per-token fp8 group scales [M, H/128] -> group-major, sorted-order [H/128, cap]; MXFP8:
+    the [M, H/32] E8M0 bytes as [M, H/128] int32 words (4 blocks each), moved the same way."""
     cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
-    _need_size(scale, _F32, p.M * (p.H // 128), "scale")
+    _need_size(scale, (torch.float32, torch.int32), p.M * (p.H // 128), "scale")
     _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
     _need_size(num_tokens_post_padded, _I32T, 1, "num_tokens_post_padded")
-    _need_size(out, _F32, (p.H // 128) * cap, "out [H/128, cap]")
+    _need_size(out, (torch.float32, torch.int32), (p.H // 128) * cap, "out [H/128, cap]")
     _check(lib().moe_permute_scales(ctypes.byref(p), _ptr(scale), _ptr(sorted_token_ids),
                                     _ptr(num_tokens_post_padded), _ptr(out), _stream(stream)),
            "moe_permute_scales")
@@ -461,3 +470,24 @@ def moe_batched_experts(a: torch.Tensor, expert_num_tokens: torch.Tensor, w13: t
 
 def moe_batched_workspace_bytes(p: MoeProblem) -> int:
     return int(lib().moe_batched_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_quant_mx_groups(x: torch.Tensor, stream=None):
+    """MXFP8 quantisation per 32 columns -> (q e4m3 [rows, cols], scale uint8 E8M0 [rows, cols/32])."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=x.device)
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quant_mx_groups(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream(stream)),
+           "moe_quant_mx_groups")
+    return q, s
+
+
+def moe_pack_mx_scales(p: MoeProblem, which: int, scale: torch.Tensor, stream=None) -> torch.Tensor:
+    """MXFP8 weight scales [E, N, K/32] uint8 -> packed words [E, K/128, N] int32."""
+    N, K = (2 * p.I, p.H) if which == 1 else (p.H, p.I)
+    _need_size(scale, (torch.uint8,), p.E * N * (K // 32), "scale")
+    out = torch.empty((p.E, K // 128, N), dtype=torch.int32, device=scale.device)
+    _check(lib().moe_pack_mx_scales(ctypes.byref(p), which, _ptr(scale), _ptr(out), _stream(stream)),
+           "moe_pack_mx_scales")
+    return out

@@ -16,6 +16,10 @@
 namespace {
 
 constexpr int64_t kAlign = 256;
+
+// 8-bit recipes: fp8 with 128x128 block scales, or MXFP8 with E8M0 scales per 32
+bool q8(const moe_problem_t& p) { return p.wdtype == MOE_W_FP8_E4M3_BLOCK128 || p.wdtype == MOE_W_MXFP8; }
+bool is_mx(const moe_problem_t& p) { return p.wdtype == MOE_W_MXFP8; }
 constexpr int kMaxE = 256;
 constexpr int kMaxTopk = 32;
 constexpr int kGroupM = 32;  // blocks per tile-scheduling window (groups never span two experts)
@@ -70,7 +74,7 @@ Layout layout(const moe_problem_t& p, const Rows& rows) {
     Layout L{};
     L.R = rows.R;
     L.cap = rows.cap;
-    const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    const bool fp8 = q8(p);  // MX scale bytes take the same room as the fp32 scales
     int64_t off = 0;
     auto take = [&](int64_t bytes) { const int64_t o = off; off += up(bytes); return o; };
     L.sorted = take(L.cap * 4);
@@ -102,16 +106,19 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->topk > e_route || p->topk > kMaxTopk) return MOE_E_INVALID;
     if (p->E > kMaxE || p->H % 128 || p->I % 128) return MOE_E_UNSUPPORTED;
     if (!block_m_ok(p->block_m)) return MOE_E_UNSUPPORTED;
-    if (p->wdtype != MOE_W_BF16 && p->wdtype != MOE_W_FP8_E4M3_BLOCK128) return MOE_E_UNSUPPORTED;
+    if (p->wdtype != MOE_W_BF16 && p->wdtype != MOE_W_FP8_E4M3_BLOCK128 && p->wdtype != MOE_W_MXFP8)
+        return MOE_E_UNSUPPORTED;
     if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && (p->block_m == 16 || p->block_m == 256))
         return MOE_E_UNSUPPORTED;
+    // MXFP8 runs on the persistent 128-row kernel, which takes K >= 256 in both GEMMs
+    if (p->wdtype == MOE_W_MXFP8 && (p->block_m != 128 || p->H < 256 || p->I < 256)) return MOE_E_UNSUPPORTED;
     if (p->weight_layout != MOE_LAYOUT_ROWS && p->weight_layout != MOE_LAYOUT_TILED)
         return MOE_E_UNSUPPORTED;
     if (p->weight_layout == MOE_LAYOUT_TILED &&
         (p->wdtype != MOE_W_BF16 || (p->block_m != 16 && p->block_m != 128 && p->block_m != 256)))
         return MOE_E_UNSUPPORTED;
     // one expert's weight matrix is addressed with 32-bit byte offsets
-    const int64_t esz = p->wdtype == MOE_W_FP8_E4M3_BLOCK128 ? 1 : 2;
+    const int64_t esz = q8(*p) ? 1 : 2;
     if (int64_t(2) * p->I * p->H * esz >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
     // positions and routed items are int32 on the device
     if (p->M * p->topk >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
@@ -130,7 +137,7 @@ hipError_t gemm_stage(const moe_problem_t& p, const Rows& rows, int which, const
                       const float* a_scale, const void* w, const float* w_scale,
                       const int32_t* sorted, const int32_t* expert_ids, const int32_t* npp,
                       void* c, void* split_ws, hipStream_t s) {
-    const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    const bool fp8 = q8(p);
     const int esz = fp8 ? 1 : 2;  // bytes per weight / activation element
     const int64_t cap = rows.cap;
     const int N = which == 1 ? 2 * p.I : p.H;
@@ -157,8 +164,10 @@ hipError_t gemm_stage(const moe_problem_t& p, const Rows& rows, int which, const
         g.a_scale = a_scale;
         g.a_scale_ld = cap;
         g.w_scale = w_scale;
-        g.w_scale_expert = static_cast<int64_t>(N / 128) * (K / 128);
+        // fp32 blocks [N/128, K/128] per expert, or MX words [K/128, N]
+        g.w_scale_expert = static_cast<int64_t>(is_mx(p) ? N : N / 128) * (K / 128);
         g.scale_groups = K / 128;
+        g.mx = is_mx(p) ? 1 : 0;
     }
     if (which == 2 && split_ws != nullptr && split_bytes(p) > 0) {
         g.part = static_cast<float*>(split_ws);
@@ -174,14 +183,14 @@ hipError_t gemm_stage(const moe_problem_t& p, const Rows& rows, int which, const
 
 // GEMM1 with SiLU-and-mul in its epilogue: z[pos] = act(x[token(pos)] w13[e]^T)
 bool act_fused(const moe_problem_t& p) {
-    return gemm_act_supported(p.block_m, p.wdtype == MOE_W_FP8_E4M3_BLOCK128, p.H);
+    return gemm_act_supported(p.block_m, q8(p), p.H);
 }
 
 hipError_t gemm_act_stage(const moe_problem_t& p, const Rows& rows, const void* a,
                           const float* a_scale, const void* w13, const float* w13_scale,
                           const int32_t* sorted, const int32_t* expert_ids, const int32_t* npp,
                           const float* weights, void* z, float* z_scale, hipStream_t s) {
-    const bool fp8 = p.wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    const bool fp8 = q8(p);
     const int esz = fp8 ? 1 : 2;
     const int64_t cap = rows.cap;
     GemmArgs g{};
@@ -209,10 +218,11 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const Rows& rows, const void* 
         g.a_scale = a_scale;
         g.a_scale_ld = cap;
         g.w_scale = w13_scale;
-        g.w_scale_expert = static_cast<int64_t>(2 * p.I / 128) * (p.H / 128);
+        g.w_scale_expert = static_cast<int64_t>(is_mx(p) ? 2 * p.I : 2 * p.I / 128) * (p.H / 128);
         g.scale_groups = p.H / 128;
         g.z_scale = z_scale;
         g.z_scale_ld = cap;
+        g.mx = is_mx(p) ? 1 : 0;
     }
     return p.block_m == 16 ? launch_stream_gemm(g, s) : launch_grouped_gemm(g, p.block_m, fp8, s);
 }
@@ -342,6 +352,16 @@ moe_status_t moe_quant_fp8_groups(const void* x, int64_t rows, int32_t cols, voi
                                        static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_quant_mx_groups(const void* x, int64_t rows, int32_t cols, void* q, void* scale,
+                                 void* stream) {
+    if (rows < 0 || cols <= 0) return MOE_E_INVALID;
+    if (cols % 128) return MOE_E_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!x || !q || !scale) return MOE_E_INVALID;
+    return hip_status(launch_quant_mxfp8(static_cast<const bf16_t*>(x), rows, cols, static_cast<uint8_t*>(q),
+                                         static_cast<uint8_t*>(scale), static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_workspace_bytes(const moe_problem_t* p) {
     if (check_problem(p) != MOE_OK || p->M == 0) return 0;
     const moe_problem_t q = chunk_problem(*p, chunk_of(*p));
@@ -361,7 +381,7 @@ moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* 
                        void* workspace, size_t workspace_bytes, void* stream,
                        bool unweighted = false) {
     if (p->M == 0) return MOE_OK;
-    const bool fp8 = p->wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    const bool fp8 = q8(*p);
     if (!x || !w13 || !w2 || !topk_ids || !y || (!topk_weights && !unweighted)) return MOE_E_INVALID;
     if (fp8 && (!w13_scale || !w2_scale)) return MOE_E_INVALID;
     const Rows rows = routed_rows(*p);
@@ -383,8 +403,9 @@ moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* 
     const void* a1 = x;
     const float* a1_scale = nullptr;
     if (fp8) {
-        err = launch_quant_fp8(static_cast<const bf16_t*>(x), M, H, ws + L.xq,
-                               reinterpret_cast<float*>(ws + L.xs), s);
+        err = is_mx(*p) ? launch_quant_mxfp8(static_cast<const bf16_t*>(x), M, H, ws + L.xq, ws + L.xs, s)
+                        : launch_quant_fp8(static_cast<const bf16_t*>(x), M, H, ws + L.xq,
+                                           reinterpret_cast<float*>(ws + L.xs), s);
         if (err != hipSuccess) return MOE_E_HIP;
         a1 = ws + L.xq;
         a1_scale = reinterpret_cast<const float*>(ws + L.xst);
@@ -526,7 +547,7 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, int32_t which, const void* 
     if (st != MOE_OK) return st;
     if (which != 1 && which != 2) return MOE_E_INVALID;
     if (p->M == 0) return MOE_OK;
-    const bool fp8 = p->wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    const bool fp8 = q8(*p);
     if (!a || !w || !expert_ids || !num_tokens_post_padded || !c) return MOE_E_INVALID;
     if (which == 1 && !sorted_token_ids) return MOE_E_INVALID;
     if (fp8 && (!a_scale || !w_scale)) return MOE_E_INVALID;
@@ -548,7 +569,7 @@ moe_status_t moe_expert_gemm_act(const moe_problem_t* p, const void* x, const fl
     if (st != MOE_OK) return st;
     if (!act_fused(*p)) return MOE_E_UNSUPPORTED;
     if (p->M == 0) return MOE_OK;
-    const bool fp8 = p->wdtype == MOE_W_FP8_E4M3_BLOCK128;
+    const bool fp8 = q8(*p);
     if (!x || !w13 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !topk_weights || !z)
         return MOE_E_INVALID;
     if (fp8 && (!x_scale || !w13_scale || !z_scale)) return MOE_E_INVALID;
@@ -566,6 +587,7 @@ moe_status_t moe_silu_and_mul(const moe_problem_t* p, const void* h,
     if (p->M == 0) return MOE_OK;
     if (!h || !sorted_token_ids || !topk_weights || !num_tokens_post_padded || !z)
         return MOE_E_INVALID;
+    if (is_mx(*p)) return MOE_E_UNSUPPORTED;  // MXFP8 quantises z in GEMM1's epilogue only
     if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && !z_scale) return MOE_E_INVALID;
     return hip_status(act_stage(*p, routed_rows(*p), h, sorted_token_ids, topk_weights, num_tokens_post_padded, z,
                                 z_scale, static_cast<hipStream_t>(stream)));
@@ -596,6 +618,20 @@ moe_status_t moe_pack_weights(const moe_problem_t* p, int32_t which, const void*
     if (a % 16 || b % 16) return MOE_E_INVALID;
     return hip_status(launch_pack_tiled(static_cast<const bf16_t*>(w), static_cast<bf16_t*>(w_packed),
                                          p->E, N, K, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_pack_mx_scales(const moe_problem_t* p, int32_t which, const void* scale,
+                                void* scale_packed, void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (which != 1 && which != 2) return MOE_E_INVALID;
+    if (!is_mx(*p)) return MOE_E_UNSUPPORTED;
+    if (!scale || !scale_packed || scale == scale_packed) return MOE_E_INVALID;
+    if (reinterpret_cast<uintptr_t>(scale) % 4 || reinterpret_cast<uintptr_t>(scale_packed) % 4)
+        return MOE_E_INVALID;
+    const int N = which == 1 ? 2 * p->I : p->H, K = which == 1 ? p->H : p->I;
+    return hip_status(launch_pack_mx_scales(static_cast<const uint8_t*>(scale), static_cast<uint32_t*>(scale_packed),
+                                            p->E, N, K, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_unpermute_reduce(const moe_problem_t* p, const void* o, const int32_t* inv_perm,

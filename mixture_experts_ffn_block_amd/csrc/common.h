@@ -45,6 +45,19 @@ __device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float 
     return static_cast<uint32_t>(both);
 }
 
+// E8M0 code of the MX block scale: the smallest s = 2^e with a <= fmax * s, code
+// e + 127 within [0, 254]; 0 for an all-zero block ("DeepGEMM FusedMoE on
+// Blackwell", MXFP8 1x32 and the UE8M0 scale format). fmax * 2^e is exact in
+// fp32 (or overflows to inf), so the comparisons decide exactly.
+__device__ __forceinline__ uint32_t mx_scale_code(float a, float fmax) {
+    if (!(a > 0.0f)) return 0;
+    int e = 0;
+    frexpf(a / fmax, &e);  // a / fmax lies in about [2^(e-1), 2^e): the answer is near e
+    while (e > -127 && a <= ldexpf(fmax, e - 1)) --e;
+    while (e < 127 && a > ldexpf(fmax, e)) ++e;
+    return static_cast<uint32_t>(e + 127);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

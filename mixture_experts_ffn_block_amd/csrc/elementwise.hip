@@ -118,6 +118,49 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict
     *reinterpret_cast<u32x2_t*>(q + row * cols + c0) = qq;
 }
 
+// MXFP8 activations ("DeepGEMM FusedMoE on Blackwell", MXFP8 1x32): each 32
+// columns of a row share one E8M0 scale, the smallest power of two s with
+// amax <= 448 s; codes E4M3(v / s). Four lanes hold a block (8 values each).
+__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const bf16_t* __restrict__ x,
+                                                          uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ scale, int cols) {
+    const int64_t row = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512 + lane * 8;
+    if (c0 >= cols) return;  // cols is a multiple of 128: whole blocks only
+    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + row * cols + c0);
+    float v[8], m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(xv[j] << 16);
+        v[2 * j + 1] = __uint_as_float(xv[j] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const uint32_t code = mx_scale_code(m, 448.0f);
+    const float inv = ldexpf(1.0f, 127 - static_cast<int>(code));
+    float c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = fminf(fmaxf(v[j] * inv, -448.0f), 448.0f);
+    *reinterpret_cast<u32x2_t*>(q + row * cols + c0) =
+        u32x2_t{cvt_e4m3x4(c[0], c[1], c[2], c[3]), cvt_e4m3x4(c[4], c[5], c[6], c[7])};
+    if ((lane & 3) == 0) scale[row * (cols / 32) + c0 / 32] = static_cast<uint8_t>(code);
+}
+
+// MX weight scales into the kernels' order: natural [E, N, K/32] bytes ->
+// [E, K/128, N] words, byte b of word (e, j, n) holding block 4 j + b of row n.
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint32_t* __restrict__ s,
+                                                             uint32_t* __restrict__ out, int64_t words,
+                                                             int N, int KW) {
+    for (int64_t d = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; d < words;
+         d += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t n = d % N, j = (d / N) % KW, e = d / (static_cast<int64_t>(N) * KW);
+        out[d] = s[(e * N + n) * KW + j];
+    }
+}
+
 // Activation scales of GEMM1 in its row order: out[g * cap + pos] is the
 // scale of the token of sorted position pos (0 for padding positions), from
 // the per-token scales scale[token, g]. Positions >= npp are not written.
@@ -222,6 +265,22 @@ hipError_t launch_quant_fp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q,
                             hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(ceil_div(cols, 2048)), static_cast<unsigned>(rows));
     hipLaunchKernelGGL(quant_fp8_kernel, grid, dim3(256), 0, stream, x, q, scale, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_mxfp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* scale,
+                              hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(cols, 2048)), static_cast<unsigned>(rows));
+    hipLaunchKernelGGL(quant_mxfp8_kernel, grid, dim3(256), 0, stream, x, q, scale, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_mx_scales(const uint8_t* s, uint32_t* out, int64_t E, int N, int K, hipStream_t stream) {
+    const int64_t words = E * N * (K / 128);
+    const int64_t blocks = ceil_div(words, 256);
+    const dim3 grid(static_cast<unsigned>(blocks < 65536 ? blocks : 65536));
+    hipLaunchKernelGGL(pack_mx_scales_kernel, grid, dim3(256), 0, stream, reinterpret_cast<const uint32_t*>(s),
+                       out, words, N, K / 128);
     return hipGetLastError();
 }
 

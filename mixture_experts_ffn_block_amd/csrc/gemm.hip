@@ -869,7 +869,15 @@ __device__ __forceinline__ void copy1_dword(const void* g, uint32_t lds) {
 
 }  // namespace f8
 
-template <class C, bool GATHER, bool ACT>
+// MX (MXFP8, "DeepGEMM FusedMoE on Blackwell", MXFP8 1x32): activations and weights
+// carry one E8M0 scale per 32 K values, which the scaled MFMA applies per lane (a
+// lane's 32 K bytes of an operand are exactly one such block), so the stage sums go
+// straight into the accumulators. The scales arrive packed four to a word
+// (blocks 4 kt .. 4 kt + 3 of a row), MN-major: the activations' [K/128, cap] by
+// sorted position, the weights' [E, K/128, N]; a stage copies 128 and 256 words.
+// The SiLU epilogue quantises z per 32 columns (one wave's slice of a 128-column
+// block) to E4M3 with an E8M0 scale byte.
+template <class C, bool GATHER, bool ACT, bool MX>
 __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p) {
     static_assert(!ACT || GATHER, "the SiLU epilogue belongs to GEMM1");
     constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES, TM = C::TM, TN = C::TN;
@@ -943,6 +951,13 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         }
         if (wave == 0) {
             sc_src = p.a_scale + m0 + (lane & 31) * 4;
+        } else if constexpr (MX) {
+            // 256 weight-row scale words of K block 0: lane l takes 4 of them. ACT:
+            // lanes 0-31 the gate rows n0.., lanes 32-63 the up rows N + n0..; else
+            // rows n0 + 4 l (clamped: rows past N are never stored)
+            const int nw = ACT ? 2 * p.N : p.N;
+            const int r0 = ACT ? (lane >> 5) * p.N + n0 + (lane & 31) * 4 : min(n0 + lane * 4, nw - 4);
+            sc_src = p.w_scale + static_cast<int64_t>(e) * p.w_scale_expert + r0;
         } else {
             // lane b < WBLOCKS: weight-block row n0/128 + b (rows past N repeat the
             // last); ACT: lane 0 the gate block, lane 1 the up block
@@ -988,6 +1003,8 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         }
         if (wave == 0)
             f8::copy1(sc_src + static_cast<int64_t>(kt) * p.a_scale_ld, lds_base + st + C::SCALE_OFF);
+        else if (wave == 1 && MX)
+            f8::copy1(sc_src + static_cast<int64_t>(kt) * (ACT ? 2 * p.N : p.N), lds_base + st + C::WSCALE_OFF);
         else if (wave == 1)
             f8::copy1_dword(sc_src + kt, lds_base + st + C::WSCALE_OFF);
     };
@@ -1009,10 +1026,14 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         i32x8_t a[TM], b[TN];
     };
     auto stage_ptr = [&](int g) { return smem + (g % STAGES) * (C::STAGE_BYTES / 16); };
-    // lane (r32, half) holds 32 consecutive bytes of K: chunks 4ks + 2half, +1
+    // lane (r32, half) holds K chunks 4ks + half and 4ks + 2 + half (16 bytes each):
+    // the matrix core reads a lane's first four registers as K [16 half, +16) of the
+    // 64-wide step and the last four as K [32 + 16 half, +16), and scales K [0, 32)
+    // and [32, 64) with the scale bytes of lanes of half 0 and half 1; so this order
+    // makes each hardware scale block one 32-wide block of K in memory
     auto frag = [&](const u32x4_t* base, int row, int ks) {
-        const u32x4_t lo = base[C::swz(row, 4 * ks + 2 * half)];
-        const u32x4_t hi = base[C::swz(row, 4 * ks + 2 * half + 1)];
+        const u32x4_t lo = base[C::swz(row, 4 * ks + half)];
+        const u32x4_t hi = base[C::swz(row, 4 * ks + 2 + half)];
         return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
@@ -1031,6 +1052,28 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
             for (int tm = 0; tm < TM; ++tm)
                 part[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     f.b[tn], f.a[tm], first ? f32x16_t{} : part[tn][tm], 0, 0, 0, 127, 0, 127);
+    };
+    // MX: each lane's E8M0 bytes (K block 4 kt + 2 ks + half) of its activation row
+    // and its weight row; the MFMA scales the products, the sums accumulate directly.
+    // ACT weight tile row r is gate row (r / 64) * 32 + r % 32 (r / 32 even) or that
+    // up row, whose words sit at [0, 128) and [128, 256) of the stage's scales.
+    auto mma_mx = [&](const Frag& f, int g, int ks) {
+        const uint32_t* sa = reinterpret_cast<const uint32_t*>(stage_ptr(g) + C::SCALE_OFF / 16);
+        const uint32_t* sw = reinterpret_cast<const uint32_t*>(stage_ptr(g) + C::WSCALE_OFF / 16);
+        const int shift = 8 * (2 * ks + half);
+        int asc[TM];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) asc[tm] = static_cast<int>((sa[arow + tm * 32 + r32] >> shift) & 0xffu);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int r = brow + tn * 32 + r32;
+            const int wi = ACT ? ((r >> 5) & 1) * 128 + (r >> 6) * 32 + (r & 31) : r;
+            const int bsc = static_cast<int>((sw[wi] >> shift) & 0xffu);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+                acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0, bsc, 0, asc[tm]);
+        }
     };
     // scale of tile row arow + tm*32 + r32 times the wave's weight-block scale
     // (ACT: column tile tn = 0 holds gate rows, tn = 1 up rows, each its own block)
@@ -1077,7 +1120,39 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         }
         // barriers that wait only for LDS traffic: the copies in flight stay in flight
         auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-        if constexpr (C::FP8_OUT) {
+        if constexpr (MX) {
+            // the row's 32 columns of this wave are one MX block: E8M0 scale byte wn of
+            // the row's word in z_scale [I/128, cap], codes E4M3(v / scale)
+            uint8_t* zsc = reinterpret_cast<uint8_t*>(p.z_scale);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const int rl = arow + tm * 32 + r32;
+                float m = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[tm][i]));
+                m = fmaxf(m, __shfl_xor(m, 32, 64));
+                const uint32_t code = mx_scale_code(m, 448.0f);
+                const float inv = ldexpf(1.0f, 127 - static_cast<int>(code));
+                if (half == 0) zsc[(static_cast<int64_t>(nb) * p.z_scale_ld + m0 + rl) * 4 + wn] = static_cast<uint8_t>(code);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float c4[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) c4[j] = fminf(fmaxf(v[tm][4 * q + j] * inv, -448.0f), 448.0f);
+                    *reinterpret_cast<uint32_t*>(ws + rl * ZP + wn * 32 + 8 * q + 4 * half) =
+                        cvt_e4m3x4(c4[0], c4[1], c4[2], c4[3]);
+                }
+            }
+            lds_barrier();
+            uint8_t* zc = reinterpret_cast<uint8_t*>(p.C);
+#pragma unroll
+            for (int pass = 0; pass < BM / (8 * C::NW); ++pass) {
+                const int rl = (pass * C::NW + wave) * 8 + lane / 8;
+                const u32x4_t z16 = *reinterpret_cast<const u32x4_t*>(ws + rl * ZP + (lane % 8) * 16);
+                __builtin_nontemporal_store(
+                    z16, reinterpret_cast<u32x4_t*>(zc + (m0 + rl) * p.ldc_bytes + nb * 128 + (lane % 8) * 16));
+            }
+        } else if constexpr (C::FP8_OUT) {
             lds_barrier();
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
@@ -1133,10 +1208,16 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         read(g, 0, f0);
         if (more) issue_a(gs);
         read(g, 1, f1);
-        mma(f0, true);
-        if (more) issue_rest(gs);
-        mma(f1, false);
-        fold(g);
+        if constexpr (MX) {
+            mma_mx(f0, g, 0);
+            if (more) issue_rest(gs);
+            mma_mx(f1, g, 1);
+        } else {
+            mma(f0, true);
+            if (more) issue_rest(gs);
+            mma(f1, false);
+            fold(g);
+        }
         if (++kt == KT) {
             kt = 0;
             int mb, nb;
@@ -1176,21 +1257,26 @@ int persistent_grid() {
     return cus[dev];
 }
 
-template <class C, bool GATHER, bool ACT>
+template <class C, bool GATHER, bool ACT, bool MX>
 hipError_t launch_fp8_as(const GemmArgs& a, hipStream_t stream) {
     const size_t lds = C::LDS_BYTES;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, GATHER, ACT>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, GATHER, ACT, MX>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (err != hipSuccess) return err;
     const dim3 grid(static_cast<unsigned>(persistent_grid()));
-    hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, GATHER, ACT>), grid, dim3(C::NW * 64), lds, stream, a);
+    hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, GATHER, ACT, MX>), grid, dim3(C::NW * 64), lds, stream, a);
     return hipGetLastError();
+}
+
+template <class C, bool MX>
+hipError_t launch_fp8_fmt(const GemmArgs& a, hipStream_t stream) {
+    if (a.act) return a.sorted ? launch_fp8_as<C, true, true, MX>(a, stream) : hipErrorInvalidValue;
+    return a.sorted ? launch_fp8_as<C, true, false, MX>(a, stream) : launch_fp8_as<C, false, false, MX>(a, stream);
 }
 
 template <class C>
 hipError_t launch_fp8(const GemmArgs& a, hipStream_t stream) {
-    if (a.act) return a.sorted ? launch_fp8_as<C, true, true>(a, stream) : hipErrorInvalidValue;
-    return a.sorted ? launch_fp8_as<C, true, false>(a, stream) : launch_fp8_as<C, false, false>(a, stream);
+    return a.mx ? launch_fp8_fmt<C, true>(a, stream) : launch_fp8_fmt<C, false>(a, stream);
 }
 
 template <class C, bool GATHER, bool ACT>

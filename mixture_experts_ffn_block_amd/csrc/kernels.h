@@ -45,6 +45,9 @@ struct GemmArgs {
     int* part_cnt;
     int part_slots;
     int n_cu;                  // workgroups of this kernel that run at once (one per CU)
+    // MX (E8M0 scale per 32 K values, packed four to a word): a_scale [K/128, a_scale_ld],
+    // w_scale [E, K/128, N_w] words (w_scale_expert words per expert), z_scale likewise
+    int mx;
     // W tiled: 16-row x 32-column tiles of 1 KB, row-major inside, ordered by row
     // block then column block (bf16; block_m 16, 128 and 256)
     int w_packed;
@@ -80,6 +83,9 @@ hipError_t launch_permute_scales(const float* scale, int groups, int topk, int R
                                  float* out, hipStream_t stream);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream);
 int concurrent_tiles();  // workgroups of the LDS-tiled GEMMs that run at once
+hipError_t launch_quant_mxfp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* scale,
+                              hipStream_t stream);  // scale [rows, cols / 32] E8M0
+hipError_t launch_pack_mx_scales(const uint8_t* s, uint32_t* out, int64_t E, int N, int K, hipStream_t stream);
 hipError_t launch_pack_tiled(const bf16_t* w, bf16_t* wp, int64_t E, int N, int K, hipStream_t stream);
 hipError_t launch_reduce(const bf16_t* o, const int32_t* inv_perm, const float* weights, int64_t M,
                          int k, int H, int use_weights, bf16_t* y, hipStream_t stream);
