@@ -91,14 +91,16 @@ class Step:
     def __init__(self, p: synth.Problem, d: synth.Inputs, layout: str = "auto", weights=None):
         import mixture_experts_ffn_block_amd as moe
         self.moe, self.p, self.d = moe, p, d
-        self.fp8 = p.wdtype in ("fp8", "mxfp8")   # 8-bit weights and activations
-        self.mx = p.wdtype == "mxfp8"              # E8M0 scales per 32 values
+        self.fp8 = p.wdtype in ("fp8", "mxfp8", "w4a8")  # 8-bit activations
+        self.mx = p.wdtype == "mxfp8"                     # E8M0 scales per 32 on both operands
+        self.w4 = p.wdtype == "w4a8"                      # E2M1 weights with E8M0 scales
         dev = d.x.device
         # an expert-parallel rank holds E / ep_size experts; ids stay global
         self.emap = d.expert_map
         G = p.E if self.emap is not None else 0
         M, H, I, E, k, B = p.M, p.H, p.I, len(p.local_experts), p.topk, p.block_m
-        wdt = moe.MOE_W_MXFP8 if self.mx else moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16
+        wdt = (moe.MOE_W_MXFP8 if self.mx else moe.MOE_W_W4A8_MXFP4 if self.w4
+               else moe.MOE_W_FP8_E4M3_BLOCK128 if self.fp8 else moe.MOE_W_BF16)
         rows = moe.make_problem(M, H, I, E, k, B, wdt, p.apply_router_weight_on_input)
         packable = not self.fp8 and B in (16, 128, 256)
         if layout == "tiled" and not packable:
@@ -133,7 +135,7 @@ class Step:
         self.w13 = d.w13q if self.fp8 else d.w13
         self.w2 = d.w2q if self.fp8 else d.w2
         self.w13s, self.w2s = d.w13s, d.w2s
-        if self.mx:  # weight-scale preparation, once, outside every timed region
+        if self.mx or self.w4:  # weight-scale preparation, once, outside every timed region
             self.w13s = moe.moe_pack_mx_scales(rows, 1, d.w13s)
             self.w2s = moe.moe_pack_mx_scales(rows, 2, d.w2s)
         if weights is not None:  # prepared by another Step of the same workload
@@ -285,11 +287,12 @@ def algorithmic(p: synth.Problem, touched: int, act_fused: bool = False, R: int 
     with the activation fused into GEMM1 that kernel writes z instead of h. R: the
     routed items computed here (all M * topk, or an expert-parallel rank's share)."""
     R = p.M * p.topk if R is None else R
-    q8 = p.wdtype in ("fp8", "mxfp8")
-    wb = 1 if q8 else 2
+    q8 = p.wdtype in ("fp8", "mxfp8", "w4a8")
+    ab = 1 if q8 else 2                            # activation bytes per value
+    wb = 0.5 if p.wdtype == "w4a8" else ab         # weight bytes per value
     # scale bytes per K value: fp32 per 128x128 block (weights) or per 128 (activations),
-    # or one E8M0 byte per 32 values (MX)
-    ws_per = 1.0 / 32 if p.wdtype == "mxfp8" else 4.0 / (128 * 128)
+    # or one E8M0 byte per 32 values (MX weights; MXFP8 activations)
+    ws_per = 1.0 / 32 if p.wdtype in ("mxfp8", "w4a8") else 4.0 / (128 * 128)
     as_per = 1.0 / 32 if p.wdtype == "mxfp8" else 4.0 / 128
     flops_g1 = 4.0 * R * p.H * p.I
     flops = 6.0 * R * p.H * p.I
@@ -301,9 +304,9 @@ def algorithmic(p: synth.Problem, touched: int, act_fused: bool = False, R: int 
     x_b = p.M * p.H * 2
     y_b = p.M * p.H * 2
     logits_b = p.M * p.E * 4
-    xin_g1 = p.M * p.H * wb + (p.M * p.H * as_per if q8 else 0)
+    xin_g1 = p.M * p.H * ab + (p.M * p.H * as_per if q8 else 0)
     if act_fused:
-        out_g1 = R * p.I * wb + (R * p.I * as_per if q8 else 0)
+        out_g1 = R * p.I * ab + (R * p.I * as_per if q8 else 0)
     else:
         out_g1 = R * 2 * p.I * 2
     return dict(flops=flops, bytes=w13_b + w2_b + x_b + y_b + logits_b,
@@ -336,11 +339,11 @@ def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.
         sub_ids = ids_np[toks]
         sel = torch.tensor(held[experts], device=d.x.device)
         x = bits16(d.x[:T])
-        if p.wdtype == "mxfp8":  # (no expert map: every expert is held)
+        if p.wdtype in ("mxfp8", "w4a8"):  # (no expert map: every expert is held)
             t0 = time.perf_counter()
             oracle.fused_experts_mx(x, bits8(d.w13q[sel]), d.w13s[sel].cpu().numpy(), bits8(d.w2q[sel]),
                                     d.w2s[sel].cpu().numpy(), remap[sub_ids], w_np[toks],
-                                    on_input=p.apply_router_weight_on_input)
+                                    w4=p.wdtype == "w4a8", on_input=p.apply_router_weight_on_input)
             return time.perf_counter() - t0, int((held[ids_np[toks]] >= 0).sum())
         if p.wdtype == "fp8":
             args = (x, bits8(d.w13q[sel]), d.w13s[sel].cpu().numpy(), bits8(d.w2q[sel]),
@@ -466,7 +469,7 @@ def main():
     alg = algorithmic(p, touched, st.act_fused, items)
     tflops = alg["flops"] / (ms * 1e-3) / 1e12
     tok_s = p.M / (ms * 1e-3)
-    dt = "fp8" if p.wdtype in ("fp8", "mxfp8") else "bf16"
+    dt = "fp8" if p.wdtype in ("fp8", "mxfp8", "w4a8") else "bf16"
     g1_s = stage_ms["gemm1"] * 1e-3
     t_mfma = alg_stage["flops_g1"] / (PEAK_TFLOPS[dt] * 1e12)
     t_hbm = alg_stage["bytes_g1"] / (PEAK_HBM_GBS * 1e9)
@@ -487,7 +490,8 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s",
         "tokens_per_s": round(tok_s, 1), "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8" if p.wdtype == "mxfp8" else dt,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"mxfp8": "mxfp8", "w4a8": "fp4 x fp8"}.get(p.wdtype, dt),
         "data": "synthetic",
         "config": {"workload": args.workload, "M": p.M, "H": p.H, "I": p.I, "E": p.E,
                    "topk": p.topk, "block_m": p.block_m, "weights": p.wdtype,

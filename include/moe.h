@@ -48,11 +48,18 @@ typedef enum {
     MOE_W_BF16 = 0,              /* bf16 weights, bf16 activations, fp32 accumulate */
     MOE_W_FP8_E4M3_BLOCK128 = 1, /* e4m3 weights with one fp32 scale per 128x128 block;
                                     activations quantised per token per 128 columns */
-    MOE_W_MXFP8 = 2              /* MXFP8 ("DeepGEMM FusedMoE on Blackwell", MXFP8 1x32):
+    MOE_W_MXFP8 = 2,             /* MXFP8 ("DeepGEMM FusedMoE on Blackwell", MXFP8 1x32):
                                     e4m3 weights and activations, one E8M0 scale (2^(c-127))
                                     per 32 K values, the smallest power of two s with
                                     amax <= 448 s; z is requantised the same way. Weight
                                     scales as packed words from moe_pack_mx_scales;
+                                    block_m 128 with H, I >= 256 */
+    MOE_W_W4A8_MXFP4 = 3         /* W4A8 ("DeepGEMM FusedMoE on Blackwell", W4A8 MXFP4):
+                                    E2M1 weights, two per byte (element 2i in the low
+                                    nibble: w13 [E, 2I, H/2], w2 [E, H, I/2] uint8), one
+                                    E8M0 scale per 32 K values (packed words as for MXFP8),
+                                    times e4m3 activations with one fp32 scale per 128
+                                    columns, as MOE_W_FP8_E4M3_BLOCK128 quantises x and z;
                                     block_m 128 with H, I >= 256 */
 } moe_wdtype_t;
 
@@ -226,7 +233,7 @@ moe_status_t moe_quant_mx_groups(const void *x, int64_t rows, int32_t cols, void
  *   which = 1: scale [E, 2I, H/32] uint8 -> scale_packed [E, H/128, 2I] uint32
  *   which = 2: scale [E, H, I/32]  uint8 -> scale_packed [E, I/128, H]  uint32
  * byte b of word (e, j, n) holds the scale of K block 4 j + b of row n.
- * Requires p->wdtype == MOE_W_MXFP8; buffers 4-byte aligned and distinct.
+ * Requires p->wdtype MOE_W_MXFP8 or MOE_W_W4A8_MXFP4; buffers 4-byte aligned and distinct.
  */
 moe_status_t moe_pack_mx_scales(const moe_problem_t *p, int32_t which, const void *scale,
                                 void *scale_packed, void *stream);

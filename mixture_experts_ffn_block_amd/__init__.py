@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
-MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8 = 0, 1, 2
+MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8, MOE_W_W4A8_MXFP4 = 0, 1, 2, 3
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
 
@@ -260,24 +260,27 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
     if expert_map is not None:
         _need(expert_map, torch.int32, "expert_map")
     _need(x, torch.bfloat16, "x")
-    fp8 = w13.dtype == torch.float8_e4m3fn
+    w4 = w13.dtype == torch.uint8                  # E2M1 weights, two per byte (W4A8)
+    fp8 = w13.dtype == torch.float8_e4m3fn or w4
     # e4m3 weights: fp32 128x128 block scales, or packed MX words (int32) from moe_pack_mx_scales
-    mx = fp8 and w13_scale is not None and w13_scale.dtype == torch.int32
-    wdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    mx = w13.dtype == torch.float8_e4m3fn and w13_scale is not None and w13_scale.dtype == torch.int32
+    wdt = torch.uint8 if w4 else torch.float8_e4m3fn if fp8 else torch.bfloat16
     _need(w13, wdt, "w13")
     _need(w2, wdt, "w2")
     _need(topk_ids, torch.int32, "topk_ids")
     _need(topk_weights, torch.float32, "topk_weights")
     if fp8:
-        _need(w13_scale, torch.int32 if mx else torch.float32, "w13_scale")
-        _need(w2_scale, torch.int32 if mx else torch.float32, "w2_scale")
+        _need(w13_scale, torch.int32 if (mx or w4) else torch.float32, "w13_scale")
+        _need(w2_scale, torch.int32 if (mx or w4) else torch.float32, "w2_scale")
     M, H = x.shape
     E, N2, H2 = w13.shape
-    if H2 != H or tuple(w2.shape) != (E, H, N2 // 2) or topk_ids.shape != topk_weights.shape \
+    d = 2 if w4 else 1
+    if H2 * d != H or tuple(w2.shape) != (E, H, N2 // 2 // d) or topk_ids.shape != topk_weights.shape \
             or topk_ids.shape[0] != M:
         raise ValueError("fused_experts: inconsistent shapes")
     p = make_problem(M, H, N2 // 2, E, topk_ids.shape[1], block_m,
-                     MOE_W_MXFP8 if mx else MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16,
+                     MOE_W_W4A8_MXFP4 if w4 else MOE_W_MXFP8 if mx else
+                     MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16,
                      apply_router_weight_on_input, weight_layout,
                      0 if expert_map is None else expert_map.numel(), chunk_tokens)
     if out is None:
@@ -309,12 +312,13 @@ def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
 
     workspace (from gemm_workspace_for) enables the split-K tail of the second GEMM, as
     fused_experts runs it."""
-    fp8 = p.wdtype in (MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8)
-    mx = p.wdtype == MOE_W_MXFP8   # scales: packed E8M0 words (int32) instead of fp32
+    w4 = p.wdtype == MOE_W_W4A8_MXFP4  # E2M1 weights, two per byte
+    fp8 = p.wdtype in (MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8) or w4
+    mx = p.wdtype == MOE_W_MXFP8       # activation scales: packed E8M0 words (int32)
     cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
     N, K = (2 * p.I, p.H) if which == 1 else (p.H, p.I)
     _need_size(a, _F8 if fp8 else _BF, (p.M if which == 1 else cap) * K, "a")
-    _need_size(w, _F8 if fp8 else _BF, p.E * N * K, "w")
+    _need_size(w, _F8 if fp8 else _BF, p.E * N * K // (2 if w4 else 1), "w")
     _need_size(expert_ids, _I32T, cap // p.block_m, "expert_ids")
     _need_size(num_tokens_post_padded, _I32T, 1, "num_tokens_post_padded")
     _need_size(c, _BF, cap * N, "c")
@@ -322,7 +326,8 @@ def moe_expert_gemm(p: MoeProblem, which: int, a: torch.Tensor, w: torch.Tensor,
         _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
     if fp8:
         _need_size(a_scale, _I32T if mx else _F32, (K // 128) * cap, "a_scale [K/128, cap]")
-        _need_size(w_scale, _I32T if mx else _F32, p.E * (N if mx else N // 128) * (K // 128), "w_scale")
+        _need_size(w_scale, _I32T if (mx or w4) else _F32, p.E * (N if (mx or w4) else N // 128) * (K // 128),
+                   "w_scale")
     _check(lib().moe_expert_gemm(ctypes.byref(p), which, _ptr(a), _ptr(a_scale), _ptr(w),
                                  _ptr(w_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
                                  _ptr(num_tokens_post_padded), _ptr(c), _ptr(workspace),
@@ -369,11 +374,12 @@ def moe_expert_gemm_act(p: MoeProblem, x: torch.Tensor, x_scale: torch.Tensor | 
 
     bf16 weights (block_m 128 or 256): z [cap, I] bf16, the scales are unused.
     fp8 weights (block_m 128): z [cap, I] e4m3 with z_scale [I/128, cap]."""
-    fp8 = p.wdtype in (MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8)
+    w4 = p.wdtype == MOE_W_W4A8_MXFP4
+    fp8 = p.wdtype in (MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8) or w4
     mx = p.wdtype == MOE_W_MXFP8
     cap = moe_align_capacity(p.M, p.topk, p.E, p.block_m)
     _need_size(x, _F8 if fp8 else _BF, p.M * p.H, "x")
-    _need_size(w13, _F8 if fp8 else _BF, p.E * 2 * p.I * p.H, "w13")
+    _need_size(w13, _F8 if fp8 else _BF, p.E * 2 * p.I * p.H // (2 if w4 else 1), "w13")
     _need_size(sorted_token_ids, _I32T, cap, "sorted_token_ids")
     _need_size(expert_ids, _I32T, cap // p.block_m, "expert_ids")
     _need_size(num_tokens_post_padded, _I32T, 1, "num_tokens_post_padded")
@@ -382,7 +388,8 @@ def moe_expert_gemm_act(p: MoeProblem, x: torch.Tensor, x_scale: torch.Tensor | 
     if fp8:
         sd = _I32T if mx else _F32
         _need_size(x_scale, sd, (p.H // 128) * cap, "x_scale [H/128, cap]")
-        _need_size(w13_scale, sd, p.E * (2 * p.I if mx else 2 * p.I // 128) * (p.H // 128), "w13_scale")
+        _need_size(w13_scale, _I32T if (mx or w4) else _F32,
+                   p.E * (2 * p.I if (mx or w4) else 2 * p.I // 128) * (p.H // 128), "w13_scale")
         _need_size(z_scale, sd, (p.I // 128) * cap, "z_scale [I/128, cap]")
     _check(lib().moe_expert_gemm_act(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(w13),
                                      _ptr(w13_scale), _ptr(sorted_token_ids), _ptr(expert_ids),

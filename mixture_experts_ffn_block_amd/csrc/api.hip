@@ -17,9 +17,15 @@ namespace {
 
 constexpr int64_t kAlign = 256;
 
-// 8-bit recipes: fp8 with 128x128 block scales, or MXFP8 with E8M0 scales per 32
-bool q8(const moe_problem_t& p) { return p.wdtype == MOE_W_FP8_E4M3_BLOCK128 || p.wdtype == MOE_W_MXFP8; }
+// 8-bit activations: fp8 with 128x128 block scales, MXFP8 (E8M0 scales per 32 on both
+// operands), or W4A8 (E2M1 weights with E8M0 scales per 32, fp8 activations per 128)
+bool q8(const moe_problem_t& p) {
+    return p.wdtype == MOE_W_FP8_E4M3_BLOCK128 || p.wdtype == MOE_W_MXFP8 || p.wdtype == MOE_W_W4A8_MXFP4;
+}
 bool is_mx(const moe_problem_t& p) { return p.wdtype == MOE_W_MXFP8; }
+bool is_w4(const moe_problem_t& p) { return p.wdtype == MOE_W_W4A8_MXFP4; }
+bool mx_weights(const moe_problem_t& p) { return is_mx(p) || is_w4(p); }  // E8M0 weight scales
+int gemm_fmt(const moe_problem_t& p) { return is_mx(p) ? 1 : is_w4(p) ? 2 : 0; }
 constexpr int kMaxE = 256;
 constexpr int kMaxTopk = 32;
 constexpr int kGroupM = 32;  // blocks per tile-scheduling window (groups never span two experts)
@@ -106,19 +112,20 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->topk > e_route || p->topk > kMaxTopk) return MOE_E_INVALID;
     if (p->E > kMaxE || p->H % 128 || p->I % 128) return MOE_E_UNSUPPORTED;
     if (!block_m_ok(p->block_m)) return MOE_E_UNSUPPORTED;
-    if (p->wdtype != MOE_W_BF16 && p->wdtype != MOE_W_FP8_E4M3_BLOCK128 && p->wdtype != MOE_W_MXFP8)
+    if (p->wdtype != MOE_W_BF16 && p->wdtype != MOE_W_FP8_E4M3_BLOCK128 && p->wdtype != MOE_W_MXFP8 &&
+        p->wdtype != MOE_W_W4A8_MXFP4)
         return MOE_E_UNSUPPORTED;
     if (p->wdtype == MOE_W_FP8_E4M3_BLOCK128 && (p->block_m == 16 || p->block_m == 256))
         return MOE_E_UNSUPPORTED;
     // MXFP8 runs on the persistent 128-row kernel, which takes K >= 256 in both GEMMs
-    if (p->wdtype == MOE_W_MXFP8 && (p->block_m != 128 || p->H < 256 || p->I < 256)) return MOE_E_UNSUPPORTED;
+    if (mx_weights(*p) && (p->block_m != 128 || p->H < 256 || p->I < 256)) return MOE_E_UNSUPPORTED;
     if (p->weight_layout != MOE_LAYOUT_ROWS && p->weight_layout != MOE_LAYOUT_TILED)
         return MOE_E_UNSUPPORTED;
     if (p->weight_layout == MOE_LAYOUT_TILED &&
         (p->wdtype != MOE_W_BF16 || (p->block_m != 16 && p->block_m != 128 && p->block_m != 256)))
         return MOE_E_UNSUPPORTED;
     // one expert's weight matrix is addressed with 32-bit byte offsets
-    const int64_t esz = q8(*p) ? 1 : 2;
+    const int64_t esz = q8(*p) ? 1 : 2;  // (E2M1 weights: half of it)
     if (int64_t(2) * p->I * p->H * esz >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
     // positions and routed items are int32 on the device
     if (p->M * p->topk >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
@@ -149,8 +156,8 @@ hipError_t gemm_stage(const moe_problem_t& p, const Rows& rows, int which, const
     g.topk = rows.topk;
     g.R = static_cast<int>(rows.R);
     g.W = w;
-    g.w_expert_bytes = static_cast<int64_t>(N) * K * esz;
-    g.ldw_bytes = static_cast<int64_t>(K) * esz;
+    g.w_expert_bytes = static_cast<int64_t>(N) * K * esz / (is_w4(p) ? 2 : 1);  // E2M1: two per byte
+    g.ldw_bytes = static_cast<int64_t>(K) * esz / (is_w4(p) ? 2 : 1);
     g.expert_ids = expert_ids;
     g.npp = npp;
     g.C = c;
@@ -165,9 +172,9 @@ hipError_t gemm_stage(const moe_problem_t& p, const Rows& rows, int which, const
         g.a_scale_ld = cap;
         g.w_scale = w_scale;
         // fp32 blocks [N/128, K/128] per expert, or MX words [K/128, N]
-        g.w_scale_expert = static_cast<int64_t>(is_mx(p) ? N : N / 128) * (K / 128);
+        g.w_scale_expert = static_cast<int64_t>(mx_weights(p) ? N : N / 128) * (K / 128);
         g.scale_groups = K / 128;
-        g.mx = is_mx(p) ? 1 : 0;
+        g.mx = gemm_fmt(p);
     }
     if (which == 2 && split_ws != nullptr && split_bytes(p) > 0) {
         g.part = static_cast<float*>(split_ws);
@@ -200,8 +207,8 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const Rows& rows, const void* 
     g.topk = rows.topk;
     g.R = static_cast<int>(rows.R);
     g.W = w13;
-    g.w_expert_bytes = static_cast<int64_t>(2) * p.I * p.H * esz;
-    g.ldw_bytes = static_cast<int64_t>(p.H) * esz;
+    g.w_expert_bytes = static_cast<int64_t>(2) * p.I * p.H * esz / (is_w4(p) ? 2 : 1);
+    g.ldw_bytes = static_cast<int64_t>(p.H) * esz / (is_w4(p) ? 2 : 1);
     g.expert_ids = expert_ids;
     g.npp = npp;
     g.C = z;
@@ -218,11 +225,11 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const Rows& rows, const void* 
         g.a_scale = a_scale;
         g.a_scale_ld = cap;
         g.w_scale = w13_scale;
-        g.w_scale_expert = static_cast<int64_t>(is_mx(p) ? 2 * p.I : 2 * p.I / 128) * (p.H / 128);
+        g.w_scale_expert = static_cast<int64_t>(mx_weights(p) ? 2 * p.I : 2 * p.I / 128) * (p.H / 128);
         g.scale_groups = p.H / 128;
         g.z_scale = z_scale;
         g.z_scale_ld = cap;
-        g.mx = is_mx(p) ? 1 : 0;
+        g.mx = gemm_fmt(p);
     }
     return p.block_m == 16 ? launch_stream_gemm(g, s) : launch_grouped_gemm(g, p.block_m, fp8, s);
 }
@@ -625,7 +632,7 @@ moe_status_t moe_pack_mx_scales(const moe_problem_t* p, int32_t which, const voi
     const moe_status_t st = check_problem(p);
     if (st != MOE_OK) return st;
     if (which != 1 && which != 2) return MOE_E_INVALID;
-    if (!is_mx(*p)) return MOE_E_UNSUPPORTED;
+    if (!mx_weights(*p)) return MOE_E_UNSUPPORTED;
     if (!scale || !scale_packed || scale == scale_packed) return MOE_E_INVALID;
     if (reinterpret_cast<uintptr_t>(scale) % 4 || reinterpret_cast<uintptr_t>(scale_packed) % 4)
         return MOE_E_INVALID;

@@ -808,21 +808,26 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
 // then writes z and its scales; h never reaches HBM.
 namespace f8 {
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+// FP4W: E2M1 weights, two per byte (W4A8): a stage's weight rows are 64 bytes
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool FP4W_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = WM_ * WN_, STAGES = STAGES_;
+    static constexpr bool FP4W = FP4W_;
     static constexpr int ROWB = 128, CH = 8, ROWS_PER_COPY = 8;
-    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    static constexpr int BROWB = FP4W ? 64 : 128, BCH = BROWB / 16, B_ROWS_PER_COPY = 1024 / BROWB;
+    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * BROWB;
     static constexpr int SCALE_OFF = A_BYTES + B_BYTES;   // 1 KB of row scales, then weight scales
     static constexpr int WSCALE_OFF = SCALE_OFF + 1024;
-    static constexpr int STAGE_BYTES = SCALE_OFF + 2048;
+    static constexpr int EPI_BYTES = 32 * ((BN / WN / 32) * 64 + 16);  // one 32-row pass of a wave's epilogue
+    // a stage also stages a tile's output, so it holds at least the epilogue's bytes
+    static constexpr int STAGE_BYTES = (SCALE_OFF + 2048 > NW * EPI_BYTES ? SCALE_OFF + 2048
+                                        : (NW * EPI_BYTES + 1023) / 1024 * 1024);
     static constexpr int IDS_OFF = STAGES * STAGE_BYTES;  // three 1 KB slots of sorted ids
     static constexpr int LDS_BYTES = IDS_OFF + 3072;
     static constexpr int A_INSTR = A_BYTES / 1024 / NW, B_INSTR = B_BYTES / 1024 / NW;
     static constexpr int L = A_INSTR + B_INSTR;  // copies per wave per stage (waves 0 and 1: L + 1)
     static constexpr int WBLOCKS = BN / 128;     // weight-scale rows per tile
     static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    static constexpr int EPI_BYTES = 32 * (TN * 64 + 16);  // one 32-row pass of a wave's epilogue
     static constexpr bool FP8_OUT = true;                  // SiLU epilogue output: e4m3 z
     static_assert(A_INSTR * NW * 1024 == A_BYTES && B_INSTR * NW * 1024 == B_BYTES, "whole copies");
     static_assert((A_INSTR == 2 || A_INSTR == 4) && (B_INSTR == 2 || B_INSTR % 4 == 0), "copy groups");
@@ -837,6 +842,10 @@ struct Cfg {
     static_assert(BM * (128 + 16) + 4 * BM * 4 <= STAGE_BYTES, "SiLU epilogue staging fits one ring slot");
     // 128-byte rows, 16-byte chunks XOR-swizzled by (row / 2) % 8
     __device__ static __forceinline__ int swz(int row, int chunk) { return row * CH + (chunk ^ ((row >> 1) & 7)); }
+    // weight rows: as above, or 64-byte rows swizzled by (row / 4) % 4
+    __device__ static __forceinline__ int bswz(int row, int chunk) {
+        return FP4W ? row * BCH + (chunk ^ ((row >> 2) & 3)) : swz(row, chunk);
+    }
 };
 
 // one 1 KB copy (16 bytes per lane) to LDS address `lds`
@@ -877,9 +886,15 @@ __device__ __forceinline__ void copy1_dword(const void* g, uint32_t lds) {
 // sorted position, the weights' [E, K/128, N]; a stage copies 128 and 256 words.
 // The SiLU epilogue quantises z per 32 columns (one wave's slice of a 128-column
 // block) to E4M3 with an E8M0 scale byte.
-template <class C, bool GATHER, bool ACT, bool MX>
+// FMT 0: fp8 with fp32 128x128 weight-block and per-128 activation scales; 1: MXFP8;
+// 2: W4A8 (E2M1 weights with E8M0 scales per 32, applied by the instruction, times
+// fp8 activations whose fp32 per-128 scale is folded per stage as in FMT 0).
+template <class C, bool GATHER, bool ACT, int FMT>
 __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p) {
     static_assert(!ACT || GATHER, "the SiLU epilogue belongs to GEMM1");
+    static_assert(C::FP4W == (FMT == 2), "E2M1 weight tiles for W4A8 only");
+    constexpr bool MX = FMT == 1;       // E8M0 scales on both operands
+    constexpr bool WMX = FMT != 0;      // E8M0 scales on the weights
     constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES, TM = C::TM, TN = C::TN;
     constexpr int A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR, L = C::L;
     extern __shared__ __attribute__((aligned(1024))) u32x4_t smem[];
@@ -941,8 +956,8 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         w_tile = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
 #pragma unroll
         for (int c = 0; c < B_INSTR; ++c) {
-            const int row = (wave * B_INSTR + c) * C::ROWS_PER_COPY + cp_row;
-            const int chunk = C::swz(row, cp_slot) - row * C::CH;
+            const int row = (wave * B_INSTR + c) * C::B_ROWS_PER_COPY + lane / C::BCH;
+            const int chunk = C::bswz(row, lane % C::BCH) - row * C::BCH;
             // ACT: tile row r is gate (r / 32 even) or up row of output column
             // n0 + 32 * (r / 64) + r % 32
             const int wrow = ACT ? ((row >> 5) & 1) * p.N + n0 + (row >> 6) * 32 + (row & 31)
@@ -951,7 +966,7 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         }
         if (wave == 0) {
             sc_src = p.a_scale + m0 + (lane & 31) * 4;
-        } else if constexpr (MX) {
+        } else if constexpr (WMX) {
             // 256 weight-row scale words of K block 0: lane l takes 4 of them. ACT:
             // lanes 0-31 the gate rows n0.., lanes 32-63 the up rows N + n0..; else
             // rows n0 + 4 l (clamped: rows past N are never stored)
@@ -993,7 +1008,7 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
     auto issue_rest = [&](int gs) {
         const int kt = gs % KT;
         const uint32_t st = static_cast<uint32_t>(gs % STAGES) * C::STAGE_BYTES;
-        const int64_t off = static_cast<int64_t>(kt) * C::ROWB;
+        const int64_t off = static_cast<int64_t>(kt) * C::BROWB;
 #pragma unroll
         for (int j = 0; j < B_INSTR / BG; ++j) {
             const uint8_t* g[BG];
@@ -1003,7 +1018,7 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         }
         if (wave == 0)
             f8::copy1(sc_src + static_cast<int64_t>(kt) * p.a_scale_ld, lds_base + st + C::SCALE_OFF);
-        else if (wave == 1 && MX)
+        else if (wave == 1 && WMX)
             f8::copy1(sc_src + static_cast<int64_t>(kt) * (ACT ? 2 * p.N : p.N), lds_base + st + C::WSCALE_OFF);
         else if (wave == 1)
             f8::copy1_dword(sc_src + kt, lds_base + st + C::WSCALE_OFF);
@@ -1037,10 +1052,19 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
+    // E2M1 weights: the instruction reads 4 registers, and unlike the e4m3 operand a
+    // lane holds 32 consecutive K values there, K [32 half, +32) of the 64-wide step
+    // (a probe pairing one-hot rows of both operands): chunk 2 ks + half, whole
+    auto frag_w4 = [&](const u32x4_t* base, int row, int ks) {
+        const u32x4_t c = base[C::bswz(row, 2 * ks + half)];
+        return i32x8_t{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
+    };
     auto read = [&](int g, int ks, Frag& f) {
         const u32x4_t* st = stage_ptr(g);
 #pragma unroll
-        for (int i = 0; i < TN; ++i) f.b[i] = frag(st + C::A_BYTES / 16, brow + i * 32 + r32, ks);
+        for (int i = 0; i < TN; ++i)
+            f.b[i] = C::FP4W ? frag_w4(st + C::A_BYTES / 16, brow + i * 32 + r32, ks)
+                             : frag(st + C::A_BYTES / 16, brow + i * 32 + r32, ks);
 #pragma unroll
         for (int i = 0; i < TM; ++i) f.a[i] = frag(st, arow + i * 32 + r32, ks);
     };
@@ -1052,6 +1076,22 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
             for (int tm = 0; tm < TM; ++tm)
                 part[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     f.b[tn], f.a[tm], first ? f32x16_t{} : part[tn][tm], 0, 0, 0, 127, 0, 127);
+    };
+    // W4A8: format 4 (E2M1) weights with their E8M0 scale per lane, e4m3 activations
+    // at unit scale (their fp32 scale is folded after the stage)
+    auto mma_w4 = [&](const Frag& f, int g, int ks, bool first) {
+        const uint32_t* sw = reinterpret_cast<const uint32_t*>(stage_ptr(g) + C::WSCALE_OFF / 16);
+        const int shift = 8 * (2 * ks + half);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int r = brow + tn * 32 + r32;
+            const int wi = ACT ? ((r >> 5) & 1) * 128 + (r >> 6) * 32 + (r & 31) : r;
+            const int bsc = static_cast<int>((sw[wi] >> shift) & 0xffu);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+                part[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.b[tn], f.a[tm], first ? f32x16_t{} : part[tn][tm], 4, 0, 0, bsc, 0, 127);
+        }
     };
     // MX: each lane's E8M0 bytes (K block 4 kt + 2 ks + half) of its activation row
     // and its weight row; the MFMA scales the products, the sums accumulate directly.
@@ -1085,7 +1125,7 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
             const float x = sx[arow + tm * 32 + r32];
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
-                const float sc = x * swb[ACT ? tn : brow / 128];
+                const float sc = FMT == 2 ? x : x * swb[ACT ? tn : brow / 128];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[tn][tm][r] += part[tn][tm][r] * sc;
             }
@@ -1212,6 +1252,11 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
             mma_mx(f0, g, 0);
             if (more) issue_rest(gs);
             mma_mx(f1, g, 1);
+        } else if constexpr (FMT == 2) {
+            mma_w4(f0, g, 0, true);
+            if (more) issue_rest(gs);
+            mma_w4(f1, g, 1, false);
+            fold(g);
         } else {
             mma(f0, true);
             if (more) issue_rest(gs);
@@ -1257,26 +1302,21 @@ int persistent_grid() {
     return cus[dev];
 }
 
-template <class C, bool GATHER, bool ACT, bool MX>
+template <class C, bool GATHER, bool ACT, int FMT>
 hipError_t launch_fp8_as(const GemmArgs& a, hipStream_t stream) {
     const size_t lds = C::LDS_BYTES;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, GATHER, ACT, MX>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(expert_gemm_fp8_kernel<C, GATHER, ACT, FMT>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (err != hipSuccess) return err;
     const dim3 grid(static_cast<unsigned>(persistent_grid()));
-    hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, GATHER, ACT, MX>), grid, dim3(C::NW * 64), lds, stream, a);
+    hipLaunchKernelGGL((expert_gemm_fp8_kernel<C, GATHER, ACT, FMT>), grid, dim3(C::NW * 64), lds, stream, a);
     return hipGetLastError();
 }
 
-template <class C, bool MX>
+template <class C, int FMT>
 hipError_t launch_fp8_fmt(const GemmArgs& a, hipStream_t stream) {
-    if (a.act) return a.sorted ? launch_fp8_as<C, true, true, MX>(a, stream) : hipErrorInvalidValue;
-    return a.sorted ? launch_fp8_as<C, true, false, MX>(a, stream) : launch_fp8_as<C, false, false, MX>(a, stream);
-}
-
-template <class C>
-hipError_t launch_fp8(const GemmArgs& a, hipStream_t stream) {
-    return a.mx ? launch_fp8_fmt<C, true>(a, stream) : launch_fp8_fmt<C, false>(a, stream);
+    if (a.act) return a.sorted ? launch_fp8_as<C, true, true, FMT>(a, stream) : hipErrorInvalidValue;
+    return a.sorted ? launch_fp8_as<C, true, false, FMT>(a, stream) : launch_fp8_as<C, false, false, FMT>(a, stream);
 }
 
 template <class C, bool GATHER, bool ACT>
@@ -1308,6 +1348,14 @@ using Dma128 = dma::Cfg<128, 512, 1, 4, 64, 8>;
 using Dma256 = dma::Cfg<256, 256, 2, 5, 64, 8>;
 // fp8: 128 tokens x 256 weight rows, 2 x 4 waves of 64 x 64, 3 stages
 using Fp8x128 = f8::Cfg<128, 256, 2, 4, 3>;
+// W4A8: the same tile over 64-byte E2M1 weight rows
+using W4x128 = f8::Cfg<128, 256, 2, 4, 3, true>;
+
+// GemmArgs::mx: 0 fp8 blocks, 1 MXFP8, 2 W4A8
+hipError_t launch_fp8(const GemmArgs& a, hipStream_t stream) {
+    if (a.mx == 2) return launch_fp8_fmt<W4x128, 2>(a, stream);
+    return a.mx ? launch_fp8_fmt<Fp8x128, 1>(a, stream) : launch_fp8_fmt<Fp8x128, 0>(a, stream);
+}
 
 template <int BM, int BN, bool FP8>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
@@ -1353,7 +1401,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, bool fp8, hipStre
             // the streaming kernel needs K / 128 >= STAGES - 1 (one tile's stages fill the
             // ring start); a single 128-wide K block takes the register-staged kernel
             case 128:
-                if (a.K >= 128 * (Fp8x128::STAGES - 1)) return launch_fp8<Fp8x128>(a, stream);
+                if (a.K >= 128 * (Fp8x128::STAGES - 1)) return launch_fp8(a, stream);
                 return a.act ? hipErrorInvalidValue : launch_tile<128, 256, true>(a, stream);
         }
     }

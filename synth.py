@@ -61,6 +61,8 @@ WORKLOADS = {
                             block_m=128, bias_std=0.0),
     # the fp8 workload's shapes and routing in MXFP8 (E8M0 scale per 32 values)
     "mxfp8_m4096": dict(M=4096, H=7168, I=2048, E=256, topk=8, wdtype="mxfp8", block_m=128),
+    # the same in W4A8: E2M1 weights with E8M0 scales per 32, fp8 activations per 128
+    "w4a8_m4096": dict(M=4096, H=7168, I=2048, E=256, topk=8, wdtype="w4a8", block_m=128),
     # a long prefill on the Mixtral shape, run in two chunks of 16K tokens
     "mixtral_prefill_m32768_chunk16k": dict(M=32768, H=4096, I=14336, E=8, topk=2, wdtype="bf16",
                                             block_m=256, chunk_tokens=16384),

@@ -108,3 +108,51 @@ def test_full_size_mx_sampled():
                                     sub.w2s.numpy(), remap[ids_np[toks]], w_np[toks])
     assert_close(bits16(y[toks]), y_ref, TOL["fp8"], name)
     assert bool(torch.isfinite(y.float()).all())
+
+
+# ------------------------------------------------------------------- W4A8 ---
+
+def run_w4(p, d, ids, w):
+    prob = moe.make_problem(p.M, p.H, p.I, p.E, p.topk, p.block_m, moe.MOE_W_W4A8_MXFP4)
+    s13, s2 = moe.moe_pack_mx_scales(prob, 1, d.w13s), moe.moe_pack_mx_scales(prob, 2, d.w2s)
+    return moe.fused_experts(d.x, d.w13q, d.w2q, ids, w, p.block_m, s13, s2,
+                             apply_router_weight_on_input=p.apply_router_weight_on_input)
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_layer_w4a8_matches_oracle(cfg):
+    p = synth.Problem(**cfg, wdtype="w4a8", block_m=128)
+    log(f"w4a8 layer {cfg}")
+    inp = synth.make_inputs(p, "cpu")
+    d = synth.Inputs(*[None if t is None else t.to(DEV) for t in (
+        inp.x, inp.logits, inp.w13, inp.w2, inp.w13q, inp.w13s, inp.w2q, inp.w2s)])
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    y = run_w4(p, d, ids, w)
+    torch.cuda.synchronize()
+    y_ref = oracle.fused_experts_mx(bits16(inp.x), inp.w13q.numpy(), inp.w13s.numpy(), inp.w2q.numpy(),
+                                    inp.w2s.numpy(), ids.cpu().numpy(), w.cpu().numpy(), w4=True,
+                                    on_input=p.apply_router_weight_on_input)
+    assert_close(bits16(y), y_ref, TOL["fp8"], str(cfg))
+
+
+def test_full_size_w4a8_sampled():
+    name = "w4a8_m4096"
+    p = synth.Problem.named(name)
+    log(f"full-size {name}")
+    d = synth.make_inputs(p, DEV)
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    y = run_w4(p, d, ids, w)
+    torch.cuda.synchronize()
+    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    rng = np.random.default_rng(0)
+    toks = sorted(set([0, p.M - 1] + list(rng.choice(p.M, 4, replace=False))))
+    experts = sorted(set(ids_np[toks].reshape(-1).tolist()))
+    remap = np.full(p.E, -1, np.int32)
+    remap[experts] = np.arange(len(experts), dtype=np.int32)
+    sel = torch.tensor(experts, device=DEV)
+    log(f"full-size {name}: oracle on tokens {toks} ({len(experts)} experts)")
+    y_ref = oracle.fused_experts_mx(bits16(d.x[toks]), d.w13q[sel].cpu().numpy(), d.w13s[sel].cpu().numpy(),
+                                    d.w2q[sel].cpu().numpy(), d.w2s[sel].cpu().numpy(), remap[ids_np[toks]],
+                                    w_np[toks], w4=True)
+    assert_close(bits16(y[toks]), y_ref, TOL["fp8"], name)
+    assert bool(torch.isfinite(y.float()).all())
