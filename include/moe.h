@@ -337,7 +337,7 @@ moe_status_t moe_batched_experts(const moe_problem_t *p, const void *a,
  * 2.6.3 and 2.6.5): every block b of block_m rows uses expert expert_ids[b].
  *   which = 1: c[pos, 0:2I] = a[sorted_token_ids[pos] / topk, :] . w13[e]^T,
  *              a = x [M, H] (bf16 or e4m3); padding rows (sorted id >= M*topk)
- *              read token 0 and are never consumed
+ *              are never consumed, and their values in c are unspecified
  *   which = 2: c[pos, 0:H] = a[pos, :] . w2[e]^T, a = z [cap, I] (bf16 or
  *              e4m3); sorted_token_ids may be NULL
  *   c [cap, N] bf16 out (fp32 accumulation, one rounding at the end).

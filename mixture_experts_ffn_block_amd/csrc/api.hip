@@ -153,6 +153,7 @@ hipError_t gemm_stage(const moe_problem_t& p, const Rows& rows, int which, const
     g.A = a;
     g.lda_bytes = static_cast<int64_t>(K) * esz;
     g.sorted = which == 1 ? sorted : nullptr;
+    g.live_ids = sorted;
     g.topk = rows.topk;
     g.R = static_cast<int>(rows.R);
     g.W = w;
@@ -204,6 +205,7 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const Rows& rows, const void* 
     g.A = a;
     g.lda_bytes = static_cast<int64_t>(p.H) * esz;
     g.sorted = sorted;
+    g.live_ids = sorted;
     g.topk = rows.topk;
     g.R = static_cast<int>(rows.R);
     g.W = w13;

@@ -30,6 +30,8 @@
 //     (workgroups are dealt round-robin over the 8 XCDs), and tiles are
 //     ordered in groups of GM row blocks per column tile so that an expert's
 //     weight tile is reused from that XCD's L2 by the row blocks that need it.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -602,6 +604,18 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
         for (int j = 0; j < TM; ++j) acc[i][j] = f32x16_t{};
 
     const int arow = wm * (BM / C::WM), brow = wn * (BN / C::WN);
+    // A block holds an expert's items, then padding rows (sorted id >= R). The
+    // wave's 32-row groups past the last one with a real row are not multiplied:
+    // their accumulators stay 0 (the SiLU epilogue writes 0 to padding rows
+    // anyway), and their LDS reads and MFMAs are left out. The copies and the
+    // barriers are the same for every wave.
+    int live = TM;
+    if (p.live_ids != nullptr) {
+        live = 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            if (ballot64(p.live_ids[m0 + arow + i * 32 + r32] < p.R) != 0) live = i + 1;
+    }
     struct Frag {
         bf16x8_t a[TM], b[TN];
     };
@@ -613,76 +627,100 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
         f.b[i] = __builtin_bit_cast(bf16x8_t,
                                     (stage_ptr(kt) + C::A_BYTES / 16)[C::swz(brow + i * 32 + r32, 2 * ks + half)]);
     };
-    auto read = [&](int kt, int ks, Frag& f) {
-#pragma unroll
-        for (int i = 0; i < TN; ++i) read_b(kt, ks, f, i);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) read_a(kt, ks, f, i);
-    };
-    auto mma = [&](const Frag& f) {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
-    };
-    // spread the TM + TN fragment reads of the next K step over this step's
-    // TM * TN MFMAs
-    auto interleave = [&]() { dma::interleave_step<0, TM + TN, TM * TN>(); };
 
-    // MFMAs of fragment set f, one weight row (tn) at a time. Between the rows
-    // go the LDS reads of the next K tile's first fragment set (into g) and the
-    // copies of tile `ck`: no long run of VMEM or LDS issues holds back the
-    // MFMAs queued behind it (a wave issues in order), and every MFMA only
-    // depends on LDS reads issued long before it.
-    auto mma_and_prefetch = [&](const Frag& f, int next_kt, Frag& g, int ck) {
+    // The K loop for LV live 32-row groups (LV = 0: the wave only copies).
+    auto k_loop = [&](auto lv) {
+        constexpr int LV = decltype(lv)::value;
+        auto read = [&](int kt, int ks, Frag& f) {
+            if constexpr (LV > 0) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
+                for (int i = 0; i < TN; ++i) read_b(kt, ks, f, i);
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            read_b(next_kt, 0, g, tn);
-#pragma unroll
-            for (int i = tn * TM / TN; i < (tn + 1) * TM / TN; ++i) read_a(next_kt, 0, g, i);
-            if (ck >= 0) {
-#pragma unroll
-                for (int j = tn * NGROUPS / TN; j < (tn + 1) * NGROUPS / TN; ++j) copy(ck, j);
+                for (int i = 0; i < LV; ++i) read_a(kt, ks, f, i);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    // Pipeline per K tile kt (NKS K steps, fragment sets alternating 0, 1):
-    //   for each K step but the last: read the next step's set while the MFMAs
-    //   of this step run;
-    //   last step: wait for tile kt+1, barrier, then its MFMAs interleaved with
-    //   the reads of tile kt+1's first set and the copies of tile kt+S-1 into
-    //   the stage of tile kt-1.
-    // S-2 tiles are in flight while tile kt is multiplied.
-    Frag fs[2];
-    for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
-    wait_barrier<C::L>(min(STAGES - 2, KT - 1));
-    read(0, 0, fs[0]);
-    auto steps_but_last = [&](int kt) {
+        };
+        auto mma = [&](const Frag& f) {
 #pragma unroll
-        for (int ks = 0; ks + 1 < NKS; ++ks) {
-            read(kt, ks + 1, fs[(ks + 1) & 1]);
-            mma(fs[ks & 1]);
-            interleave();
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < LV; ++tm)
+                    acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
+        };
+        // spread the LV + TN fragment reads of the next K step over this step's
+        // LV * TN MFMAs
+        auto interleave = [&]() {
+            if constexpr (LV > 0) dma::interleave_step<0, LV + TN, LV * TN>();
+        };
+
+        // MFMAs of fragment set f, one weight row (tn) at a time. Between the rows
+        // go the LDS reads of the next K tile's first fragment set (into g) and the
+        // copies of tile `ck`: no long run of VMEM or LDS issues holds back the
+        // MFMAs queued behind it (a wave issues in order), and every MFMA only
+        // depends on LDS reads issued long before it.
+        auto mma_and_prefetch = [&](const Frag& f, int next_kt, Frag& g, int ck) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+                for (int tm = 0; tm < LV; ++tm)
+                    acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (LV > 0) {
+                    read_b(next_kt, 0, g, tn);
+#pragma unroll
+                    for (int i = tn * LV / TN; i < (tn + 1) * LV / TN; ++i) read_a(next_kt, 0, g, i);
+                }
+                if (ck >= 0) {
+#pragma unroll
+                    for (int j = tn * NGROUPS / TN; j < (tn + 1) * NGROUPS / TN; ++j) copy(ck, j);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        // Pipeline per K tile kt (NKS K steps, fragment sets alternating 0, 1):
+        //   for each K step but the last: read the next step's set while the MFMAs
+        //   of this step run;
+        //   last step: wait for tile kt+1, barrier, then its MFMAs interleaved with
+        //   the reads of tile kt+1's first set and the copies of tile kt+S-1 into
+        //   the stage of tile kt-1.
+        // S-2 tiles are in flight while tile kt is multiplied.
+        Frag fs[2];
+        for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
+        wait_barrier<C::L>(min(STAGES - 2, KT - 1));
+        read(0, 0, fs[0]);
+        auto steps_but_last = [&](int kt) {
+#pragma unroll
+            for (int ks = 0; ks + 1 < NKS; ++ks) {
+                read(kt, ks + 1, fs[(ks + 1) & 1]);
+                mma(fs[ks & 1]);
+                interleave();
+            }
+        };
+        // (the last K tile is peeled off, so the reads of the next tile's first
+        // set are unconditional and the LDS counter waits stay exact)
+        for (int kt = 0; kt + 1 < KT; ++kt) {
+            steps_but_last(kt);
+            // tile kt+1 landed (tiles kt+2 .. kt+S-2 may still be in flight);
+            // every wave has finished reading the stage of tile kt-1
+            wait_barrier<C::L>(min(STAGES - 3, KT - 2 - kt));
+            mma_and_prefetch(fs[1], kt + 1, fs[0], kt + STAGES - 1 < KT ? kt + STAGES - 1 : -1);
         }
+        steps_but_last(KT - 1);
+        mma(fs[1]);
     };
-    // (the last K tile is peeled off, so the reads of the next tile's first
-    // set are unconditional and the LDS counter waits stay exact)
-    for (int kt = 0; kt + 1 < KT; ++kt) {
-        steps_but_last(kt);
-        // tile kt+1 landed (tiles kt+2 .. kt+S-2 may still be in flight);
-        // every wave has finished reading the stage of tile kt-1
-        wait_barrier<C::L>(min(STAGES - 3, KT - 2 - kt));
-        mma_and_prefetch(fs[1], kt + 1, fs[0], kt + STAGES - 1 < KT ? kt + STAGES - 1 : -1);
+    static_assert(TM <= 4, "live row group counts 0 .. 4");
+    if (live >= TM) {
+        k_loop(std::integral_constant<int, TM>{});
+    } else if (live == 0) {
+        k_loop(std::integral_constant<int, 0>{});
+    } else if constexpr (TM > 1) {
+        if (live == 1) {
+            k_loop(std::integral_constant<int, 1>{});
+        } else if constexpr (TM > 2) {
+            if (live == 2) k_loop(std::integral_constant<int, 2>{});
+            else if constexpr (TM > 3) k_loop(std::integral_constant<int, 3>{});
+        }
     }
-    steps_but_last(KT - 1);
-    mma(fs[1]);
 
     // no copies are in flight; once every wave is past its last fragment
     // read, the ring holds the epilogue staging

@@ -12,6 +12,8 @@ struct GemmArgs {
     const void* A;             // activation rows (bf16 or e4m3)
     int64_t lda_bytes;         // row stride of A
     const int32_t* sorted;     // non-null: row(pos) = sorted[pos] / topk (gather); null: row = pos
+    const int32_t* live_ids;   // sorted ids read only to find row groups that hold padding alone
+                               // (not multiplied); null: every row is multiplied
     int topk;
     int R;                     // M * topk; sorted entries >= R are padding
     const void* W;             // [E, N, K] weights
