@@ -20,6 +20,15 @@
 // Padding rows and the tail get the sentinel R; blocks past the padded total
 // get expert -1.
 //
+// Large inputs (R >= 4096) run the same steps on many CUs, in three kernels, so
+// that no single CU makes all the scattered stores: (1) each workgroup counts
+// the experts of its chunk of 1024 items into a [G, E] table, kept in the
+// inv_perm buffer until (3) overwrites it; (2) each workgroup sums the table
+// (totals, and the items of earlier chunks per expert), scans the padded totals
+// and places its chunk as in step 3 above, and a share of the blocks get their
+// expert and sentinels; (3) inv_perm is the inverse of the placement. The
+// layout is the same as the one-workgroup kernel's, bit for bit.
+//
 // Expert-parallel shard ("vLLM modular_kernel.py notes", expert_map: global
 // expert id -> this rank's expert, -1 for experts on other ranks; "DeepGEMM
 // FusedMoE on Blackwell", 2.6.2 ep_scatter skips items of remote experts): with
@@ -138,6 +147,152 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     }
 }
 
+// ---- multi-workgroup form -------------------------------------------------
+constexpr int kMultiThreads = 256;
+constexpr int kMultiWaves = kMultiThreads / MOE_WAVE;
+constexpr int kChunk = 1024;  // items per workgroup (kMultiThreads * 4)
+constexpr int64_t kMultiMinItems = 4096;
+
+// (1) expert counts of chunk g into table[g][0:E]
+__global__ __launch_bounds__(kMultiThreads) void align_count_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, const int32_t* __restrict__ emap, int E_global,
+    int32_t* __restrict__ table) {
+    __shared__ int32_t cnt[kMaxE];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kMultiThreads) cnt[e] = 0;
+    __syncthreads();
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kChunk;
+    const int64_t r1 = r0 + kChunk < R ? r0 + kChunk : R;
+    for (int64_t r = r0 + tid; r < r1; r += kMultiThreads) {
+        const int e = local_expert(ids[r], emap, E_global);
+        if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kMultiThreads) table[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+// (2) segment starts from the table, this chunk's stable placement, and the expert
+// and sentinels of blocks g, g + G, ...
+__global__ __launch_bounds__(kMultiThreads) void align_place_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, int B, int64_t cap,
+    const int32_t* __restrict__ emap, int E_global, const int32_t* __restrict__ table, int G,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids, int32_t* __restrict__ npp_out) {
+    __shared__ int32_t wave_off[kMultiWaves][kMaxE];
+    __shared__ int32_t seg_start[kMaxE + 1];
+    __shared__ int32_t count[kMaxE];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = blockIdx.x;
+
+    // totals over all chunks and the items of chunks before g, per expert
+    int n = 0, before = 0;
+    if (tid < E) {
+        // 32 loads in flight at a time
+        for (int j0 = 0; j0 < G; j0 += 32) {
+            int c[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) c[u] = j0 + u < G ? table[static_cast<int64_t>(j0 + u) * E + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                n += c[u];
+                before += j0 + u < g ? c[u] : 0;
+            }
+        }
+        count[tid] = n;
+    }
+    if (tid < kMaxE) seg_start[tid + 1] = tid < E ? static_cast<int>(ceil_div(n, B) * B) : 0;
+    if (tid == 0) seg_start[0] = 0;
+    for (int i = tid; i < kMultiWaves * kMaxE; i += kMultiThreads) (&wave_off[0][0])[i] = 0;
+    __syncthreads();
+    for (int d = 1; d < kMaxE; d <<= 1) {
+        int add = 0;
+        if (tid < kMaxE && tid + 1 - d >= 1) add = seg_start[tid + 1 - d];
+        __syncthreads();
+        if (tid < kMaxE) seg_start[tid + 1] += add;
+        __syncthreads();
+    }
+
+    // per-wave counts of this chunk (wave w owns items [r0 + 256 w, r0 + 256 (w + 1)))
+    const int64_t r0 = static_cast<int64_t>(g) * kChunk + wave * (kChunk / kMultiWaves);
+    const int64_t end = r0 + kChunk / kMultiWaves;
+    const int64_t r1 = end < R ? end : R;
+    // the wave's 256 items, four per lane, loaded once for the counts and the placement
+    constexpr int PER_LANE = kChunk / kMultiWaves / 64;
+    int el[PER_LANE];
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) el[i] = r0 + i * 64 + lane < r1 ? ids[r0 + i * 64 + lane] : -1;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) el[i] = r0 + i * 64 + lane < r1 ? local_expert(el[i], emap, E_global) : -1;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i)
+        if (static_cast<unsigned>(el[i]) < static_cast<unsigned>(E)) atomicAdd(&wave_off[wave][el[i]], 1);
+    __syncthreads();
+    if (tid < E) {
+        int run = seg_start[tid] + before;
+        for (int w = 0; w < kMultiWaves; ++w) {
+            const int c = wave_off[w][tid];
+            wave_off[w][tid] = run;
+            run += c;
+        }
+    }
+    const int total = seg_start[E];
+    if (g == 0 && tid == 0) *npp_out = total;
+    __syncthreads();
+
+    // blocks g, g + G, ...: the workgroup finds the block's expert (every thread
+    // the same search) and writes the sentinel rows together
+    const int64_t nblocks = cap / B;
+    for (int64_t b = g; b < nblocks; b += G) {
+        int e = -1;
+        if (b * B < total) {
+            int lo = 0, hi = E - 1;  // last e with seg_start[e] <= b*B
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (seg_start[mid] <= b * B) lo = mid; else hi = mid - 1;
+            }
+            e = lo;
+        }
+        if (tid == 0) expert_ids[b] = e;
+        const int64_t s = e < 0 ? b * B : seg_start[e] + count[e];
+        for (int64_t pos = (b * B > s ? b * B : s) + tid; pos < (b + 1) * B; pos += kMultiThreads)
+            sorted[pos] = static_cast<int32_t>(R);
+    }
+
+    // stable placement (as in the one-workgroup kernel)
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const int64_t r = r0 + i * 64 + lane;
+        const int e = el[i];
+        const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        uint64_t peers = ballot64(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool set = (e >> bit) & 1;
+            const uint64_t m = ballot64(set);
+            peers &= set ? m : ~m;
+        }
+        if (valid) {
+            const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+            sorted[wave_off[wave][e] + rank] = static_cast<int32_t>(r);
+            if (lane == 63 - __clzll(peers)) wave_off[wave][e] += __popcll(peers);
+        }
+    }
+}
+
+// (3) inv_perm[sorted[pos]] = pos for real rows; -1 for items of experts held elsewhere
+__global__ __launch_bounds__(256) void align_inverse_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, int64_t cap, const int32_t* __restrict__ emap,
+    int E_global, const int32_t* __restrict__ sorted, int32_t* __restrict__ inv_perm) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < cap; i += stride) {
+        const int r = sorted[i];
+        if (r < R) inv_perm[r] = static_cast<int32_t>(i);
+        if (i < R) {
+            const int e = local_expert(ids[i], emap, E_global);
+            if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) inv_perm[i] = -1;
+        }
+    }
+}
+
 // batched form ("vLLM modular_kernel.py notes", BatchedExperts: E batches of
 // max_M rows with per-expert counts): one top-1 id per row, -1 past the count
 __global__ __launch_bounds__(256) void batched_ids_kernel(const int32_t* __restrict__ counts, int E,
@@ -162,7 +317,19 @@ hipError_t launch_batched_ids(const int32_t* counts, int E, int64_t max_M, int32
 hipError_t launch_align(const int32_t* ids, int64_t R, int E, int B, int64_t cap,
                         const int32_t* emap, int E_global, int32_t* sorted, int32_t* expert_ids,
                         int32_t* npp, int32_t* inv_perm, hipStream_t stream) {
-    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), 0, stream, ids, R, E, B, cap, emap,
-                       E_global, sorted, expert_ids, npp, inv_perm);
+    const int64_t G = ceil_div(R, kChunk);
+    if (R < kMultiMinItems || G * E > R || G > (1 << 20)) {
+        hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), 0, stream, ids, R, E, B, cap, emap,
+                           E_global, sorted, expert_ids, npp, inv_perm);
+        return hipGetLastError();
+    }
+    // the [G, E] count table lives in inv_perm (R entries) until the inverse pass
+    hipLaunchKernelGGL(align_count_kernel, dim3(static_cast<unsigned>(G)), dim3(kMultiThreads), 0, stream,
+                       ids, R, E, emap, E_global, inv_perm);
+    hipLaunchKernelGGL(align_place_kernel, dim3(static_cast<unsigned>(G)), dim3(kMultiThreads), 0, stream,
+                       ids, R, E, B, cap, emap, E_global, inv_perm, static_cast<int>(G), sorted, expert_ids, npp);
+    const int64_t blocks = ceil_div(cap, 256);
+    hipLaunchKernelGGL(align_inverse_kernel, dim3(static_cast<unsigned>(blocks < 2048 ? blocks : 2048)), dim3(256),
+                       0, stream, ids, R, E, cap, emap, E_global, sorted, inv_perm);
     return hipGetLastError();
 }
