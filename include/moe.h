@@ -30,6 +30,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; these declarations are its
+ * exported interface. */
+#pragma GCC visibility push(default)
+
 typedef enum {
     MOE_OK = 0,
     MOE_E_INVALID = 1,     /* null pointer, negative size, topk outside [1, min(E, 32)]
@@ -435,6 +439,8 @@ moe_status_t moe_pack_weights(const moe_problem_t *p, int32_t which, const void 
 
 /* Host-only: a static, human-readable name of a status code. */
 const char *moe_status_string(moe_status_t s);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -3,6 +3,8 @@ every host-side check returns its status before any launch."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -15,7 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"if", "defined"})
+    src = "\n".join(l for l in src.splitlines() if not l.lstrip().startswith("#"))
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -24,6 +27,17 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(moe.EXPORTS), names
     for n in names:
         assert getattr(L, n) is not None
+
+
+def test_library_exports_nothing_else():
+    # internal launchers and helpers have hidden visibility
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    funcs = {l.split()[-1] for l in out.splitlines() if len(l.split()) == 3 and l.split()[1] == "T"}
+    assert funcs == set(declared_functions()), sorted(funcs ^ set(declared_functions()))
 
 
 def test_capacity_matches_oracle():

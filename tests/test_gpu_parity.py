@@ -164,6 +164,60 @@ def test_align_many_workgroups_boundaries():
         check_align(np.sort(ids, axis=0), E, B)
 
 
+
+@pytest.mark.parametrize("block_m", [128, 256])
+def test_gemm_real_rows_around_padding_groups(block_m):
+    # hand-made layouts in which padding rows (sorted id >= M*topk) fill whole 32-row
+    # groups before, between and after real rows, and whole blocks: every real row
+    # still gets its product in both GEMMs (groups of padding alone are not multiplied)
+    M, topk, E, H, I = 96, 2, 3, 256, 256
+    R, B = M * topk, block_m
+    p = synth.Problem(M=M, H=H, I=I, E=E, topk=topk, block_m=B, wdtype="bf16")
+    log(f"padding groups block_m={B}")
+    d = to_dev(synth.make_inputs(p, "cpu"))
+    prob = moe.make_problem(M, H, I, E, topk, B)
+    cap = moe.moe_align_capacity(M, topk, E, B)
+    nb = cap // B
+    assert nb >= 4
+    rows = {0: (0, list(range(32, 64)) + [B - 1]),   # block: (expert, real rows)
+            1: (1, [0]),
+            2: (2, []),
+            3: (0, [0, 64, 101] + ([130, 200, 255] if B == 256 else []))}
+    for b in range(4, nb):
+        rows[b] = (1, list(range(B - 32, B))) if b % 2 == 0 else (-1, [])
+    g = np.random.default_rng(11)
+    items = iter(g.permutation(R))
+    sorted_ids = np.full(cap, R, np.int32)
+    expert_ids = np.empty(nb, np.int32)
+    for b, (e, rr) in rows.items():
+        expert_ids[b] = e
+        for r in rr:
+            sorted_ids[b * B + r] = next(items)
+    s = torch.from_numpy(sorted_ids).to(DEV)
+    ex = torch.from_numpy(expert_ids).to(DEV)
+    npp = torch.tensor([cap], dtype=torch.int32, device=DEV)
+    h = torch.empty((cap, 2 * I), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_gemm(prob, 1, d.x, d.w13, s, ex, npp, h)
+    zg = torch.Generator().manual_seed(2)
+    z = torch.randn(cap, I, generator=zg).to(torch.bfloat16)
+    o = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_gemm(prob, 2, z.to(DEV), d.w2, s, ex, npp, o)
+    torch.cuda.synchronize()
+    xb, w13b, w2b = bits16(d.x), bits16(d.w13), bits16(d.w2)
+    hb, ob, zb = bits16(h), bits16(o), bits16(z)
+    checked = 0
+    for pos in range(cap):
+        r, e = int(sorted_ids[pos]), int(expert_ids[pos // B])
+        if r >= R or e < 0:
+            continue
+        for got, ref in ((hb[pos], oracle.gemm1_bf16(xb[r // topk], w13b[e])),
+                         (ob[pos], oracle.gemm2_bf16(zb[pos], w2b[e]))):
+            g64, r64 = bf16_f64(got), bf16_f64(ref)
+            assert np.all(np.abs(g64 - r64) <= 2e-2 * np.maximum(1.0, np.abs(r64))), (pos, r, e)
+        checked += 1
+    assert checked == sum(len(rr) for e, rr in rows.values() if e >= 0)
+
+
 # ------------------------------------------------------------------- quant ---
 
 def test_quant_fp8_bit_exact():
