@@ -20,7 +20,7 @@
 // Padding rows and the tail get the sentinel R; blocks past the padded total
 // get expert -1.
 //
-// Large inputs (R >= 4096) run the same steps on many CUs, in three kernels, so
+// Large inputs (R >= 8192) run the same steps on many CUs, in three kernels, so
 // that no single CU makes all the scattered stores: (1) each workgroup counts
 // the experts of its chunk of 1024 items into a [G, E] table, kept in the
 // inv_perm buffer until (3) overwrites it; (2) each workgroup sums the table
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
 constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / MOE_WAVE;
 constexpr int kChunk = 1024;  // items per workgroup (kMultiThreads * 4)
-constexpr int64_t kMultiMinItems = 4096;
+constexpr int64_t kMultiMinItems = 8192;
 
 // (1) expert counts of chunk g into table[g][0:E]
 __global__ __launch_bounds__(kMultiThreads) void align_count_kernel(
@@ -238,23 +238,21 @@ __global__ __launch_bounds__(kMultiThreads) void align_place_kernel(
     if (g == 0 && tid == 0) *npp_out = total;
     __syncthreads();
 
-    // blocks g, g + G, ...: the workgroup finds the block's expert (every thread
-    // the same search) and writes the sentinel rows together
-    const int64_t nblocks = cap / B;
-    for (int64_t b = g; b < nblocks; b += G) {
+    // positions g * 256 + tid, stride 256 G: padding rows and the tail get the
+    // sentinel, and each block start gives its block's expert
+    for (int64_t pos = static_cast<int64_t>(g) * kMultiThreads + tid; pos < cap;
+         pos += static_cast<int64_t>(G) * kMultiThreads) {
         int e = -1;
-        if (b * B < total) {
-            int lo = 0, hi = E - 1;  // last e with seg_start[e] <= b*B
+        if (pos < total) {
+            int lo = 0, hi = E - 1;  // last e with seg_start[e] <= pos
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (seg_start[mid] <= b * B) lo = mid; else hi = mid - 1;
+                if (seg_start[mid] <= pos) lo = mid; else hi = mid - 1;
             }
             e = lo;
         }
-        if (tid == 0) expert_ids[b] = e;
-        const int64_t s = e < 0 ? b * B : seg_start[e] + count[e];
-        for (int64_t pos = (b * B > s ? b * B : s) + tid; pos < (b + 1) * B; pos += kMultiThreads)
-            sorted[pos] = static_cast<int32_t>(R);
+        if (pos % B == 0) expert_ids[pos / B] = e;
+        if (e < 0 || pos >= seg_start[e] + count[e]) sorted[pos] = static_cast<int32_t>(R);
     }
 
     // stable placement (as in the one-workgroup kernel)

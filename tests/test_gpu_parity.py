@@ -152,12 +152,12 @@ def test_align_edge_cases():
 
 
 def test_align_many_workgroups_boundaries():
-    # from 4096 items on, chunks of 1024 items are counted and placed by separate
+    # from 8192 items on, chunks of 1024 items are counted and placed by separate
     # workgroups: both sides of that switch, ragged last chunks, chunk boundaries
     # inside one expert's run (ids in ascending order) and a single expert
     g = np.random.default_rng(3)
-    for M, k, E, B in ((4095, 1, 256, 16), (4096, 1, 256, 16), (4097, 1, 7, 128), (1025, 4, 5, 256),
-                       (9000, 8, 256, 64), (5000, 1, 1, 128)):
+    for M, k, E, B in ((8191, 1, 256, 16), (8192, 1, 256, 16), (8193, 1, 7, 128), (2049, 4, 5, 256),
+                       (9000, 8, 256, 64), (9000, 1, 1, 128)):
         log(f"align many-wg M={M} k={k} E={E} B={B}")
         ids = np.stack([g.choice(E, k, replace=False) for _ in range(M)]).astype(np.int32)
         check_align(ids, E, B)
