@@ -13,8 +13,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
  *     stream-ordered, never synchronises the host, and reads no device data
  *     on the host.
- *   - The library allocates nothing and keeps no global state: scratch space
- *     comes from the caller's workspace. Calls are thread-safe.
+ *   - The library allocates nothing and keeps no state beyond a per-device
+ *     cache of the compute-unit count: scratch space comes from the caller's
+ *     workspace. Calls are thread-safe.
  *   - Arguments are validated on the host before any launch; a failing check
  *     returns its status and launches nothing.
  *   - Tensors are dense, row-major and contiguous. bf16 is stored as its

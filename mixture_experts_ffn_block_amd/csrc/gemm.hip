@@ -30,6 +30,7 @@
 //     (workgroups are dealt round-robin over the 8 XCDs), and tiles are
 //     ordered in groups of GM row blocks per column tile so that an expert's
 //     weight tile is reused from that XCD's L2 by the row blocks that need it.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -1327,17 +1328,21 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
     if (i < n) p[i] = 0;
 }
 
-// one workgroup per CU (multiple of 8 so that every XCD gets the same count)
+// one workgroup per CU (multiple of 8 so that every XCD gets the same count); the
+// count is cached per device (relaxed atomics: concurrent first calls store the
+// same value)
 int persistent_grid() {
-    static int cus[64] = {};
+    static std::atomic<int> cus[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
-        cus[dev] = n / 8 * 8;
+        c = n / 8 * 8;
+        cus[dev].store(c, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return c;
 }
 
 template <class C, bool GATHER, bool ACT, int FMT>
