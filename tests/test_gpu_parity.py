@@ -165,17 +165,18 @@ def test_align_many_workgroups_boundaries():
 
 
 
-@pytest.mark.parametrize("block_m", [128, 256])
-def test_gemm_real_rows_around_padding_groups(block_m):
+@pytest.mark.parametrize("block_m,wdtype", [(128, "bf16"), (256, "bf16"), (128, "fp8")])
+def test_gemm_real_rows_around_padding_groups(block_m, wdtype):
     # hand-made layouts in which padding rows (sorted id >= M*topk) fill whole 32-row
     # groups before, between and after real rows, and whole blocks: every real row
     # still gets its product in both GEMMs (groups of padding alone are not multiplied)
-    M, topk, E, H, I = 96, 2, 3, 256, 256
+    M, topk, E, H, I = 96, 2, 3, 512, 256
     R, B = M * topk, block_m
-    p = synth.Problem(M=M, H=H, I=I, E=E, topk=topk, block_m=B, wdtype="bf16")
-    log(f"padding groups block_m={B}")
+    fp8 = wdtype == "fp8"
+    p = synth.Problem(M=M, H=H, I=I, E=E, topk=topk, block_m=B, wdtype=wdtype)
+    log(f"padding groups block_m={B} {wdtype}")
     d = to_dev(synth.make_inputs(p, "cpu"))
-    prob = moe.make_problem(M, H, I, E, topk, B)
+    prob = moe.make_problem(M, H, I, E, topk, B, moe.MOE_W_FP8_E4M3_BLOCK128 if fp8 else moe.MOE_W_BF16)
     cap = moe.moe_align_capacity(M, topk, E, B)
     nb = cap // B
     assert nb >= 4
@@ -197,26 +198,41 @@ def test_gemm_real_rows_around_padding_groups(block_m):
     ex = torch.from_numpy(expert_ids).to(DEV)
     npp = torch.tensor([cap], dtype=torch.int32, device=DEV)
     h = torch.empty((cap, 2 * I), dtype=torch.bfloat16, device=DEV)
-    moe.moe_expert_gemm(prob, 1, d.x, d.w13, s, ex, npp, h)
+    o = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
     zg = torch.Generator().manual_seed(2)
     z = torch.randn(cap, I, generator=zg).to(torch.bfloat16)
-    o = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
-    moe.moe_expert_gemm(prob, 2, z.to(DEV), d.w2, s, ex, npp, o)
+    if fp8:
+        xq, xs = moe.moe_quant_fp8_groups(d.x)
+        xst = torch.empty((H // 128, cap), dtype=torch.float32, device=DEV)
+        moe.moe_permute_scales(prob, xs, s, npp, xst)
+        moe.moe_expert_gemm(prob, 1, xq, d.w13q, s, ex, npp, h, xst, d.w13s)
+        zq, zs = moe.moe_quant_fp8_groups(z.to(DEV))
+        zst = zs.t().contiguous()  # [I/128, cap], by position
+        moe.moe_expert_gemm(prob, 2, zq, d.w2q, s, ex, npp, o, zst, d.w2s)
+        xqb, xsb, zqb, zsb = bits8(xq), xs.cpu().numpy(), bits8(zq), zs.cpu().numpy()
+        w13qb, w13sb, w2qb, w2sb = bits8(d.w13q), d.w13s.cpu().numpy(), bits8(d.w2q), d.w2s.cpu().numpy()
+        ref1 = lambda r, e: oracle.gemm_fp8(xqb[r // topk], xsb[r // topk], w13qb[e], w13sb[e])
+        ref2 = lambda pos, e: oracle.gemm_fp8(zqb[pos], zsb[pos], w2qb[e], w2sb[e])
+        tol = 6e-2
+    else:
+        moe.moe_expert_gemm(prob, 1, d.x, d.w13, s, ex, npp, h)
+        moe.moe_expert_gemm(prob, 2, z.to(DEV), d.w2, s, ex, npp, o)
+        xb, w13b, w2b, zb = bits16(d.x), bits16(d.w13), bits16(d.w2), bits16(z)
+        ref1 = lambda r, e: oracle.gemm1_bf16(xb[r // topk], w13b[e])
+        ref2 = lambda pos, e: oracle.gemm2_bf16(zb[pos], w2b[e])
+        tol = 2e-2
     torch.cuda.synchronize()
-    xb, w13b, w2b = bits16(d.x), bits16(d.w13), bits16(d.w2)
-    hb, ob, zb = bits16(h), bits16(o), bits16(z)
+    hb, ob = bits16(h), bits16(o)
     checked = 0
     for pos in range(cap):
         r, e = int(sorted_ids[pos]), int(expert_ids[pos // B])
         if r >= R or e < 0:
             continue
-        for got, ref in ((hb[pos], oracle.gemm1_bf16(xb[r // topk], w13b[e])),
-                         (ob[pos], oracle.gemm2_bf16(zb[pos], w2b[e]))):
+        for got, ref in ((hb[pos], ref1(r, e)), (ob[pos], ref2(pos, e))):
             g64, r64 = bf16_f64(got), bf16_f64(ref)
-            assert np.all(np.abs(g64 - r64) <= 2e-2 * np.maximum(1.0, np.abs(r64))), (pos, r, e)
+            assert np.all(np.abs(g64 - r64) <= tol * np.maximum(1.0, np.abs(r64))), (pos, r, e)
         checked += 1
     assert checked == sum(len(rr) for e, rr in rows.values() if e >= 0)
-
 
 # ------------------------------------------------------------------- quant ---
 
