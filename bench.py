@@ -439,17 +439,19 @@ def main():
     touched = int(np.unique(ids_host[held[ids_host]]).size)
     items = int(held[ids_host].sum())
 
-    # timed region: K steps through the product entry points
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: K steps through the product entry points (an event between steps
+    # gives each step's own duration; it does not synchronise)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         st.fused()
-    stop.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(stop) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
     # stage breakdown: the same kernels stage by stage, HIP events on the same stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
@@ -504,6 +506,7 @@ def main():
                       if p.batched else {}),
                    **({"chunk_tokens": p.chunk_tokens, "stage_scope": f"first chunk of {pc.M} tokens"}
                       if chunked else {})},
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "step_roofline_frac": round(t_star / (ms * 1e-3), 4),
         "roofline": roof,
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
