@@ -438,8 +438,8 @@ moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* 
         err = act_stage(*p, rows, ho, sorted, topk_weights, npp, z, zs, s);
         if (err != hipSuccess) return MOE_E_HIP;
     }
-    err = gemm_stage(*p, rows, 2, z, reinterpret_cast<const float*>(ws + L.zs), w2, w2_scale, sorted,
-                     expert_ids, npp, ho, L.split >= 0 ? ws + L.split : nullptr, s);
+    err = gemm_stage(*p, rows, 2, z, zs, w2, w2_scale, sorted, expert_ids, npp, ho,
+                     L.split >= 0 ? ws + L.split : nullptr, s);
     if (err != hipSuccess) return MOE_E_HIP;
     return hip_status(reduce_stage(*p, ho, inv_perm, topk_weights, y, s, unweighted));
 }
