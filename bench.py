@@ -313,6 +313,61 @@ def algorithmic(p: synth.Problem, touched: int, act_fused: bool = False, R: int 
                 flops_g1=flops_g1, bytes_g1=w13_b + xin_g1 + out_g1)
 
 
+def stage_work(p: synth.Problem, touched: int, R: int, npp: int, act_fused: bool):
+    """Algorithmic HBM bytes (and FLOP for the GEMMs) of each stage of one step: what the
+    stage must read and write at least, padding rows counted only where a stage writes
+    them (align's layout, the per-row activation outputs)."""
+    q8 = p.wdtype in ("fp8", "mxfp8", "w4a8")
+    ab = 1 if q8 else 2
+    wb = 0.5 if p.wdtype == "w4a8" else ab
+    a_sc = 1.0 / 32 if p.wdtype == "mxfp8" else 4.0 / 128       # activation scale bytes per value
+    w_sc = 1.0 / 32 if p.wdtype in ("mxfp8", "w4a8") else 4.0 / (128 * 128)
+    M, H, I, E, k = p.M, p.H, p.I, p.E, p.topk
+    w = {}
+    w["router"] = {"bytes": M * E * 4 + M * k * 8}
+    if q8:
+        w["quant"] = {"bytes": M * H * 2 + M * H + M * H * a_sc}
+    # align: ids in; sorted ids, block experts, inv_perm out (+ the activation scales'
+    # permute on the 8-bit paths)
+    w["align"] = {"bytes": R * 4 + npp * 4 + npp // p.block_m * 4 + R * 4
+                  + ((M * H * a_sc + npp * H * a_sc) if q8 else 0)}
+    z_b = npp * I * ab + (npp * I * a_sc if q8 else 0)
+    w13 = touched * 2 * I * H * (wb + (w_sc if q8 else 0))
+    w2 = touched * H * I * (wb + (w_sc if q8 else 0))
+    x_in = M * H * ab + (M * H * a_sc if q8 else 0)
+    if act_fused:
+        w["gemm1"] = {"flops": 4.0 * R * H * I, "bytes": w13 + x_in + z_b}
+    else:
+        w["gemm1"] = {"flops": 4.0 * R * H * I, "bytes": w13 + x_in + npp * 2 * I * 2}
+        w["act"] = {"bytes": npp * 2 * I * 2 + z_b}
+    w["gemm2"] = {"flops": 2.0 * R * H * I, "bytes": w2 + z_b + npp * H * 2}
+    w["reduce"] = {"bytes": R * H * 2 + R * 4 + M * H * 2}
+    return w
+
+
+def stage_roofline(work: dict, stage_ms: dict, dt: str) -> dict:
+    """Each stage's achieved rate against its binding roofline (the larger of its FLOP
+    and byte times at the spec peaks). A stage whose roofline time is under 2 us is
+    bound by launch and dependency latency, not by either peak: it reports its time."""
+    out = {}
+    for name, wk in work.items():
+        ms = stage_ms.get(name, 0.0)
+        if ms <= 0:
+            continue
+        t = ms * 1e-3
+        t_hbm = wk["bytes"] / (PEAK_HBM_GBS * 1e9)
+        t_mfma = wk.get("flops", 0.0) / (PEAK_TFLOPS[dt] * 1e12)
+        if max(t_hbm, t_mfma) < 2e-6:
+            out[name] = {"bound": "latency", "us": round(ms * 1e3, 1), "roofline_us": round(max(t_hbm, t_mfma) * 1e6, 2)}
+        elif t_mfma > t_hbm:
+            out[name] = {"bound": "mfma", "achieved": round(wk["flops"] / t / 1e12, 2), "unit": "TFLOP/s",
+                         "frac": round(t_mfma / t, 4)}
+        else:
+            out[name] = {"bound": "hbm", "achieved": round(wk["bytes"] / t / 1e9, 1), "unit": "GB/s",
+                         "frac": round(t_hbm / t, 4)}
+    return out
+
+
 def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.Tensor,
                  target_s: float):
     """The CPU oracle on a bounded sample of tokens (test infrastructure, timed as a baseline)."""
@@ -468,6 +523,14 @@ def main():
                 for j, name in enumerate(Step.STAGES)}
     staged_total = float(np.mean([e[0].elapsed_time(e[7]) for e in evs]))
 
+    touched_stage, items_stage = int(np.unique(ids_stage[held[ids_stage]]).size), int(held[ids_stage].sum())
+    if p.batched:  # the staged run is the top-1 problem over the E * M batch rows; no router
+        work = stage_work(dataclasses.replace(pc, M=p.E * p.M, topk=1), touched_stage, items_stage,
+                          int(sst.npp_q.item()), sst.act_fused)
+        del work["router"]
+    else:
+        work = stage_work(pc, touched_stage, items_stage, int(sst.npp.item()), sst.act_fused)
+
     alg = algorithmic(p, touched, st.act_fused, items)
     tflops = alg["flops"] / (ms * 1e-3) / 1e12
     tok_s = p.M / (ms * 1e-3)
@@ -510,6 +573,7 @@ def main():
         "step_roofline_frac": round(t_star / (ms * 1e-3), 4),
         "roofline": roof,
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_roofline": stage_roofline(work, stage_ms, dt),
         "staged_ms_per_step": round(staged_total, 4),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
     }
