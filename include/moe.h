@@ -344,7 +344,9 @@ moe_status_t moe_batched_experts(const moe_problem_t *p, const void *a,
  *              a = x [M, H] (bf16 or e4m3); padding rows (sorted id >= M*topk)
  *              are never consumed, and their values in c are unspecified
  *   which = 2: c[pos, 0:H] = a[pos, :] . w2[e]^T, a = z [cap, I] (bf16 or
- *              e4m3); sorted_token_ids may be NULL
+ *              e4m3); sorted_token_ids may be NULL (every row is then computed);
+ *              given, it marks the padding rows, whose values in c are again
+ *              unspecified (groups of padding rows alone may be left out)
  *   c [cap, N] bf16 out (fp32 accumulation, one rounding at the end).
  *   fp8: a_scale is [K/128, cap] fp32, group-major and indexed by sorted
  *   position (a_scale[g * cap + pos] belongs to row pos of the layout; built
