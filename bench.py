@@ -66,6 +66,23 @@ def measured_traffic(workload: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
+def measured_mfma(workload: str):
+    """MFMA-busy fraction of the SIMDs and the clock during GEMM1 from the committed
+    counter profile of this workload (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE), or
+    None if there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"gemm1_{workload}_mfma.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip().split()[0]
+    if kv.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return {"busy_fraction": float(kv["mfma_busy_fraction"]), "clock_ghz": float(kv["clock_ghz"])}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -546,6 +563,10 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(args.workload)
+    if roof["bound"] == "mfma":
+        # counters: the share of SIMD cycles the matrix cores were busy, and the clock
+        # (the chip is power-limited, so the spec peak at 2.4 GHz is not reached)
+        roof["mfma_counters"] = measured_mfma(args.workload)
     roof["kernel"] = ("gemm1 + SiLU-and-mul epilogue (grouped expert GEMM, gathered token rows x w13, writes z)"
                       if st.act_fused else "gemm1 (grouped expert GEMM, gathered token rows x w13)")
     roof["avg_ms"] = round(stage_ms["gemm1"], 4)

@@ -81,11 +81,23 @@ def test_traffic_needs_a_profile_of_the_current_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("w") == 1234.0
 
 
+def test_mfma_counters_need_a_profile_of_the_current_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.measured_mfma("w") is None
+    f = tmp_path / "gemm1_w_mfma.txt"
+    body = "mfma_busy_fraction = 0.5   (note)\nclock_ghz = 1.8   (note)\n"
+    f.write_text(body + "kernel_source_sha256 = 0\n")
+    assert bench.measured_mfma("w") is None
+    f.write_text(body + f"kernel_source_sha256 = {bench.kernel_source_digest()}\n")
+    assert bench.measured_mfma("w") == {"busy_fraction": 0.5, "clock_ghz": 1.8}
+
+
 def test_committed_profiles_match_the_committed_sources():
     # every GEMM1 traffic profile under profiles/ was taken on the kernel sources as
     # they stand (bench.py would otherwise report traffic as unknown)
     digest = bench.kernel_source_digest()
-    files = [n for n in os.listdir(os.path.join(ROOT, "profiles")) if n.endswith("_traffic.txt")]
+    files = [n for n in os.listdir(os.path.join(ROOT, "profiles"))
+             if n.endswith("_traffic.txt") or n.endswith("_mfma.txt")]
     assert files
     for n in files:
         text = open(os.path.join(ROOT, "profiles", n)).read()
