@@ -469,7 +469,7 @@ def cpu_baseline_batched(p: synth.Problem, d: synth.Inputs, st: "BatchedStep", t
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1",
                           "gpus_requested": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():
