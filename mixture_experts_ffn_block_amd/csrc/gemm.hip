@@ -24,12 +24,21 @@
 //     a temporary and added to the fp32 accumulator times
 //     (token scale * weight block scale). The token scale is constant per
 //     lane (one output row per lane), the weight scale per workgroup tile.
-//   * Loads are prefetched into registers one K tile ahead while the current
-//     tile is multiplied; LDS is double buffered (one barrier per K tile).
 //   * The 1-D grid is remapped so consecutive tiles run on the same XCD
 //     (workgroups are dealt round-robin over the 8 XCDs), and tiles are
 //     ordered in groups of GM row blocks per column tile so that an expert's
 //     weight tile is reused from that XCD's L2 by the row blocks that need it.
+//
+// The kernels in this file, by block_m:
+//   * 32 / 64: expert_gemm_kernel, loads prefetched into registers one K tile
+//     ahead, LDS double buffered (one barrier per K tile).
+//   * 128 / 256, bf16: expert_gemm_dma_kernel, a ring of 4-5 LDS stages filled by
+//     direct-to-LDS copies, 8 waves; row groups of padding alone are not
+//     multiplied; GEMM1 may carry SiLU-and-mul in its epilogue, GEMM2 splits a
+//     last, partly filled round of tiles along K.
+//   * 128, fp8 / MXFP8 / W4A8: expert_gemm_fp8_kernel, persistent, one continuous
+//     stream of K stages across a workgroup's tiles, scaled MFMA.
+// (block_m 16, the weight-streaming decode GEMM, is in gemm_stream.hip.)
 #include <atomic>
 #include <type_traits>
 
