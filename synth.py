@@ -159,6 +159,7 @@ def block_quant_fp8(w: torch.Tensor):
 
 
 _E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+_MX_STACK = 1 << 27  # weights quantised per mx_quant call when MX weights are drawn
 
 
 def mx_quant(w: torch.Tensor, fmt: str):
@@ -239,11 +240,21 @@ def make_inputs(p: Problem, device="cpu") -> Inputs:
         w2q = torch.empty((EL, H, I // div), dtype=dt, device=device)
         w13s = torch.empty((EL, 2 * I, H // 32), dtype=torch.uint8, device=device)
         w2s = torch.empty((EL, H, I // 32), dtype=torch.uint8, device=device)
-        for i, e in enumerate(held):
-            m13 = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H)).to(torch.bfloat16)
-            w13q[i], w13s[i] = mx_quant(m13, fmt)
-            m2 = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I)).to(torch.bfloat16)
-            w2q[i], w2s[i] = mx_quant(m2, fmt)
+        # the quantiser works row by row, so a stack of experts gets each expert's own
+        # codes and scales; stacks of up to _MX_STACK weights make far fewer launches
+        step = max(1, _MX_STACK // (2 * I * H))
+        experts = list(held)
+        for j in range(0, EL, step):
+            stack = experts[j:j + step]
+            n = len(stack)
+            m13 = torch.stack([_randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H))
+                               .to(torch.bfloat16) for e in stack])
+            q, sc = mx_quant(m13.view(n * 2 * I, H), fmt)
+            w13q[j:j + n], w13s[j:j + n] = q.view(n, 2 * I, -1), sc.view(n, 2 * I, -1)
+            m2 = torch.stack([_randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I))
+                              .to(torch.bfloat16) for e in stack])
+            q, sc = mx_quant(m2.view(n * H, I), fmt)
+            w2q[j:j + n], w2s[j:j + n] = q.view(n, H, -1), sc.view(n, H, -1)
         return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s, expert_map=emap, score_bias=sbias)
     raise ValueError(f"unknown weight dtype {p.wdtype!r}")
 

@@ -2,6 +2,7 @@
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import synth
@@ -60,3 +61,19 @@ def test_expert_parallel_rank_holds_its_slice_of_the_same_weights():
         else:
             assert r.w13q.shape[0] == 2 and r.w2s.shape[0] == 2
     assert synth.make_inputs(synth.Problem(M=2, H=128, I=128, E=4, topk=1), "cpu").expert_map is None
+
+
+@pytest.mark.parametrize("wdtype", ["mxfp8", "w4a8"])
+@pytest.mark.parametrize("stack", [1 << 27, 2 * 256 * 128 * 3])  # one stack; stacks of 3 experts
+def test_mx_weights_are_each_experts_own_quantisation(monkeypatch, wdtype, stack):
+    monkeypatch.setattr(synth, "_MX_STACK", stack)
+    p = synth.Problem(M=4, H=128, I=256, E=7, topk=2, wdtype=wdtype, block_m=128)
+    d = synth.make_inputs(p, "cpu")
+    fmt = "e4m3" if wdtype == "mxfp8" else "e2m1"
+    for e in range(p.E):
+        m13 = synth._randn((2 * p.I, p.H), "cpu", p.seed, synth._T_W13, e, 1.0 / math.sqrt(p.H))
+        q, s = synth.mx_quant(m13.to(torch.bfloat16), fmt)
+        assert torch.equal(d.w13q[e].view(torch.uint8), q.view(torch.uint8)) and torch.equal(d.w13s[e], s)
+        m2 = synth._randn((p.H, p.I), "cpu", p.seed, synth._T_W2, e, 1.0 / math.sqrt(p.I))
+        q, s = synth.mx_quant(m2.to(torch.bfloat16), fmt)
+        assert torch.equal(d.w2q[e].view(torch.uint8), q.view(torch.uint8)) and torch.equal(d.w2s[e], s)
