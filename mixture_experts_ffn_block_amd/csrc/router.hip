@@ -22,6 +22,14 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
     return v > bv || (v == bv && e < be);
 }
 
+// A NaN logit is read as -inf: it ranks below every number and its softmax
+// term is 0, so every chosen id stays in [0, E) (without this a row of NaNs
+// would beat nothing and leave the search's start value as the id).
+__device__ __forceinline__ float load_logit(const float* row, int e) {
+    const float v = row[e];
+    return v != v ? -INFINITY : v;
+}
+
 template <int EPL>
 __global__ __launch_bounds__(kTokensPerBlock * MOE_WAVE) void topk_softmax_kernel(
     const float* __restrict__ logits, int64_t M, int E, int k, int renormalize,
@@ -36,7 +44,7 @@ __global__ __launch_bounds__(kTokensPerBlock * MOE_WAVE) void topk_softmax_kerne
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? row[e] : -INFINITY;
+        v[i] = e < E ? load_logit(row, e) : -INFINITY;
         if (e < E) alive |= 1u << i;
     }
 
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(kTokensPerBlock * MOE_WAVE) void topk_grouped_kerne
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? row[e] : -INFINITY;
+        v[i] = e < E ? load_logit(row, e) : -INFINITY;
         key[i] = v[i];
         if (e < E) {
             alive |= 1u << i;

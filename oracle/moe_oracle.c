@@ -333,12 +333,24 @@ int oracle_fused_experts_mx(int64_t M, int H, int I, int E, int k, int mx_w4,
 /* S = TopK(p, k), weights renormalised over S when `renormalize` is set.     */
 /* ------------------------------------------------------------------------ */
 
+/* A NaN logit is read as -inf: it ranks below every number, so it is chosen
+ * only when fewer than k experts have another value, and then by the
+ * lower-index rule; its softmax term is 0. (The pages do not say what a NaN
+ * score does; this reading keeps every chosen id in [0, E).) A token whose
+ * logits are all NaN or -inf has an undefined softmax: its weights come out
+ * NaN from the arithmetic below (exp(-inf - -inf)). */
+static void load_scores(const float *logits, int E, float *s)
+{
+    for (int e = 0; e < E; ++e) s[e] = isnan(logits[e]) ? -INFINITY : logits[e];
+}
+
 int oracle_topk(const float *logits, int64_t M, int E, int k, int renormalize,
                 int32_t *ids, float *weights)
 {
     if (k < 1 || k > E || E > 1024 || k > 64) return 1;
     for (int64_t t = 0; t < M; ++t) {
-        const float *s = logits + t * E;
+        float s[1024];
+        load_scores(logits + t * E, E, s);
         double smax = -INFINITY;
         for (int e = 0; e < E; ++e)
             if (s[e] > smax) smax = s[e];
@@ -392,7 +404,8 @@ int oracle_topk_grouped(const float *logits, int64_t M, int E, int k, int scorin
     int gs = E / G;
     if (k > topk_group * gs || (bias && (scoring != 1 || gs < 2))) return 1;
     for (int64_t t = 0; t < M; ++t) {
-        const float *s = logits + t * E;
+        float s[1024];
+        load_scores(logits + t * E, E, s);
         float key[1024];
         for (int e = 0; e < E; ++e) key[e] = bias ? sigmoid_f32(s[e]) + bias[e] : s[e];
         char allowed[1024];

@@ -30,6 +30,14 @@ generation is chunked):
   (two per byte, element 2i in the low nibble), each 32 columns of a row
   sharing one E8M0 scale 2^ceil(log2(amax / fmax)) (fmax 448 or 6), stored
   [E, N, K/32] uint8; E2M1 takes the nearest grid value (ties to the smaller).
+* Spread scales (``scale_spread`` = s > 0, quantised formats only): before
+  quantisation every bf16 master is multiplied by powers of two, so that the
+  block scales differ by up to 2^(2s+4) inside a tensor and a scale read from
+  the wrong block, group or expert changes the result by a large factor. Weight
+  blocks (one per 128 rows x 128 columns for fp8, x 32 columns for the MX
+  formats) get 2^(c_e + d) with c_e ~ U{-2..2} per expert and d ~ U{-s..s} per
+  block; x gets 2^d per (token, 128 columns) (fp8, W4A8) or (token, 32
+  columns) (MXFP8). Each factor table has its own seeded generator.
 * Expert-parallel workloads (``ep_size`` > 1): the logits cover all E experts
   (global routing); rank ``ep_rank`` holds the contiguous range of E / ep_size
   experts starting at ``ep_rank * E / ep_size``, whose weights are the same
@@ -84,6 +92,7 @@ WORKLOADS = {
 }
 
 _T_X, _T_LOGITS, _T_BIAS, _T_W13, _T_W2, _T_SCORE_BIAS = 1, 2, 3, 4, 5, 6
+_T_SPREAD_X, _T_SPREAD_W13, _T_SPREAD_W2 = 7, 8, 9
 
 
 @dataclasses.dataclass
@@ -111,6 +120,7 @@ class Problem:
     score_bias_std: float = 0.0
     routed_scale: float = 1.0
     chunk_tokens: int = 0         # > 0: the layer runs on chunks of this many tokens
+    scale_spread: int = 0         # > 0: power-of-two factors spread the quantisation scales
 
     @property
     def local_experts(self) -> range:
@@ -140,6 +150,19 @@ def _randn(shape, device, seed, tensor_id, expert=0, std=1.0) -> torch.Tensor:
     if std != 1.0:
         t.mul_(std)
     return t
+
+
+def _spread_rows(n_rows: int, n_cols: int, col_block: int, device, seed, tensor_id, expert,
+                 spread: int, per_expert: bool) -> torch.Tensor:
+    """fp32 factors 2^p [n_rows, n_cols]: one exponent per 128 rows x col_block columns
+    (per row x col_block columns when not per_expert, for activations), p = c + d with
+    c ~ U{-2..2} for the expert (0 for activations) and d ~ U{-spread..spread}."""
+    g = _gen(device, seed, tensor_id, expert)
+    rb = 128 if per_expert else 1
+    c = int(torch.randint(-2, 3, (1,), generator=g, device=device).item()) if per_expert else 0
+    d = torch.randint(-spread, spread + 1, (n_rows // rb, n_cols // col_block), generator=g, device=device)
+    f = torch.exp2((c + d).float())
+    return f.repeat_interleave(rb, 0).repeat_interleave(col_block, 1)
 
 
 def block_quant_fp8(w: torch.Tensor):
@@ -202,7 +225,26 @@ class Inputs:
 def make_inputs(p: Problem, device="cpu") -> Inputs:
     """Draw the seeded synthetic inputs of problem ``p`` on ``device``."""
     M, H, I, E = p.M, p.H, p.I, p.E
-    x = _randn((M, H), device, p.seed, _T_X).to(torch.bfloat16)
+    spread = p.scale_spread if p.wdtype != "bf16" else 0
+    kb = 32 if p.wdtype in ("mxfp8", "w4a8") else 128   # columns per weight scale block
+    x = _randn((M, H), device, p.seed, _T_X)
+    if spread and M:
+        x *= _spread_rows(M, H, 32 if p.wdtype == "mxfp8" else 128, device, p.seed, _T_SPREAD_X, 0,
+                          spread, False)
+    x = x.to(torch.bfloat16)
+
+    def master13(e):
+        m = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H))
+        if spread:
+            m *= _spread_rows(2 * I, H, kb, device, p.seed, _T_SPREAD_W13, e, spread, True)
+        return m.to(torch.bfloat16)
+
+    def master2(e):
+        m = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I))
+        if spread:
+            m *= _spread_rows(H, I, kb, device, p.seed, _T_SPREAD_W2, e, spread, True)
+        return m.to(torch.bfloat16)
+
     logits = _randn((M, E), device, p.seed, _T_LOGITS)
     if p.bias_std:
         logits += _randn((E,), device, p.seed, _T_BIAS, std=p.bias_std)[None, :]
@@ -227,10 +269,8 @@ def make_inputs(p: Problem, device="cpu") -> Inputs:
         w13s = torch.empty((EL, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
         w2s = torch.empty((EL, H // 128, I // 128), dtype=torch.float32, device=device)
         for i, e in enumerate(held):
-            m13 = _randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H)).to(torch.bfloat16)
-            w13q[i], w13s[i] = block_quant_fp8(m13)
-            m2 = _randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I)).to(torch.bfloat16)
-            w2q[i], w2s[i] = block_quant_fp8(m2)
+            w13q[i], w13s[i] = block_quant_fp8(master13(e))
+            w2q[i], w2s[i] = block_quant_fp8(master2(e))
         return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s, expert_map=emap, score_bias=sbias)
     if p.wdtype in ("mxfp8", "w4a8"):
         fmt = "e4m3" if p.wdtype == "mxfp8" else "e2m1"
@@ -247,12 +287,10 @@ def make_inputs(p: Problem, device="cpu") -> Inputs:
         for j in range(0, EL, step):
             stack = experts[j:j + step]
             n = len(stack)
-            m13 = torch.stack([_randn((2 * I, H), device, p.seed, _T_W13, e, 1.0 / math.sqrt(H))
-                               .to(torch.bfloat16) for e in stack])
+            m13 = torch.stack([master13(e) for e in stack])
             q, sc = mx_quant(m13.view(n * 2 * I, H), fmt)
             w13q[j:j + n], w13s[j:j + n] = q.view(n, 2 * I, -1), sc.view(n, 2 * I, -1)
-            m2 = torch.stack([_randn((H, I), device, p.seed, _T_W2, e, 1.0 / math.sqrt(I))
-                              .to(torch.bfloat16) for e in stack])
+            m2 = torch.stack([master2(e) for e in stack])
             q, sc = mx_quant(m2.view(n * H, I), fmt)
             w2q[j:j + n], w2s[j:j + n] = q.view(n, H, -1), sc.view(n, H, -1)
         return Inputs(x, logits, None, None, w13q, w13s, w2q, w2s, expert_map=emap, score_bias=sbias)
