@@ -88,7 +88,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill_m4096", choices=list(synth.WORKLOADS))
+    # the default is the largest single-GPU configuration: the DeepSeek-V3-shaped prefill
+    # with skewed routing (8192 tokens, 256 experts, top-8; 5.77 TFLOP per step)
+    ap.add_argument("--workload", default="dsv3_skewed_prefill_m8192", choices=list(synth.WORKLOADS))
     ap.add_argument("--block-m", type=int, default=None, help="override the workload's block_m")
     ap.add_argument("--weight-layout", default="auto", choices=("auto", "rows", "tiled"),
                     help="element order of w13/w2: auto = the tiled order where the library "
@@ -385,6 +387,38 @@ def stage_roofline(work: dict, stage_ms: dict, dt: str) -> dict:
     return out
 
 
+def cpu_model() -> str:
+    """The host CPU's model name and logical CPU count (from /proc/cpuinfo)."""
+    try:
+        names = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")]
+        return f"{names[0]} ({len(names)} logical CPUs)" if names else "unknown"
+    except OSError:
+        return "unknown"
+
+
+def copy_bandwidth(mib: int = 2048, reps: int = 10) -> dict:
+    """Achievable HBM bandwidth on this GPU: a device-to-device copy of `mib` MiB (read
+    plus write bytes over the copy's time, HIP events on the current stream), timed
+    outside every timed region; the median of `reps` copies."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = float(np.median(times))
+    del src, dst
+    return {"copy_GBs": round(2 * (mib << 20) / t / 1e9, 1), "bytes_per_copy": 2 * (mib << 20),
+            "spec_GBs": PEAK_HBM_GBS, "frac_of_spec": round(2 * (mib << 20) / t / 1e9 / PEAK_HBM_GBS, 4),
+            "method": f"torch copy_ of {mib} MiB on the device, median of {reps}, read + write bytes"}
+
+
 def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.Tensor,
                  target_s: float):
     """The CPU oracle on a bounded sample of tokens (test infrastructure, timed as a baseline)."""
@@ -435,7 +469,7 @@ def cpu_baseline(p: synth.Problem, d: synth.Inputs, ids: torch.Tensor, w: torch.
         dt, items = run(T)
     flops = 6.0 * items * p.H * p.I
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "tokens_per_s": round(T / dt, 3), "seconds": round(dt, 3),
+            "kind": "oracle", "cpu": cpu_model(), "tokens_per_s": round(T / dt, 3), "seconds": round(dt, 3),
             "sample": f"first {T} of {p.M} tokens of the same workload (all their top-{p.topk} "
                       f"experts held here, {items} routed items), plain C oracle, fp64 "
                       f"accumulation, {threads} OpenMP threads"}
@@ -461,7 +495,7 @@ def cpu_baseline_batched(p: synth.Problem, d: synth.Inputs, st: "BatchedStep", t
         dt = run(n)
     items = int(np.clip(counts[:n], 0, p.M).sum())
     return {"value": round(6.0 * items * p.H * p.I / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "cpu": cpu_model(), "seconds": round(dt, 3),
             "sample": f"the batches of the first {n} of {p.E} experts ({items} rows), plain C oracle, "
                       f"fp64 accumulation, {threads} OpenMP threads"}
 
@@ -499,6 +533,8 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         del src, dst
+    torch.cuda.synchronize()
+    hbm = copy_bandwidth()  # outside every timed region
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -597,6 +633,7 @@ def main():
         "stage_roofline": stage_roofline(work, stage_ms, dt),
         "staged_ms_per_step": round(staged_total, 4),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "hbm_measured": hbm,
     }
     if args.cpu_seconds > 0:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)

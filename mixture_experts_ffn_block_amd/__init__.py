@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# MOE_LIB_PATH names another build of the same sources (the host-sanitizer build of
+# tests/test_sanitized.py); by default the in-tree library
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 MOE_W_BF16, MOE_W_FP8_E4M3_BLOCK128, MOE_W_MXFP8, MOE_W_W4A8_MXFP4 = 0, 1, 2, 3
@@ -131,6 +133,30 @@ def _need_size(t: torch.Tensor | None, dtypes, numel: int, name: str):
                          f"(contiguous={t.is_contiguous()}, device={t.device})")
     if t.numel() < numel:
         raise ValueError(f"{name}: needs {numel} elements, has {t.numel()}")
+
+
+def weight_scale_shapes(wdtype: int, E: int, H: int, I: int):
+    """Exact shapes of (w13_scale, w2_scale) for a weight format, or None for bf16: fp32
+    128x128 blocks [E, 2I/128, H/128] and [E, H/128, I/128], or the packed E8M0 words of
+    moe_pack_mx_scales [E, H/128, 2I] and [E, I/128, H] (MXFP8, W4A8)."""
+    if wdtype == MOE_W_FP8_E4M3_BLOCK128:
+        return (E, 2 * I // 128, H // 128), (E, H // 128, I // 128)
+    if wdtype in (MOE_W_MXFP8, MOE_W_W4A8_MXFP4):
+        return (E, H // 128, 2 * I), (E, I // 128, H)
+    return None
+
+
+def check_weight_scales(wdtype: int, E: int, H: int, I: int, w13_scale, w2_scale, what: str):
+    """Raise ValueError unless both scale tensors have exactly the shapes the kernels index
+    (a smaller tensor, e.g. one expert's or another rank's slice, would be read past its end)."""
+    want = weight_scale_shapes(wdtype, E, H, I)
+    if want is None:
+        return
+    for name, t, shape in (("w13_scale", w13_scale, want[0]), ("w2_scale", w2_scale, want[1])):
+        if t is None:
+            raise ValueError(f"{what}: {name} is required for this weight format")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{what}: {name} has shape {tuple(t.shape)}, expected {shape}")
 
 
 _F8 = (torch.float8_e4m3fn, torch.uint8)
@@ -283,6 +309,7 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
                      MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16,
                      apply_router_weight_on_input, weight_layout,
                      0 if expert_map is None else expert_map.numel(), chunk_tokens)
+    check_weight_scales(p.wdtype, E, H, N2 // 2, w13_scale, w2_scale, "fused_experts")
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
@@ -462,6 +489,7 @@ def moe_batched_experts(a: torch.Tensor, expert_num_tokens: torch.Tensor, w13: t
         _need(w2_scale, torch.float32, "w2_scale")
     p = make_problem(max_M, H, N2 // 2, E, 1, block_m,
                      MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16, False, weight_layout)
+    check_weight_scales(p.wdtype, E, H, N2 // 2, w13_scale, w2_scale, "moe_batched_experts")
     if out is None:
         out = torch.empty_like(a)
     _need(out, torch.bfloat16, "out")

@@ -167,10 +167,12 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, TilePos& t) {
 // tiles of the full rounds run whole, and when the tail would fill at most half
 // a round, each tail tile is cut into S = 2 or 4 K ranges that fill one round
 // (S divides the K stages; tail S <= part_slots). Workgroup h < F W takes tile h
-// in the XCD-contiguous order of the F W tiles. The S ranges of a tail tile run
-// on one XCD (workgroup h runs on XCD h % 8, and F W is a multiple of 8): unit
-// u = h - F W serves tail tile j = u % 8 + 8 ((u / 8) / S), K range (u / 8) % S,
-// so its partial tiles and its counter stay in that XCD's L2. The grid has
+// in the XCD-contiguous order of the F W tiles. The S ranges of a tail tile are
+// given workgroup ids congruent mod 8 (unit u = h - F W serves tail tile
+// j = u % 8 + 8 ((u / 8) / S), K range (u / 8) % S), which the dispatcher
+// places on one XCD when it deals workgroups round-robin, so their partials
+// tend to meet in one L2; the partials are published with an agent-scope
+// release, so the result does not depend on that placement. The grid has
 // W + 32 extra workgroups for this (8 ceil(tail / 8) S <= W + 7 S).
 struct SplitPos {
     int tile, S, chunk, slot, tail_tile;  // slot: partial tile index; -1 for a whole tile
@@ -741,12 +743,14 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
         if (sp.slot >= 0) {
             // Every K range writes its fp32 partial tile (in accumulator register
             // order: index ((wave, tn, tm, r), lane)), then counts itself in; the
-            // last to arrive sums the S partials in range order (deterministic),
-            // stores the tile and resets the counter. All ranges of a tile run on
-            // one XCD, whose L2 holds the partials and the counter: stores are
-            // complete in L2 once vmcnt drains (the L1 writes through), the
-            // counter's atomic is performed in L2, and the partials were never in
-            // the reading CU's L1 (each is read once, by the last arrival).
+            // last to arrive sums the S partials in range order (deterministic)
+            // and stores the tile. Ordering: the workgroup barrier puts every
+            // wave's partial stores before thread 0's counter update, which is an
+            // agent-scope release (the partials become visible to every CU, on any
+            // XCD) and acquire (the last arrival then sees every other range's
+            // partials). One release and one acquire per workgroup, not per wave.
+            // The ranges of a tile are still placed on one XCD, but only so that
+            // their partials meet in one L2; correctness does not depend on it.
             constexpr int TILE_F = C::NW * TN * TM * 16 * 64;
             static_assert(TILE_F == BM * BN, "one partial per output");
             float* part = p.part + static_cast<int64_t>(sp.slot) * TILE_F;
@@ -757,11 +761,10 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         part[(((wave * TN + tn) * TM + tm) * 16 + r) * 64 + lane] = acc[tn][tm][r];
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             int* cnt = p.part_cnt + sp.tail_tile;
             int* flag = reinterpret_cast<int*>(smem);
-            if (tid == 0) *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             const int arrived = *flag;
             if (arrived != sp.S - 1) return;
@@ -777,7 +780,6 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
                         for (int c = 1; c < sp.S; ++c) v += first[static_cast<int64_t>(c) * TILE_F + idx];
                         acc[tn][tm][r] = v;
                     }
-            if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();  // the flag's LDS word is reused by the staging below
         }
     }

@@ -42,7 +42,7 @@ struct GemmArgs {
     int64_t z_scale_ld;
     // split-K of a last, partly filled round of tiles (non-gathered GEMM on the DMA
     // tiles): part holds part_slots fp32 partial tiles, part_cnt one arrival counter
-    // per split tile (zero before the launch; the last arrival resets it); null: off
+    // per split tile (zeroed by a fill kernel before every launch); null: off
     float* part;
     int* part_cnt;
     int part_slots;

@@ -20,7 +20,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_SO = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_SO names another build of the same source (the sanitizer build of
+# tests/test_oracle_sanitized.py); by default the in-tree library
+_SO = os.environ.get("MOE_ORACLE_SO") or os.path.join(_HERE, "libmoe_oracle.so")
 _lib = None
 
 _P = ctypes.c_void_p

@@ -227,3 +227,29 @@ def test_chunked_workspace():
     assert chunked == moe.moe_workspace_bytes(P(M=256, block_m=64)) and chunked < full
     assert moe.moe_workspace_bytes(P(M=100, block_m=64, chunk_tokens=256)) == moe.moe_workspace_bytes(P(M=100, block_m=64))
     assert moe.moe_workspace_bytes(P(chunk_tokens=-1)) == 0
+
+
+def test_weight_scale_shapes_are_checked_exactly():
+    # the binding refuses scale tensors the kernels would read past (one expert's, a
+    # rank's slice, a transposed grid, unpacked MX bytes) before anything is launched
+    import torch
+    E, H, I = 4, 512, 256
+    f = lambda *s: torch.empty(s, dtype=torch.float32)
+    w = lambda *s: torch.empty(s, dtype=torch.int32)
+    fp8, mx, w4 = moe.MOE_W_FP8_E4M3_BLOCK128, moe.MOE_W_MXFP8, moe.MOE_W_W4A8_MXFP4
+    moe.check_weight_scales(fp8, E, H, I, f(E, 4, 4), f(E, 4, 2), "t")
+    moe.check_weight_scales(mx, E, H, I, w(E, 4, 512), w(E, 2, 512), "t")
+    moe.check_weight_scales(w4, E, H, I, w(E, 4, 512), w(E, 2, 512), "t")
+    moe.check_weight_scales(moe.MOE_W_BF16, E, H, I, None, None, "t")
+    bad = [
+        (fp8, f(1, 4, 4), f(E, 4, 2)),            # one expert's scales
+        (fp8, f(E, 4, 4), f(E, 2, 4)),            # w2 grid transposed
+        (fp8, f(E // 2, 4, 4), f(E // 2, 4, 2)),  # half of the experts
+        (fp8, None, f(E, 4, 2)),
+        (mx, w(E, 4, 512), w(E, 512, 2)),          # not the packed MN-major words
+        (mx, w(E, 1024, 16), w(E, 2, 512)),        # unpacked [E, N, K/32] shape
+        (w4, w(E, 4, 256), w(E, 2, 512)),
+    ]
+    for wd, a, b in bad:
+        with pytest.raises(ValueError):
+            moe.check_weight_scales(wd, E, H, I, a, b, "t")

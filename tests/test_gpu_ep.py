@@ -8,6 +8,7 @@ import torch
 
 import mixture_experts_ffn_block_amd as moe
 import oracle
+import sampled
 import synth
 from hostutil import bits16, bits8
 from test_gpu_parity import DEV, TOL, assert_close, log, to_dev
@@ -101,7 +102,9 @@ def test_layer_ep_matches_oracle(cfg):
     ids, w = moe.moe_topk(d.logits, p.topk)
     y = run_ep(p, d, ids, w)
     torch.cuda.synchronize()
-    y_ref = oracle_ep(p, inp, ids.cpu().numpy(), w.cpu().numpy())
+    ids_ref, w_ref = oracle.topk(inp.logits.numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    y_ref = oracle_ep(p, inp, ids_ref, w_ref)
     assert_close(bits16(y), y_ref, TOL[p.wdtype], str(cfg))
     if p.wdtype == "bf16" and p.block_m in (16, 128, 256):
         y_t = run_ep(p, d, ids, w, moe.MOE_LAYOUT_TILED)
@@ -139,23 +142,24 @@ def test_full_size_ep_rank_sampled():
     torch.cuda.synchronize()
     assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
     y = ys[0]
-    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    ids_np, w_np = oracle.topk(d.logits.cpu().numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_np)
     emap = d.expert_map.cpu().numpy()
     local = emap[ids_np] >= 0
     per_rank = np.bincount(ids_np.reshape(-1) // (p.E // p.ep_size), minlength=p.ep_size)
     assert int(np.argmax(per_rank)) == p.ep_rank and per_rank[p.ep_rank] == local.sum()
     assert np.all(y[torch.from_numpy(~local.any(1)).to(DEV)].float().cpu().numpy() == 0)
-    # samples: tokens with the fewest and the most local slots, one with exactly one, random ones
+    # samples: one real row of every block of the rank's layout, tokens with the fewest and
+    # the most local slots, one with exactly one, random ones up to 128
     nloc = local.sum(1)
-    rng = np.random.default_rng(0)
     picks = [int(np.argmin(nloc)), int(np.argmax(nloc))] + [int(t) for t in np.nonzero(nloc == 1)[0][:1]]
-    toks = sorted(set(picks + list(rng.choice(p.M, 5, replace=False))))
+    toks = sorted(set(picks + sampled.pick_tokens(ids_np, len(p.local_experts), p.block_m, expert_map=emap)))
     held = sorted(set(emap[ids_np[toks]][local[toks]].tolist()))
     sub_map = np.full(p.E, -1, np.int32)
     for i, le in enumerate(held):
         sub_map[np.nonzero(emap == le)[0][0]] = i
     sel = torch.tensor(held, device=DEV)
-    log(f"full-size {name}: oracle on tokens {toks} ({len(held)} local experts)")
+    log(f"full-size {name}: oracle on {len(toks)} tokens ({len(held)} local experts)")
     y_ref = oracle.fused_experts_bf16(bits16(d.x[toks]), bits16(d.w13[sel]), bits16(d.w2[sel]),
                                       ids_np[toks], w_np[toks], expert_map=sub_map)
     assert_close(bits16(y[toks]), y_ref, TOL["bf16"], name)

@@ -56,7 +56,9 @@ def test_layer_at_the_limits(cfg):
     ids, w = moe.moe_topk(d.logits, p.topk)
     y = run_layer(p, d, ids, w)
     torch.cuda.synchronize()
-    assert_close(bits16(y), oracle_layer(p, inp, ids.cpu().numpy(), w.cpu().numpy()), TOL[p.wdtype], str(cfg))
+    ids_ref, w_ref = oracle.topk(inp.logits.numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert_close(bits16(y), oracle_layer(p, inp, ids_ref, w_ref), TOL[p.wdtype], str(cfg))
 
 
 def test_no_tokens_through_every_entry_point():

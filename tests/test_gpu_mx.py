@@ -8,6 +8,7 @@ import torch
 
 import mixture_experts_ffn_block_amd as moe
 import oracle
+import sampled
 import synth
 from hostutil import bits16, bits8
 from test_gpu_parity import DEV, TOL, assert_close, log
@@ -82,32 +83,34 @@ def test_layer_mx_matches_oracle(cfg):
     ids, w = moe.moe_topk(d.logits, p.topk)
     y = run_mx(p, d, ids, w)
     torch.cuda.synchronize()
-    y_ref = oracle_mx(p, inp, ids.cpu().numpy(), w.cpu().numpy())
+    ids_ref, w_ref = oracle.topk(inp.logits.numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    y_ref = oracle_mx(p, inp, ids_ref, w_ref)
     assert_close(bits16(y), y_ref, TOL["fp8"], str(cfg))
 
 
-def test_full_size_mx_sampled():
-    name = "mxfp8_m4096"
+def full_size_mx_sampled(name, run):
     p = synth.Problem.named(name)
+    w4 = p.wdtype == "w4a8"
     log(f"full-size {name}")
     d = synth.make_inputs(p, DEV)
     ids, w = moe.moe_topk(d.logits, p.topk)
-    y = run_mx(p, d, ids, w)
+    y = run(p, d, ids, w)
     torch.cuda.synchronize()
-    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
-    rng = np.random.default_rng(0)
-    toks = sorted(set([0, p.M - 1] + list(rng.choice(p.M, 4, replace=False))))
-    experts = sorted(set(ids_np[toks].reshape(-1).tolist()))
-    remap = np.full(p.E, -1, np.int32)
-    remap[experts] = np.arange(len(experts), dtype=np.int32)
+    ids_np, w_np = oracle.topk(d.logits.cpu().numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_np)
+    toks = sampled.pick_tokens(ids_np, p.E, p.block_m)
+    experts, sub_ids = sampled.expert_subset(ids_np, toks, p.E)
     sel = torch.tensor(experts, device=DEV)
-    sub = synth.Inputs(d.x[toks].cpu(), None, None, None, d.w13q[sel].cpu(), d.w13s[sel].cpu(),
-                       d.w2q[sel].cpu(), d.w2s[sel].cpu())
-    log(f"full-size {name}: oracle on tokens {toks} ({len(experts)} experts)")
-    y_ref = oracle.fused_experts_mx(bits16(sub.x), bits8(sub.w13q), sub.w13s.numpy(), bits8(sub.w2q),
-                                    sub.w2s.numpy(), remap[ids_np[toks]], w_np[toks])
+    log(f"full-size {name}: oracle on {len(toks)} tokens ({len(experts)} experts)")
+    y_ref = oracle.fused_experts_mx(bits16(d.x[toks]), bits8(d.w13q[sel]), d.w13s[sel].cpu().numpy(),
+                                    bits8(d.w2q[sel]), d.w2s[sel].cpu().numpy(), sub_ids, w_np[toks], w4=w4)
     assert_close(bits16(y[toks]), y_ref, TOL["fp8"], name)
     assert bool(torch.isfinite(y.float()).all())
+
+
+def test_full_size_mx_sampled():
+    full_size_mx_sampled("mxfp8_m4096", run_mx)
 
 
 # ------------------------------------------------------------------- W4A8 ---
@@ -129,30 +132,13 @@ def test_layer_w4a8_matches_oracle(cfg):
     ids, w = moe.moe_topk(d.logits, p.topk)
     y = run_w4(p, d, ids, w)
     torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.topk(inp.logits.numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
     y_ref = oracle.fused_experts_mx(bits16(inp.x), inp.w13q.numpy(), inp.w13s.numpy(), inp.w2q.numpy(),
-                                    inp.w2s.numpy(), ids.cpu().numpy(), w.cpu().numpy(), w4=True,
+                                    inp.w2s.numpy(), ids_ref, w_ref, w4=True,
                                     on_input=p.apply_router_weight_on_input)
     assert_close(bits16(y), y_ref, TOL["fp8"], str(cfg))
 
 
 def test_full_size_w4a8_sampled():
-    name = "w4a8_m4096"
-    p = synth.Problem.named(name)
-    log(f"full-size {name}")
-    d = synth.make_inputs(p, DEV)
-    ids, w = moe.moe_topk(d.logits, p.topk)
-    y = run_w4(p, d, ids, w)
-    torch.cuda.synchronize()
-    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
-    rng = np.random.default_rng(0)
-    toks = sorted(set([0, p.M - 1] + list(rng.choice(p.M, 4, replace=False))))
-    experts = sorted(set(ids_np[toks].reshape(-1).tolist()))
-    remap = np.full(p.E, -1, np.int32)
-    remap[experts] = np.arange(len(experts), dtype=np.int32)
-    sel = torch.tensor(experts, device=DEV)
-    log(f"full-size {name}: oracle on tokens {toks} ({len(experts)} experts)")
-    y_ref = oracle.fused_experts_mx(bits16(d.x[toks]), d.w13q[sel].cpu().numpy(), d.w13s[sel].cpu().numpy(),
-                                    d.w2q[sel].cpu().numpy(), d.w2s[sel].cpu().numpy(), remap[ids_np[toks]],
-                                    w_np[toks], w4=True)
-    assert_close(bits16(y[toks]), y_ref, TOL["fp8"], name)
-    assert bool(torch.isfinite(y.float()).all())
+    full_size_mx_sampled("w4a8_m4096", run_w4)

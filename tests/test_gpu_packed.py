@@ -91,8 +91,10 @@ def test_layer_tiled_matches_rows_and_oracle(cfg):
                                 weight_layout=TILED)
     torch.cuda.synchronize()
     assert torch.equal(y_rows.view(torch.int16), y_tiled.view(torch.int16))
-    y_ref = oracle.fused_experts_bf16(bits16(inp.x), bits16(inp.w13), bits16(inp.w2),
-                                      ids.cpu().numpy(), w.cpu().numpy(), on_input=on)
+    ids_ref, w_ref = oracle.topk(inp.logits.numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    y_ref = oracle.fused_experts_bf16(bits16(inp.x), bits16(inp.w13), bits16(inp.w2), ids_ref, w_ref,
+                                      on_input=on)
     assert_close(bits16(y_tiled), y_ref, TOL["bf16"], str(cfg))
 
 

@@ -14,6 +14,7 @@ import torch
 
 import mixture_experts_ffn_block_amd as moe
 import oracle
+import sampled
 import synth
 from hostutil import bf16_f64, bits16, bits8
 
@@ -115,6 +116,51 @@ def test_router_ties_and_unnormalised():
         ids_ref, w_ref = oracle.topk(logits.numpy(), 4, renormalize=renorm)
         assert np.array_equal(ids.cpu().numpy(), ids_ref)
         assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
+
+
+def test_router_nan_logits():
+    # a NaN logit ranks below every number (the oracle's reading); a token whose logits
+    # are all NaN gets ids 0..k-1 and NaN weights, so its y row is NaN, not silently 0
+    g = torch.Generator().manual_seed(11)
+    logits = torch.randn(64, 256, generator=g)
+    logits[0, :200] = float("nan")
+    logits[1, [3, 77, 130, 255]] = float("nan")
+    logits[2, :] = float("nan")
+    logits[3, 5] = float("-inf")
+    logits[3, 6] = float("nan")
+    for renorm in (True, False):
+        ids, w = moe.moe_topk(logits.to(DEV), 8, renormalize=renorm)
+        ids_ref, w_ref = oracle.topk(logits.numpy(), 8, renormalize=renorm)
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        wg = w.cpu().numpy()
+        assert np.array_equal(np.isnan(wg), np.isnan(w_ref))
+        ok = ~np.isnan(w_ref)
+        assert np.abs(wg[ok] - w_ref[ok]).max() <= 1e-6
+    ids, w = moe.moe_topk_grouped(logits.to(DEV), 8, "sigmoid", True, 8, 4,
+                                  torch.zeros(256, device=DEV), 2.5)
+    ids_ref, _ = oracle.topk_grouped(logits.numpy(), 8, "sigmoid", True, 8, 4, np.zeros(256, np.float32), 2.5)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert ((ids >= 0) & (ids < 256)).all()
+    # through the layer: finite rows stay finite, the all-NaN token's row is NaN
+    p = synth.Problem(M=64, H=256, I=256, E=256, topk=8, block_m=16)
+    d = to_dev(synth.make_inputs(synth.Problem(M=64, H=256, I=256, E=256, topk=8), "cpu"))
+    ids, w = moe.moe_topk(logits.to(DEV), 8)
+    y = run_layer(p, d, ids, w).float()
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(y[2]).all())
+    keep = torch.ones(64, dtype=torch.bool)
+    keep[2] = False
+    assert bool(torch.isfinite(y[keep.to(DEV)]).all())
+
+
+def test_binding_rejects_mis_shaped_weight_scales():
+    p = synth.Problem(M=40, H=256, I=256, E=4, topk=2, block_m=64, wdtype="fp8")
+    d = to_dev(synth.make_inputs(p, "cpu"))
+    ids, w = moe.moe_topk(d.logits, p.topk)
+    for s13, s2 in ((d.w13s[:1], d.w2s), (d.w13s, d.w2s.transpose(1, 2).contiguous()[:, :1]),
+                    (d.w13s, d.w2s[:2])):
+        with pytest.raises(ValueError, match="scale"):
+            moe.fused_experts(d.x, d.w13q, d.w2q, ids, w, p.block_m, s13.contiguous(), s2.contiguous())
 
 
 # ------------------------------------------------------------------- align ---
@@ -430,7 +476,8 @@ def test_layer_small_elementwise(cfg):
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
     y = run_layer(p, d, ids, w)
     torch.cuda.synchronize()
-    y_ref = oracle_layer(p, inp, ids_ref, w.cpu().numpy())
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
+    y_ref = oracle_layer(p, inp, ids_ref, w_ref)
     assert_close(bits16(y), y_ref, TOL[p.wdtype], str(cfg))
 
 
@@ -475,7 +522,7 @@ def test_token_permutation_equivariance():
 
 # --------------------------------------------------- full-size, sampled ---
 
-def sampled_check(name, n_samples=6):
+def sampled_check(name):
     p = synth.Problem.named(name)
     log(f"full-size {name}: generating inputs on the device")
     d = synth.make_inputs(p, DEV)
@@ -483,19 +530,15 @@ def sampled_check(name, n_samples=6):
     y = run_layer(p, d, ids, w)
     torch.cuda.synchronize()
     ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
-    ids_ref, _ = route_oracle(p, d.logits.cpu().numpy(), d.score_bias)
+    ids_ref, w_ref = route_oracle(p, d.logits.cpu().numpy(), d.score_bias)
     assert np.array_equal(ids_np, ids_ref)
-    # samples: first, last, and tokens routed to the busiest expert
-    counts = np.bincount(ids_np.reshape(-1), minlength=p.E)
-    busiest = np.nonzero((ids_np == counts.argmax()).any(1))[0]
-    rng = np.random.default_rng(0)
-    toks = sorted(set([0, p.M - 1] + list(rng.choice(busiest, 2, replace=False)) +
-                      list(rng.choice(p.M, n_samples - 4, replace=False))))
-    experts = sorted(set(ids_np[toks].reshape(-1).tolist()))
-    remap = {e: i for i, e in enumerate(experts)}
-    sub_ids = np.vectorize(remap.get)(ids_np[toks]).astype(np.int32)
+    assert np.abs(w_np - w_ref).max() <= 1e-6 * max(1.0, p.routed_scale)
+    # one real row of every block of the layout (every tile), single-token experts,
+    # first and last tokens, random ones up to 128
+    toks = sampled.pick_tokens(ids_ref, p.E, p.block_m, chunk=p.chunk_tokens)
+    experts, sub_ids = sampled.expert_subset(ids_ref, toks, p.E)
     sel = torch.tensor(experts, device=DEV)
-    log(f"full-size {name}: oracle on tokens {toks} ({len(experts)} experts)")
+    log(f"full-size {name}: oracle on {len(toks)} tokens ({len(experts)} experts)")
     sub = synth.Inputs(d.x[toks].cpu(), None,
                        None if d.w13 is None else d.w13[sel].cpu(),
                        None if d.w2 is None else d.w2[sel].cpu(),
@@ -503,7 +546,7 @@ def sampled_check(name, n_samples=6):
                        None if d.w13s is None else d.w13s[sel].cpu(),
                        None if d.w2q is None else d.w2q[sel].cpu(),
                        None if d.w2s is None else d.w2s[sel].cpu())
-    y_ref = oracle_layer(p, sub, sub_ids, w_np[toks])
+    y_ref = oracle_layer(p, sub, sub_ids, w_ref[toks])
     assert_close(bits16(y[toks]), y_ref, TOL[p.wdtype], name)
     assert bool(torch.isfinite(y.float()).all())
 
@@ -542,7 +585,9 @@ def test_layer_chunked(cfg):
     y_in = run_layer(p, d, ids, w, out=d.x)
     torch.cuda.synchronize()
     assert torch.equal(y_in, y) and not torch.equal(d.x, x_copy)
-    y_ref = oracle_layer(p, inp, ids.cpu().numpy(), w.cpu().numpy())
+    ids_ref, w_ref = oracle.topk(inp.logits.numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    y_ref = oracle_layer(p, inp, ids_ref, w_ref)
     assert_close(bits16(y), y_ref, TOL[p.wdtype], str(cfg))
     assert_close(bits16(y), bits16(one), TOL[p.wdtype], "chunked vs one pass")
     if p.chunk_tokens >= p.M:

@@ -82,7 +82,11 @@ def test_random_problem_matches_oracle(cfg):
         y = moe.fused_experts(d.x, w13, w2, ids, w, p.block_m, apply_router_weight_on_input=on,
                               weight_layout=layout, expert_map=emap, chunk_tokens=p.chunk_tokens)
     torch.cuda.synchronize()
-    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    # the oracle's own router: ids bit for bit, weights within 1e-6, and its weights feed
+    # the oracle layer
+    ids_np, w_np = oracle.topk(inp.logits.numpy(), p.topk)
+    assert np.array_equal(ids.cpu().numpy(), ids_np)
+    assert np.abs(w.cpu().numpy() - w_np).max() <= 1e-6
     em = None if inp.expert_map is None else inp.expert_map.numpy()
     if p.wdtype in ("mxfp8", "w4a8"):
         y_ref = oracle.fused_experts_mx(bits16(inp.x), bits8(inp.w13q) if p.wdtype == "mxfp8" else inp.w13q.numpy(),
