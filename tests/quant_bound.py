@@ -76,7 +76,8 @@ def quant_err(vabs: np.ndarray, group: int, e8m0: bool) -> np.ndarray:
 
 
 def silu(g):
-    return g / (1.0 + np.exp(-g))
+    with np.errstate(over="ignore"):   # exp(-g) = inf for very negative g: SiLU(g) = -0
+        return g / (1.0 + np.exp(-g))
 
 
 class Act:
