@@ -274,6 +274,32 @@ moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w1
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fused_experts for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * arguments as fused_experts without the workspace; the layer's scratch lives
+ * in a static device array of the library, 64 MiB on every GPU the library runs
+ * on, held until the process ends. Nothing is allocated or freed by the call.
+ *   Returns MOE_E_WORKSPACE when the problem needs more than 64 MiB of scratch:
+ *   moe_workspace_bytes(p) without its second-GEMM split-K part, i.e. with
+ *   cap = moe_align_capacity(M', topk, E, block_m) and M' = min(M, chunk_tokens
+ *   if set), about cap * (max(2 I, H) * 2 + I * 2) + 4 (cap + M' topk) bytes for
+ *   bf16 (decode-sized problems and token chunks fit; set chunk_tokens for
+ *   larger M). MOE_E_INVALID for num_global_experts != 0 (no expert map here).
+ *   The second GEMM sums every tile's K range in one pass (the split-K tail of
+ *   fused_experts needs 64 MiB of partials on its own), so with bf16 weights and
+ *   block_m 128 / 256 the bits can differ from fused_experts' in the last place;
+ *   elsewhere they are the same.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a GPU
+ *   (on different streams, or from different threads without ordering) race and
+ *   give undefined results. Everything the layer reads from the array it first
+ *   writes in the same call, so its contents between calls do not matter.
+ */
+moe_status_t fused_experts_static(const moe_problem_t *p, const void *x, const void *w13,
+                                  const float *w13_scale, const void *w2, const float *w2_scale,
+                                  const int32_t *topk_ids, const float *topk_weights, void *y,
+                                  void *stream);
+
+/*
  * The same layer on one rank of an expert-parallel shard ("vLLM
  * modular_kernel.py notes", the expert_map argument of fused_experts: a table
  * from global expert ids to this rank's experts, -1 for experts held by other

@@ -29,7 +29,8 @@ EXPORTS = ("moe_topk", "moe_topk_grouped", "moe_align_capacity", "moe_align_bloc
            "moe_expert_gemm", "moe_silu_and_mul",
            "moe_expert_gemm_act_supported", "moe_expert_gemm_act", "moe_permute_scales",
            "moe_unpermute_reduce", "moe_pack_weights", "moe_batched_workspace_bytes",
-           "moe_batched_experts", "moe_quant_mx_groups", "moe_pack_mx_scales", "moe_status_string")
+           "moe_batched_experts", "moe_quant_mx_groups", "moe_pack_mx_scales", "moe_status_string",
+           "fused_experts_static")
 
 
 class MoeProblem(ctypes.Structure):
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_size_t, _P]
         L.fused_experts_ep.argtypes = [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, ctypes.c_size_t, _P]
+        L.fused_experts_static.argtypes = [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P]
         PP = ctypes.POINTER(MoeProblem)
         L.moe_expert_gemm_workspace_bytes.argtypes = [PP]
         L.moe_expert_gemm_workspace_bytes.restype = ctypes.c_size_t
@@ -93,7 +95,8 @@ def lib() -> ctypes.CDLL:
                      "moe_quant_fp8_groups", "fused_experts", "fused_experts_ep",
                      "moe_expert_gemm", "moe_silu_and_mul", "moe_permute_scales",
                      "moe_expert_gemm_act", "moe_unpermute_reduce", "moe_pack_weights",
-                     "moe_batched_experts", "moe_quant_mx_groups", "moe_pack_mx_scales"):
+                     "moe_batched_experts", "moe_quant_mx_groups", "moe_pack_mx_scales",
+                     "fused_experts_static"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -271,18 +274,10 @@ def workspace_for(p: MoeProblem, device="cuda") -> torch.Tensor:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids: torch.Tensor,
-                  topk_weights: torch.Tensor, block_m: int, w13_scale: torch.Tensor | None = None,
-                  w2_scale: torch.Tensor | None = None, apply_router_weight_on_input=False,
-                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                  stream=None, weight_layout=MOE_LAYOUT_ROWS,
-                  expert_map: torch.Tensor | None = None, chunk_tokens: int = 0) -> torch.Tensor:
-    """y = fused MoE expert forward (bf16 [M, H]). `out` may be `x` (in place).
-
-    weight_layout MOE_LAYOUT_TILED: w13 and w2 come from moe_pack_weights (same shapes).
-    expert_map [G] int32 (one expert-parallel rank): topk_ids are global ids in [0, G),
-    w13 / w2 hold this rank's E experts, and y sums only the slots of those experts.
-    chunk_tokens > 0: the layer runs on chunks of that many tokens (workspace for one chunk)."""
+def _layer_problem(x, w13, w2, topk_ids, topk_weights, block_m, w13_scale, w2_scale,
+                   apply_router_weight_on_input, weight_layout, expert_map, chunk_tokens, what) -> MoeProblem:
+    """Checks the layer's tensors (dtypes, contiguity, shapes, scale shapes) and returns the
+    problem they describe."""
     if expert_map is not None:
         _need(expert_map, torch.int32, "expert_map")
     _need(x, torch.bfloat16, "x")
@@ -303,13 +298,30 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
     d = 2 if w4 else 1
     if H2 * d != H or tuple(w2.shape) != (E, H, N2 // 2 // d) or topk_ids.shape != topk_weights.shape \
             or topk_ids.shape[0] != M:
-        raise ValueError("fused_experts: inconsistent shapes")
+        raise ValueError(f"{what}: inconsistent shapes")
     p = make_problem(M, H, N2 // 2, E, topk_ids.shape[1], block_m,
                      MOE_W_W4A8_MXFP4 if w4 else MOE_W_MXFP8 if mx else
                      MOE_W_FP8_E4M3_BLOCK128 if fp8 else MOE_W_BF16,
                      apply_router_weight_on_input, weight_layout,
                      0 if expert_map is None else expert_map.numel(), chunk_tokens)
-    check_weight_scales(p.wdtype, E, H, N2 // 2, w13_scale, w2_scale, "fused_experts")
+    check_weight_scales(p.wdtype, E, H, N2 // 2, w13_scale, w2_scale, what)
+    return p
+
+
+def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids: torch.Tensor,
+                  topk_weights: torch.Tensor, block_m: int, w13_scale: torch.Tensor | None = None,
+                  w2_scale: torch.Tensor | None = None, apply_router_weight_on_input=False,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None, weight_layout=MOE_LAYOUT_ROWS,
+                  expert_map: torch.Tensor | None = None, chunk_tokens: int = 0) -> torch.Tensor:
+    """y = fused MoE expert forward (bf16 [M, H]). `out` may be `x` (in place).
+
+    weight_layout MOE_LAYOUT_TILED: w13 and w2 come from moe_pack_weights (same shapes).
+    expert_map [G] int32 (one expert-parallel rank): topk_ids are global ids in [0, G),
+    w13 / w2 hold this rank's E experts, and y sums only the slots of those experts.
+    chunk_tokens > 0: the layer runs on chunks of that many tokens (workspace for one chunk)."""
+    p = _layer_problem(x, w13, w2, topk_ids, topk_weights, block_m, w13_scale, w2_scale,
+                       apply_router_weight_on_input, weight_layout, expert_map, chunk_tokens, "fused_experts")
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
@@ -325,6 +337,25 @@ def fused_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids
                                       _ptr(topk_weights), _ptr(out), _ptr(workspace),
                                       workspace.numel(), _stream(stream)),
                "fused_experts_ep")
+    return out
+
+
+def fused_experts_static(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, topk_ids: torch.Tensor,
+                         topk_weights: torch.Tensor, block_m: int, out: torch.Tensor,
+                         w13_scale: torch.Tensor | None = None, w2_scale: torch.Tensor | None = None,
+                         apply_router_weight_on_input=False, stream=None, weight_layout=MOE_LAYOUT_ROWS,
+                         chunk_tokens: int = 0) -> torch.Tensor:
+    """fused_experts with the library's static scratch (64 MiB per GPU) instead of a
+    workspace, for callers that cannot allocate: `out` [M, H] bf16 is required (this call
+    allocates nothing). Raises MoeError (workspace too small) when the problem needs more
+    scratch than that."""
+    p = _layer_problem(x, w13, w2, topk_ids, topk_weights, block_m, w13_scale, w2_scale,
+                       apply_router_weight_on_input, weight_layout, None, chunk_tokens, "fused_experts_static")
+    _need_size(out, _BF, p.M * p.H, "out")
+    _check(lib().fused_experts_static(ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                      _ptr(w2_scale), _ptr(topk_ids), _ptr(topk_weights), _ptr(out),
+                                      _stream(stream)),
+           "fused_experts_static")
     return out
 
 

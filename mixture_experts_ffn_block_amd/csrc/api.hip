@@ -10,6 +10,8 @@
 // workspace is one caller-owned block carved into the intermediate buffers;
 // the GEMM1 output and the GEMM2 output share storage because their
 // lifetimes do not overlap ("fused_moe.py analysis", intermediate caches).
+#include <atomic>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -76,7 +78,9 @@ int64_t split_bytes(const moe_problem_t& p) {
     return kSplitSlots * kTileOutputs * 4 + kSplitSlots * 4;
 }
 
-Layout layout(const moe_problem_t& p, const Rows& rows) {
+// with_split = false: no room for the second GEMM's split-K tail (the layer then
+// sums every tile's K range in one pass)
+Layout layout(const moe_problem_t& p, const Rows& rows, bool with_split = true) {
     Layout L{};
     L.R = rows.R;
     L.cap = rows.cap;
@@ -94,7 +98,7 @@ Layout layout(const moe_problem_t& p, const Rows& rows) {
     L.ho = take(h_bytes > o_bytes ? h_bytes : o_bytes);
     L.z = take(L.cap * p.I * (fp8 ? 1 : 2));
     L.zs = fp8 ? take(L.cap * (p.I / 128) * 4) : -1;   // [I/128, cap]
-    L.split = split_bytes(p) ? take(split_bytes(p)) : -1;
+    L.split = (with_split && split_bytes(p)) ? take(split_bytes(p)) : -1;
     L.total = off;
     return L;
 }
@@ -388,13 +392,13 @@ moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* 
                        const float* w13_scale, const void* w2, const float* w2_scale,
                        const int32_t* topk_ids, const float* topk_weights, void* y,
                        void* workspace, size_t workspace_bytes, void* stream,
-                       bool unweighted = false) {
+                       bool unweighted = false, bool with_split = true) {
     if (p->M == 0) return MOE_OK;
     const bool fp8 = q8(*p);
     if (!x || !w13 || !w2 || !topk_ids || !y || (!topk_weights && !unweighted)) return MOE_E_INVALID;
     if (fp8 && (!w13_scale || !w2_scale)) return MOE_E_INVALID;
     const Rows rows = routed_rows(*p);
-    const Layout L = layout(*p, rows);
+    const Layout L = layout(*p, rows, with_split);
     if (!workspace || workspace_bytes < static_cast<size_t>(L.total)) return MOE_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return MOE_E_INVALID;
 
@@ -471,11 +475,12 @@ moe_status_t check_batched(const moe_problem_t* p) {
 moe_status_t run_chunked(const moe_problem_t* p, const int32_t* emap, const void* x, const void* w13,
                          const float* w13_scale, const void* w2, const float* w2_scale,
                          const int32_t* topk_ids, const float* topk_weights, void* y,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         bool with_split = true) {
     const int64_t chunk = chunk_of(*p);
     if (chunk == p->M)
         return run_fused(p, emap, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y,
-                         workspace, workspace_bytes, stream);
+                         workspace, workspace_bytes, stream, false, with_split);
     if (!x || !topk_ids || !topk_weights || !y) return MOE_E_INVALID;
     const int64_t row = static_cast<int64_t>(p->H) * 2;  // bytes of one x / y row
     for (int64_t t0 = 0; t0 < p->M; t0 += chunk) {
@@ -483,15 +488,61 @@ moe_status_t run_chunked(const moe_problem_t* p, const int32_t* emap, const void
         const moe_status_t st = run_fused(
             &q, emap, static_cast<const uint8_t*>(x) + t0 * row, w13, w13_scale, w2, w2_scale,
             topk_ids + t0 * p->topk, topk_weights + t0 * p->topk, static_cast<uint8_t*>(y) + t0 * row,
-            workspace, workspace_bytes, stream);
+            workspace, workspace_bytes, stream, false, with_split);
         if (st != MOE_OK) return st;
     }
     return MOE_OK;
 }
 
+// ---- scratch for callers that cannot allocate ------------------------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends. In host code the array's name is only a host-side
+// stand-in, so its device address is looked up once per device (with that
+// device current, on the entry point's first call there) and kept; kernels and
+// copies use that address, never the name.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> scratch_addr[kMaxDevices];
+
+// this device's copy of `scratch` (null if the lookup fails); concurrent first calls
+// look up and store the same address
+uint8_t* static_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    uint8_t* ptr = scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return nullptr;
+        ptr = static_cast<uint8_t*>(a);
+        scratch_addr[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status_t fused_experts_static(const moe_problem_t* p, const void* x, const void* w13,
+                                  const float* w13_scale, const void* w2, const float* w2_scale,
+                                  const int32_t* topk_ids, const float* topk_weights, void* y,
+                                  void* stream) {
+    const moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->num_global_experts != 0) return MOE_E_INVALID;
+    if (p->M == 0) return MOE_OK;
+    if (!x || !w13 || !w2 || !topk_ids || !topk_weights || !y) return MOE_E_INVALID;
+    if (q8(*p) && (!w13_scale || !w2_scale)) return MOE_E_INVALID;
+    const moe_problem_t q = chunk_problem(*p, chunk_of(*p));
+    const int64_t need = layout(q, routed_rows(q), false).total;
+    if (need > static_cast<int64_t>(kStaticScratchBytes)) return MOE_E_WORKSPACE;
+    uint8_t* ws = static_scratch();
+    if (ws == nullptr) return MOE_E_HIP;
+    return run_chunked(p, nullptr, x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, y, ws,
+                       kStaticScratchBytes, stream, false);
+}
 
 moe_status_t fused_experts(const moe_problem_t* p, const void* x, const void* w13,
                            const float* w13_scale, const void* w2, const float* w2_scale,

@@ -253,3 +253,24 @@ def test_weight_scale_shapes_are_checked_exactly():
     for wd, a, b in bad:
         with pytest.raises(ValueError):
             moe.check_weight_scales(wd, E, H, I, a, b, "t")
+
+
+def test_static_scratch_entry_point_validation():
+    # fused_experts_static: the checks of fused_experts, an expert map refused, and a
+    # problem whose scratch exceeds the library's 64 MiB array refused before any launch
+    L = moe.lib()
+    d = ctypes.c_void_p(1 << 20)
+    for kw, status in [(dict(M=-1), moe.MOE_E_INVALID), (dict(topk=9), moe.MOE_E_INVALID),
+                       (dict(H=200), moe.MOE_E_UNSUPPORTED), (dict(block_m=48), moe.MOE_E_UNSUPPORTED)]:
+        assert L.fused_experts_static(ctypes.byref(P(**kw)), d, d, None, d, None, d, d, d, None) == status
+    assert L.fused_experts_static(ctypes.byref(P(M=0)), None, None, None, None, None, None, None, None,
+                                  None) == moe.MOE_OK
+    assert L.fused_experts_static(ctypes.byref(P()), None, d, None, d, None, d, d, d, None) == moe.MOE_E_INVALID
+    ep = moe.make_problem(64, 256, 512, 4, 2, 16, num_global_experts=8)
+    assert L.fused_experts_static(ctypes.byref(ep), d, d, None, d, None, d, d, d, None) == moe.MOE_E_INVALID
+    pf = P(wdtype=moe.MOE_W_FP8_E4M3_BLOCK128, block_m=64)
+    assert L.fused_experts_static(ctypes.byref(pf), d, d, None, d, None, d, d, d, None) == moe.MOE_E_INVALID
+    # the Mixtral-shaped prefill needs ~1.5 GB of scratch; the decode workload's fits
+    big = moe.make_problem(4096, 4096, 14336, 8, 2, 256)
+    assert L.fused_experts_static(ctypes.byref(big), d, d, None, d, None, d, d, d, None) == moe.MOE_E_WORKSPACE
+    assert moe.moe_workspace_bytes(moe.make_problem(32, 2048, 768, 128, 8, 16)) < 64 << 20
