@@ -10,7 +10,7 @@
 // gfx950 design: one 1024-thread workgroup (16 wavefronts). Each wavefront
 // owns a contiguous chunk of items.
 //   1. per-wave expert histogram in LDS (counts do not depend on order);
-//   2. per-expert totals, padded counts, an LDS scan over experts, and each
+//   2. per-expert totals, padded counts, a one-wavefront scan over experts, and each
 //      wave's starting offset inside every expert segment;
 //   3. stable scatter: a wave takes 64 items at a time; lanes holding the same
 //      expert find each other with 8 ballots over the bits of the expert id
@@ -51,6 +51,31 @@ __device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ 
     return static_cast<unsigned>(id) < static_cast<unsigned>(E_global) ? emap[id] : -1;
 }
 
+// In place, by one wavefront: seg_start[1 .. kMaxE] holds the padded size of each
+// expert and becomes the inclusive prefix sum (seg_start[0] stays 0). Lane l sums
+// experts 4l .. 4l+3; a shuffle scan over the lanes gives each its exclusive prefix.
+__device__ __forceinline__ void scan_segments(int32_t* seg_start, int lane) {
+    static_assert(kMaxE == 4 * MOE_WAVE, "four experts per lane");
+    int v[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = seg_start[4 * lane + i + 1];
+        sum += v[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+        const int t = __shfl_up(incl, o, MOE_WAVE);
+        if (lane >= o) incl += t;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        run += v[i];
+        seg_start[4 * lane + i + 1] = run;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void align_kernel(
     const int32_t* __restrict__ ids, int64_t R, int E, int B, int64_t cap,
     const int32_t* __restrict__ emap, int E_global,
@@ -75,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     }
     __syncthreads();
 
-    // 2. totals, padded sizes, scan over experts (Hillis-Steele in LDS)
+    // 2. totals, padded sizes, scan over experts
     int n = 0, padded = 0;
     if (tid < E) {
         for (int w = 0; w < kWaves; ++w) n += wave_off[w][tid];
@@ -85,13 +110,10 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     if (tid < kMaxE) seg_start[tid + 1] = tid < E ? padded : 0;
     if (tid == 0) seg_start[0] = 0;
     __syncthreads();
-    for (int d = 1; d < kMaxE; d <<= 1) {
-        int add = 0;
-        if (tid < kMaxE && tid + 1 - d >= 1) add = seg_start[tid + 1 - d];
-        __syncthreads();
-        if (tid < kMaxE) seg_start[tid + 1] += add;
-        __syncthreads();
-    }
+    // one wavefront scans the padded sizes: lane l sums experts 4l .. 4l+3, a
+    // shuffle scan over the lanes gives each lane its exclusive prefix
+    if (wave == 0) scan_segments(seg_start, lane);
+    __syncthreads();
     // seg_start[e] is now the inclusive sum over experts < e of padded sizes
     if (tid < E) {
         int run = seg_start[tid];
@@ -203,13 +225,8 @@ __global__ __launch_bounds__(kMultiThreads) void align_place_kernel(
     if (tid == 0) seg_start[0] = 0;
     for (int i = tid; i < kMultiWaves * kMaxE; i += kMultiThreads) (&wave_off[0][0])[i] = 0;
     __syncthreads();
-    for (int d = 1; d < kMaxE; d <<= 1) {
-        int add = 0;
-        if (tid < kMaxE && tid + 1 - d >= 1) add = seg_start[tid + 1 - d];
-        __syncthreads();
-        if (tid < kMaxE) seg_start[tid + 1] += add;
-        __syncthreads();
-    }
+    // (read after the barrier that follows the counts below)
+    if (wave == 0) scan_segments(seg_start, lane);
 
     // per-wave counts of this chunk (wave w owns items [r0 + 256 w, r0 + 256 (w + 1)))
     const int64_t r0 = static_cast<int64_t>(g) * kChunk + wave * (kChunk / kMultiWaves);
