@@ -173,8 +173,12 @@ class Step:
                                p.routed_scale, out=(self.ids, self.w))
 
     def fused(self):
-        m, d = self.moe, self.d
         self.route()
+        self.experts()
+
+    def experts(self):
+        """fused_experts alone, on the router's last ids and weights."""
+        m, d = self.moe, self.d
         m.fused_experts(d.x, self.w13, self.w2, self.ids, self.w, self.p.block_m,
                         self.w13s, self.w2s, self.p.apply_router_weight_on_input, out=self.y,
                         workspace=self.ws, weight_layout=self.wl, expert_map=self.emap,
@@ -273,6 +277,9 @@ class BatchedStep(Step):
     def fused(self):
         self.moe.moe_batched_experts(self.a, self.counts, self.w13, self.w2, self.p.block_m,
                                      out=self.out, workspace=self.bws, weight_layout=self.wl)
+
+    def experts(self):
+        self.fused()
 
     def staged(self, ev):
         m, q = self.moe, self.q
@@ -562,6 +569,14 @@ def main():
     wall = time.perf_counter() - t_wall
     ms = marks[0].elapsed_time(marks[-1]) / args.steps
     per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    # fused_experts alone (the router's output already in place), K calls
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record()
+    for _ in range(args.steps):
+        st.experts()
+    b_ev.record()
+    torch.cuda.synchronize()
+    ms_experts = a_ev.elapsed_time(b_ev) / args.steps
 
     # stage breakdown: the same kernels stage by stage, HIP events on the same stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
@@ -640,10 +655,19 @@ def main():
                       if chunked else {})},
         "ms_per_step_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "step_roofline_frac": round(t_star / (ms * 1e-3), 4),
+        # the step's algorithmic FLOP and bytes against the spec peaks, each on its own
+        "step_fractions": {"mfma": round(alg["flops"] / (PEAK_TFLOPS[dt] * 1e12) / (ms * 1e-3), 4),
+                           "hbm_algorithmic": round(alg["bytes"] / (PEAK_HBM_GBS * 1e9) / (ms * 1e-3), 4)},
+        "step_bytes_algorithmic": int(alg["bytes"]),
+        "ms_fused_experts": round(ms_experts, 4),
         "roofline": roof,
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_roofline": stage_roofline(work, stage_ms, dt),
         "staged_ms_per_step": round(staged_total, 4),
+        # as built: what the staged kernels read and write at least, intermediates included
+        "staged_bytes_as_built": int(sum(w["bytes"] for w in work.values())),
+        "staged_hbm_frac_as_built": round(sum(w["bytes"] for w in work.values()) / (PEAK_HBM_GBS * 1e9)
+                                          / (staged_total * 1e-3), 4),
         "empty_event_interval_ms": round(empty_ms, 4),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "hbm_measured": hbm,
