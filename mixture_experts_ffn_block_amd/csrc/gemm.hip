@@ -744,11 +744,13 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
             // Every K range writes its fp32 partial tile (in accumulator register
             // order: index ((wave, tn, tm, r), lane)), then counts itself in; the
             // last to arrive sums the S partials in range order (deterministic)
-            // and stores the tile. Ordering: the workgroup barrier puts every
-            // wave's partial stores before thread 0's counter update, which is an
-            // agent-scope release (the partials become visible to every CU, on any
-            // XCD) and acquire (the last arrival then sees every other range's
-            // partials). One release and one acquire per workgroup, not per wave.
+            // and stores the tile. Ordering: every wave waits until its own partial
+            // stores are complete (acknowledged by L2; the workgroup barrier alone
+            // does not wait for them on this target), then the barrier, then thread
+            // 0's counter update, an agent-scope release (L2 written back, so the
+            // partials are visible to every CU, on any XCD) and acquire (the last
+            // arrival then sees every other range's partials). One release and one
+            // acquire per workgroup, not per wave.
             // The ranges of a tile are still placed on one XCD, but only so that
             // their partials meet in one L2; correctness does not depend on it.
             constexpr int TILE_F = C::NW * TN * TM * 16 * 64;
@@ -761,6 +763,7 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         part[(((wave * TN + tn) * TM + tm) * 16 + r) * 64 + lane] = acc[tn][tm][r];
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             int* cnt = p.part_cnt + sp.tail_tile;
             int* flag = reinterpret_cast<int*>(smem);
