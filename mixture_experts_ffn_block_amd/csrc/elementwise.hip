@@ -22,30 +22,32 @@
 namespace {
 
 // ---------------------------------------------------------------- bf16 act --
-// One thread per 8 output elements. Rows >= num_tokens_post_padded are not
+// One thread per 8 output elements of a row, the rows strided over the grid's
+// y dimension (at most 65535 of them). Rows >= num_tokens_post_padded are not
 // touched; padding rows (sentinel item) are written as zeros.
 __global__ __launch_bounds__(256) void silu_mul_bf16_kernel(
     const bf16_t* __restrict__ h, bf16_t* __restrict__ z, const int32_t* __restrict__ sorted,
     const float* __restrict__ weights, int R, int I, const int32_t* __restrict__ npp_ptr,
     int on_input) {
-    const int64_t pos = blockIdx.y;
-    if (pos >= *npp_ptr) return;
     const int i0 = (blockIdx.x * 256 + threadIdx.x) * 8;
     if (i0 >= I) return;
-    const int r = sorted[pos];
-    u32x4_t out{0, 0, 0, 0};
-    if (r < R) {
-        const float alpha = on_input ? weights[r] : 1.0f;
-        const u32x4_t g = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + i0);
-        const u32x4_t u = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + I + i0);
+    const int64_t npp = *npp_ptr;
+    for (int64_t pos = blockIdx.y; pos < npp; pos += gridDim.y) {
+        const int r = sorted[pos];
+        u32x4_t out{0, 0, 0, 0};
+        if (r < R) {
+            const float alpha = on_input ? weights[r] : 1.0f;
+            const u32x4_t g = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + i0);
+            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + I + i0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float g0 = __uint_as_float(g[j] << 16), g1 = __uint_as_float(g[j] & 0xffff0000u);
-            const float u0 = __uint_as_float(u[j] << 16), u1 = __uint_as_float(u[j] & 0xffff0000u);
-            out[j] = pack_bf16x2(alpha * silu_f32(g0) * u0, alpha * silu_f32(g1) * u1);
+            for (int j = 0; j < 4; ++j) {
+                const float g0 = __uint_as_float(g[j] << 16), g1 = __uint_as_float(g[j] & 0xffff0000u);
+                const float u0 = __uint_as_float(u[j] << 16), u1 = __uint_as_float(u[j] & 0xffff0000u);
+                out[j] = pack_bf16x2(alpha * silu_f32(g0) * u0, alpha * silu_f32(g1) * u1);
+            }
         }
+        *reinterpret_cast<u32x4_t*>(z + pos * I + i0) = out;
     }
-    *reinterpret_cast<u32x4_t*>(z + pos * I + i0) = out;
 }
 
 // ------------------------------------------------------ fp8 group quantiser --
@@ -67,55 +69,60 @@ __device__ __forceinline__ u32x2_t quant_group8(const float (&v)[8], float* scal
 }
 
 // SiLU-and-mul, then per-row per-128 fp8 quantisation of the fp32 result.
-// One wavefront per (row, 4 groups). The scales are stored group-major,
+// One wavefront per (row, 4 groups), rows strided over the grid's y dimension.
+// The scales are stored group-major,
 // zs[g * cap + pos], so that the GEMM reads a block's 128 row scales of one
 // group as one contiguous run.
 __global__ __launch_bounds__(256) void silu_mul_fp8_kernel(
     const bf16_t* __restrict__ h, uint8_t* __restrict__ zq, float* __restrict__ zs,
     const int32_t* __restrict__ sorted, const float* __restrict__ weights, int R, int I,
     int64_t cap, const int32_t* __restrict__ npp_ptr, int on_input) {
-    const int64_t pos = blockIdx.y;
-    if (pos >= *npp_ptr) return;
     const int lane = threadIdx.x & 63;
     const int i0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512 + lane * 8;
-    if (i0 >= I) return;
-    const int r = sorted[pos];
-    float v[8];
-    if (r < R) {
-        const float alpha = on_input ? weights[r] : 1.0f;
-        const u32x4_t g = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + i0);
-        const u32x4_t u = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + I + i0);
+    if (i0 >= I) return;  // I is a multiple of 128: whole groups leave together
+    const int64_t npp = *npp_ptr;
+    for (int64_t pos = blockIdx.y; pos < npp; pos += gridDim.y) {
+        const int r = sorted[pos];
+        float v[8];
+        if (r < R) {
+            const float alpha = on_input ? weights[r] : 1.0f;
+            const u32x4_t g = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + i0);
+            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(h + pos * 2 * I + I + i0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[2 * j] = alpha * silu_f32(__uint_as_float(g[j] << 16)) * __uint_as_float(u[j] << 16);
-            v[2 * j + 1] = alpha * silu_f32(__uint_as_float(g[j] & 0xffff0000u)) *
-                           __uint_as_float(u[j] & 0xffff0000u);
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = alpha * silu_f32(__uint_as_float(g[j] << 16)) * __uint_as_float(u[j] << 16);
+                v[2 * j + 1] = alpha * silu_f32(__uint_as_float(g[j] & 0xffff0000u)) *
+                               __uint_as_float(u[j] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = 0.0f;
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+        const u32x2_t q = quant_group8(v, zs + (i0 / 128) * cap + pos, (lane & 15) == 0);
+        *reinterpret_cast<u32x2_t*>(zq + pos * I + i0) = q;
     }
-    const u32x2_t q = quant_group8(v, zs + (i0 / 128) * cap + pos, (lane & 15) == 0);
-    *reinterpret_cast<u32x2_t*>(zq + pos * I + i0) = q;
 }
 
-// Per-row, per-128-column quantisation of a bf16 matrix [rows, cols].
+// Per-row, per-128-column quantisation of a bf16 matrix [rows, cols]; rows strided
+// over the grid's y dimension.
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict__ x,
                                                         uint8_t* __restrict__ q,
-                                                        float* __restrict__ scale, int cols) {
-    const int64_t row = blockIdx.y;
+                                                        float* __restrict__ scale, int cols,
+                                                        int64_t rows) {
     const int lane = threadIdx.x & 63;
     const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512 + lane * 8;
-    if (c0 >= cols) return;
-    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + row * cols + c0);
-    float v[8];
+    if (c0 >= cols) return;  // cols is a multiple of 128: whole groups leave together
+    for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + row * cols + c0);
+        float v[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[2 * j] = __uint_as_float(xv[j] << 16);
-        v[2 * j + 1] = __uint_as_float(xv[j] & 0xffff0000u);
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(xv[j] << 16);
+            v[2 * j + 1] = __uint_as_float(xv[j] & 0xffff0000u);
+        }
+        const u32x2_t qq = quant_group8(v, scale + row * (cols / 128) + c0 / 128, (lane & 15) == 0);
+        *reinterpret_cast<u32x2_t*>(q + row * cols + c0) = qq;
     }
-    const u32x2_t qq = quant_group8(v, scale + row * (cols / 128) + c0 / 128, (lane & 15) == 0);
-    *reinterpret_cast<u32x2_t*>(q + row * cols + c0) = qq;
 }
 
 // MXFP8 activations ("DeepGEMM FusedMoE on Blackwell", MXFP8 1x32): each 32
@@ -123,30 +130,32 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict
 // amax <= 448 s; codes E4M3(v / s). Four lanes hold a block (8 values each).
 __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const bf16_t* __restrict__ x,
                                                           uint8_t* __restrict__ q,
-                                                          uint8_t* __restrict__ scale, int cols) {
-    const int64_t row = blockIdx.y;
+                                                          uint8_t* __restrict__ scale, int cols,
+                                                          int64_t rows) {
     const int lane = threadIdx.x & 63;
     const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512 + lane * 8;
     if (c0 >= cols) return;  // cols is a multiple of 128: whole blocks only
-    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + row * cols + c0);
-    float v[8], m = 0.0f;
+    for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + row * cols + c0);
+        float v[8], m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[2 * j] = __uint_as_float(xv[j] << 16);
-        v[2 * j + 1] = __uint_as_float(xv[j] & 0xffff0000u);
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(xv[j] << 16);
+            v[2 * j + 1] = __uint_as_float(xv[j] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        const uint32_t code = mx_scale_code(m, 448.0f);
+        const float inv = ldexpf(1.0f, 127 - static_cast<int>(code));
+        float c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = fminf(fmaxf(v[j] * inv, -448.0f), 448.0f);
+        *reinterpret_cast<u32x2_t*>(q + row * cols + c0) =
+            u32x2_t{cvt_e4m3x4(c[0], c[1], c[2], c[3]), cvt_e4m3x4(c[4], c[5], c[6], c[7])};
+        if ((lane & 3) == 0) scale[row * (cols / 32) + c0 / 32] = static_cast<uint8_t>(code);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
-    const uint32_t code = mx_scale_code(m, 448.0f);
-    const float inv = ldexpf(1.0f, 127 - static_cast<int>(code));
-    float c[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) c[j] = fminf(fmaxf(v[j] * inv, -448.0f), 448.0f);
-    *reinterpret_cast<u32x2_t*>(q + row * cols + c0) =
-        u32x2_t{cvt_e4m3x4(c[0], c[1], c[2], c[3]), cvt_e4m3x4(c[4], c[5], c[6], c[7])};
-    if ((lane & 3) == 0) scale[row * (cols / 32) + c0 / 32] = static_cast<uint8_t>(code);
 }
 
 // MX weight scales into the kernels' order: natural [E, N, K/32] bytes ->
@@ -183,26 +192,27 @@ __global__ __launch_bounds__(256) void reduce_kernel(const bf16_t* __restrict__ 
                                                      const int32_t* __restrict__ inv_perm,
                                                      const float* __restrict__ weights, int k,
                                                      int H, int use_weights,
-                                                     bf16_t* __restrict__ y) {
-    const int64_t t = blockIdx.y;
+                                                     bf16_t* __restrict__ y, int64_t M) {
     const int n0 = (blockIdx.x * 256 + threadIdx.x) * 8;
     if (n0 >= H) return;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-        const int pos = inv_perm[t * k + j];
-        if (pos < 0) continue;
-        const float a = use_weights ? weights[t * k + j] : 1.0f;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o + static_cast<int64_t>(pos) * H + n0);
+    for (int64_t t = blockIdx.y; t < M; t += gridDim.y) {
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int j = 0; j < k; ++j) {
+            const int pos = inv_perm[t * k + j];
+            if (pos < 0) continue;
+            const float a = use_weights ? weights[t * k + j] : 1.0f;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o + static_cast<int64_t>(pos) * H + n0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += a * __uint_as_float(v[i] << 16);
-            acc[2 * i + 1] += a * __uint_as_float(v[i] & 0xffff0000u);
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += a * __uint_as_float(v[i] << 16);
+                acc[2 * i + 1] += a * __uint_as_float(v[i] & 0xffff0000u);
+            }
         }
-    }
-    u32x4_t out;
+        u32x4_t out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    *reinterpret_cast<u32x4_t*>(y + t * H + n0) = out;
+        for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+        *reinterpret_cast<u32x4_t*>(y + t * H + n0) = out;
+    }
 }
 
 // ------------------------------------------------------------- weight pack --
@@ -234,10 +244,15 @@ hipError_t launch_pack_tiled(const bf16_t* w, bf16_t* wp, int64_t E, int N, int 
     return hipGetLastError();
 }
 
+// rows go along the grid's y dimension, at most kMaxGridY of them; the kernels
+// stride over the rest
+constexpr int64_t kMaxGridY = 65535;
+unsigned grid_rows(int64_t rows) { return static_cast<unsigned>(rows < kMaxGridY ? (rows > 0 ? rows : 1) : kMaxGridY); }
+
 hipError_t launch_silu_mul_bf16(const bf16_t* h, bf16_t* z, const int32_t* sorted,
                                 const float* weights, int R, int I, int64_t cap,
                                 const int32_t* npp, int on_input, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(ceil_div(I / 8, 256)), static_cast<unsigned>(cap));
+    const dim3 grid(static_cast<unsigned>(ceil_div(I / 8, 256)), grid_rows(cap));
     hipLaunchKernelGGL(silu_mul_bf16_kernel, grid, dim3(256), 0, stream, h, z, sorted, weights, R,
                        I, npp, on_input);
     return hipGetLastError();
@@ -246,7 +261,7 @@ hipError_t launch_silu_mul_bf16(const bf16_t* h, bf16_t* z, const int32_t* sorte
 hipError_t launch_silu_mul_fp8(const bf16_t* h, uint8_t* zq, float* zs, const int32_t* sorted,
                                const float* weights, int R, int I, int64_t cap,
                                const int32_t* npp, int on_input, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(ceil_div(I, 2048)), static_cast<unsigned>(cap));
+    const dim3 grid(static_cast<unsigned>(ceil_div(I, 2048)), grid_rows(cap));
     hipLaunchKernelGGL(silu_mul_fp8_kernel, grid, dim3(256), 0, stream, h, zq, zs, sorted,
                        weights, R, I, cap, npp, on_input);
     return hipGetLastError();
@@ -263,15 +278,15 @@ hipError_t launch_permute_scales(const float* scale, int groups, int topk, int R
 
 hipError_t launch_quant_fp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q, float* scale,
                             hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(ceil_div(cols, 2048)), static_cast<unsigned>(rows));
-    hipLaunchKernelGGL(quant_fp8_kernel, grid, dim3(256), 0, stream, x, q, scale, cols);
+    const dim3 grid(static_cast<unsigned>(ceil_div(cols, 2048)), grid_rows(rows));
+    hipLaunchKernelGGL(quant_fp8_kernel, grid, dim3(256), 0, stream, x, q, scale, cols, rows);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_mxfp8(const bf16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* scale,
                               hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(ceil_div(cols, 2048)), static_cast<unsigned>(rows));
-    hipLaunchKernelGGL(quant_mxfp8_kernel, grid, dim3(256), 0, stream, x, q, scale, cols);
+    const dim3 grid(static_cast<unsigned>(ceil_div(cols, 2048)), grid_rows(rows));
+    hipLaunchKernelGGL(quant_mxfp8_kernel, grid, dim3(256), 0, stream, x, q, scale, cols, rows);
     return hipGetLastError();
 }
 
@@ -286,8 +301,8 @@ hipError_t launch_pack_mx_scales(const uint8_t* s, uint32_t* out, int64_t E, int
 
 hipError_t launch_reduce(const bf16_t* o, const int32_t* inv_perm, const float* weights, int64_t M,
                          int k, int H, int use_weights, bf16_t* y, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(ceil_div(H / 8, 256)), static_cast<unsigned>(M));
+    const dim3 grid(static_cast<unsigned>(ceil_div(H / 8, 256)), grid_rows(M));
     hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, o, inv_perm, weights, k, H,
-                       use_weights, y);
+                       use_weights, y, M);
     return hipGetLastError();
 }
