@@ -44,7 +44,8 @@ typedef enum {
                               other than block_m 128 with H, I >= 256, the
                               tiled layout other than bf16 with block_m 16, 128 or 256,
                               more than 2^31 routed rows, one expert's w13 of 2 GiB
-                              or more */
+                              or more, or GEMM grids (row blocks x 128-column tiles)
+                              of 2^31 workgroups or more */
     MOE_E_WORKSPACE = 3,   /* workspace_bytes < moe_workspace_bytes(p) */
     MOE_E_HIP = 4          /* a kernel launch failed (hipGetLastError) */
 } moe_status_t;

@@ -133,7 +133,12 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (int64_t(2) * p->I * p->H * esz >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
     // positions and routed items are int32 on the device
     if (p->M * p->topk >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
-    if (moe_align_capacity(p->M, p->topk, p->E, p->block_m) >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
+    const int64_t cap = moe_align_capacity(p->M, p->topk, p->E, p->block_m);
+    if (cap >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
+    // the GEMM grids (row blocks x column tiles of at least 128 columns, plus one round
+    // of split-K workgroups) are int32 on the device and in the launch
+    const int64_t n_max = 2 * static_cast<int64_t>(p->I) > p->H ? 2 * static_cast<int64_t>(p->I) : p->H;
+    if ((cap / p->block_m) * (n_max / 128 + 1) + 1024 >= (int64_t(1) << 31)) return MOE_E_UNSUPPORTED;
     return MOE_OK;
 }
 

@@ -68,6 +68,8 @@ def P(**kw):
     (dict(weight_layout=moe.MOE_LAYOUT_TILED, block_m=32), moe.MOE_E_UNSUPPORTED),
     (dict(weight_layout=moe.MOE_LAYOUT_TILED, block_m=128, wdtype=moe.MOE_W_FP8_E4M3_BLOCK128),
      moe.MOE_E_UNSUPPORTED),
+    # row blocks x column tiles of the GEMM grids past int32 (2^26 tokens, top-8, block_m 16)
+    (dict(M=1 << 26, topk=8, E=256, H=4096, I=14336), moe.MOE_E_UNSUPPORTED),
 ])
 def test_fused_experts_validation(kw, status):
     p = P(**kw)
@@ -76,6 +78,11 @@ def test_fused_experts_validation(kw, status):
     rc = moe.lib().fused_experts(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy,
                                  dummy, dummy, 1 << 40, None)
     assert rc == status
+
+
+def test_large_problem_below_the_grid_limit_is_accepted():
+    # 2^20 tokens of the same shape: 64 Ki row blocks x 225 column tiles fit
+    assert moe.moe_workspace_bytes(P(M=1 << 20, topk=8, E=256, H=4096, I=14336)) > 0
 
 
 def test_fused_experts_pointer_and_workspace_checks():
