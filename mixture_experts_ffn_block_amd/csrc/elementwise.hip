@@ -16,6 +16,8 @@
 //   rewritten once after loading into the layout the kernel reads).
 //
 // All are HBM-bound; every thread moves 16-byte vectors.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -188,6 +190,7 @@ __global__ __launch_bounds__(256) void permute_scales_kernel(const float* __rest
 
 // ------------------------------------------------------------------ reduce --
 // y[t, n] = bf16( sum_j alpha_j * o[inv_perm[t, j], n] ), fp32, slot order.
+template <int KMAX>
 __global__ __launch_bounds__(256) void reduce_kernel(const bf16_t* __restrict__ o,
                                                      const int32_t* __restrict__ inv_perm,
                                                      const float* __restrict__ weights, int k,
@@ -196,16 +199,29 @@ __global__ __launch_bounds__(256) void reduce_kernel(const bf16_t* __restrict__ 
     const int n0 = (blockIdx.x * 256 + threadIdx.x) * 8;
     if (n0 >= H) return;
     for (int64_t t = blockIdx.y; t < M; t += gridDim.y) {
+        // all the token's positions and weights, then all its output rows, are loaded
+        // before the first use: two memory latencies per token instead of two per slot
+        int pos[KMAX];
+        float a[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            pos[j] = j < k ? inv_perm[t * k + j] : -1;
+            a[j] = (j < k && use_weights) ? weights[t * k + j] : 1.0f;
+        }
+        u32x4_t v[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            v[j] = pos[j] >= 0 ? *reinterpret_cast<const u32x4_t*>(o + static_cast<int64_t>(pos[j]) * H + n0)
+                               : u32x4_t{0, 0, 0, 0};
+        // fp32 sum in slot order; slots of experts held elsewhere (-1) are skipped
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < k; ++j) {
-            const int pos = inv_perm[t * k + j];
-            if (pos < 0) continue;
-            const float a = use_weights ? weights[t * k + j] : 1.0f;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o + static_cast<int64_t>(pos) * H + n0);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (pos[j] < 0) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += a * __uint_as_float(v[i] << 16);
-                acc[2 * i + 1] += a * __uint_as_float(v[i] & 0xffff0000u);
+                acc[2 * i] += a[j] * __uint_as_float(v[j][i] << 16);
+                acc[2 * i + 1] += a[j] * __uint_as_float(v[j][i] & 0xffff0000u);
             }
         }
         u32x4_t out;
@@ -302,7 +318,16 @@ hipError_t launch_pack_mx_scales(const uint8_t* s, uint32_t* out, int64_t E, int
 hipError_t launch_reduce(const bf16_t* o, const int32_t* inv_perm, const float* weights, int64_t M,
                          int k, int H, int use_weights, bf16_t* y, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(ceil_div(H / 8, 256)), grid_rows(M));
-    hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, o, inv_perm, weights, k, H,
-                       use_weights, y, M);
+    // slots per token rounded up to a power of two (k <= 32)
+    auto go = [&](auto kmax) {
+        hipLaunchKernelGGL(reduce_kernel<decltype(kmax)::value>, grid, dim3(256), 0, stream, o, inv_perm,
+                           weights, k, H, use_weights, y, M);
+    };
+    if (k <= 1) go(std::integral_constant<int, 1>{});
+    else if (k <= 2) go(std::integral_constant<int, 2>{});
+    else if (k <= 4) go(std::integral_constant<int, 4>{});
+    else if (k <= 8) go(std::integral_constant<int, 8>{});
+    else if (k <= 16) go(std::integral_constant<int, 16>{});
+    else go(std::integral_constant<int, 32>{});
     return hipGetLastError();
 }
