@@ -72,7 +72,7 @@ def run_ep(p, d, ids, w, layout=moe.MOE_LAYOUT_ROWS):
                                  apply_router_weight_on_input=on, expert_map=d.expert_map)
     w13, w2 = d.w13, d.w2
     if layout == moe.MOE_LAYOUT_TILED:
-        prob = moe.make_problem(p.M, p.H, p.I, len(p.local_experts), p.topk, p.block_m)
+        prob = moe.make_problem(p.M, p.H, p.I, len(p.local_experts), 1, p.block_m)  # top-k does not matter to packing
         w13, w2 = moe.moe_pack_weights(prob, 1, w13), moe.moe_pack_weights(prob, 2, w2)
     return moe.fused_experts(d.x, w13, w2, ids, w, p.block_m, apply_router_weight_on_input=on,
                              expert_map=d.expert_map, weight_layout=layout)

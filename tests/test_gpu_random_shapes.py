@@ -76,7 +76,8 @@ def test_random_problem_matches_oracle(cfg):
     else:
         w13, w2, layout = d.w13, d.w2, moe.MOE_LAYOUT_ROWS
         if tiled:
-            prob = moe.make_problem(p.M, p.H, p.I, len(p.local_experts), p.topk, p.block_m)
+            # (the packing problem names the held experts only; top-k does not matter to it)
+            prob = moe.make_problem(p.M, p.H, p.I, len(p.local_experts), 1, p.block_m)
             w13, w2 = moe.moe_pack_weights(prob, 1, w13), moe.moe_pack_weights(prob, 2, w2)
             layout = moe.MOE_LAYOUT_TILED
         y = moe.fused_experts(d.x, w13, w2, ids, w, p.block_m, apply_router_weight_on_input=on,
