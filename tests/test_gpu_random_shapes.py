@@ -44,7 +44,7 @@ def draw_case(i: int) -> dict:
     return cfg
 
 
-CASES = [draw_case(i) for i in range(80)]
+CASES = [draw_case(i) for i in range(200)]
 
 
 @pytest.fixture(scope="module", autouse=True)
