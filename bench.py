@@ -35,7 +35,7 @@ METRIC = "fused-MoE layer TFLOP/s and tokens/s at 1 MI355X; % of MFMA or HBM roo
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("gemm.hip", "gemm_stream.hip", "common.h", "kernels.h", "api.hip")
+KERNEL_SOURCES = ("gemm.hip", "gemm_stream.hip", "layout.h", "common.h", "kernels.h", "api.hip")
 
 
 def kernel_source_digest() -> str:

@@ -37,45 +37,12 @@
 // and the reduce skips their slots.
 #include "common.h"
 #include "kernels.h"
+#include "layout.h"
 
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / MOE_WAVE;
-constexpr int kMaxE = 256;
-
-// this rank's expert of global id `id`: the id itself without a map; ids outside
-// the routing range and map entries outside [0, E) count as not local (-1)
-__device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ emap, int E_global) {
-    if (emap == nullptr) return id;
-    return static_cast<unsigned>(id) < static_cast<unsigned>(E_global) ? emap[id] : -1;
-}
-
-// In place, by one wavefront: seg_start[1 .. kMaxE] holds the padded size of each
-// expert and becomes the inclusive prefix sum (seg_start[0] stays 0). Lane l sums
-// experts 4l .. 4l+3; a shuffle scan over the lanes gives each its exclusive prefix.
-__device__ __forceinline__ void scan_segments(int32_t* seg_start, int lane) {
-    static_assert(kMaxE == 4 * MOE_WAVE, "four experts per lane");
-    int v[4], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[i] = seg_start[4 * lane + i + 1];
-        sum += v[i];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-        const int t = __shfl_up(incl, o, MOE_WAVE);
-        if (lane >= o) incl += t;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        run += v[i];
-        seg_start[4 * lane + i + 1] = run;
-    }
-}
-
 __global__ __launch_bounds__(kThreads) void align_kernel(
     const int32_t* __restrict__ ids, int64_t R, int E, int B, int64_t cap,
     const int32_t* __restrict__ emap, int E_global,
@@ -111,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     if (tid == 0) seg_start[0] = 0;
     __syncthreads();
     // one wavefront scans the padded sizes: lane l sums experts 4l .. 4l+3, a
-    // shuffle scan over the lanes gives each lane its exclusive prefix
+    // DPP scan over the lanes gives each lane its exclusive prefix
     if (wave == 0) scan_segments(seg_start, lane);
     __syncthreads();
     // seg_start[e] is now the inclusive sum over experts < e of padded sizes
@@ -131,14 +98,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     const int64_t nblocks = cap / B;
     for (int64_t b = tid; b < nblocks; b += kThreads) {
         int e = -1;
-        if (b * B < total) {
-            int lo = 0, hi = E - 1;  // last e with seg_start[e] <= b*B
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (seg_start[mid] <= b * B) lo = mid; else hi = mid - 1;
-            }
-            e = lo;
-        }
+        if (b * B < total) e = segment_of(seg_start, E, b * B);
         expert_ids[b] = e;
         const int64_t s = e < 0 ? b * B : seg_start[e] + count[e];
         for (int64_t pos = b * B > s ? b * B : s; pos < (b + 1) * B; ++pos)
@@ -260,14 +220,7 @@ __global__ __launch_bounds__(kMultiThreads) void align_place_kernel(
     for (int64_t pos = static_cast<int64_t>(g) * kMultiThreads + tid; pos < cap;
          pos += static_cast<int64_t>(G) * kMultiThreads) {
         int e = -1;
-        if (pos < total) {
-            int lo = 0, hi = E - 1;  // last e with seg_start[e] <= pos
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (seg_start[mid] <= pos) lo = mid; else hi = mid - 1;
-            }
-            e = lo;
-        }
+        if (pos < total) e = segment_of(seg_start, E, pos);
         if (pos % B == 0) expert_ids[pos / B] = e;
         if (e < 0 || pos >= seg_start[e] + count[e]) sorted[pos] = static_cast<int32_t>(R);
     }

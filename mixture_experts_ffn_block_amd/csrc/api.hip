@@ -203,10 +203,23 @@ bool act_fused(const moe_problem_t& p) {
     return gemm_act_supported(p.block_m, q8(p), p.H);
 }
 
+// Where GEMM1 builds the routing layout itself instead of reading it: the routed
+// ids (with the expert map, if any) and the layout buffers it fills.
+struct SelfAlign {
+    const int32_t* ids;
+    const int32_t* emap;
+    int E_global;
+    int32_t* sorted;
+    int32_t* expert_ids;
+    int32_t* npp;
+    int32_t* inv_perm;
+};
+
 hipError_t gemm_act_stage(const moe_problem_t& p, const Rows& rows, const void* a,
                           const float* a_scale, const void* w13, const float* w13_scale,
                           const int32_t* sorted, const int32_t* expert_ids, const int32_t* npp,
-                          const float* weights, void* z, float* z_scale, hipStream_t s) {
+                          const float* weights, void* z, float* z_scale, hipStream_t s,
+                          const SelfAlign* self = nullptr) {
     const bool fp8 = q8(p);
     const int esz = fp8 ? 1 : 2;
     const int64_t cap = rows.cap;
@@ -232,6 +245,16 @@ hipError_t gemm_act_stage(const moe_problem_t& p, const Rows& rows, const void* 
     g.act = 1;
     g.act_weights = weights;
     g.act_on_input = p.apply_router_weight_on_input ? 1 : 0;
+    if (self) {
+        g.route_ids = self->ids;
+        g.route_emap = self->emap;
+        g.route_E_global = self->E_global;
+        g.route_E = p.E;
+        g.out_sorted = self->sorted;
+        g.out_expert_ids = self->expert_ids;
+        g.out_npp = self->npp;
+        g.out_inv_perm = self->inv_perm;
+    }
     if (fp8) {
         g.a_scale = a_scale;
         g.a_scale_ld = cap;
@@ -428,9 +451,14 @@ moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* 
         a1 = ws + L.xq;
         a1_scale = reinterpret_cast<const float*>(ws + L.xst);
     }
-    err = launch_align(topk_ids, M * p->topk, p->E, p->block_m, L.cap, emap, p->num_global_experts,
-                       sorted, expert_ids, npp, inv_perm, s);
-    if (err != hipSuccess) return MOE_E_HIP;
+    // decode-sized bf16 problems: GEMM1 builds the layout itself (one launch fewer)
+    const bool self_align = p->block_m == 16 && !fp8 && act_fused(*p) && rows.R <= kSelfAlignMaxR;
+    const SelfAlign self{topk_ids, emap, p->num_global_experts, sorted, expert_ids, npp, inv_perm};
+    if (!self_align) {
+        err = launch_align(topk_ids, M * p->topk, p->E, p->block_m, L.cap, emap, p->num_global_experts,
+                           sorted, expert_ids, npp, inv_perm, s);
+        if (err != hipSuccess) return MOE_E_HIP;
+    }
     if (fp8) {
         err = permute_stage(*p, rows, reinterpret_cast<const float*>(ws + L.xs), sorted, npp,
                             reinterpret_cast<float*>(ws + L.xst), s);
@@ -439,7 +467,7 @@ moe_status_t run_fused(const moe_problem_t* p, const int32_t* emap, const void* 
     float* zs = fp8 ? reinterpret_cast<float*>(ws + L.zs) : nullptr;
     if (act_fused(*p)) {
         err = gemm_act_stage(*p, rows, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp,
-                             topk_weights, z, zs, s);
+                             topk_weights, z, zs, s, self_align ? &self : nullptr);
         if (err != hipSuccess) return MOE_E_HIP;
     } else {
         err = gemm_stage(*p, rows, 1, a1, a1_scale, w13, w13_scale, sorted, expert_ids, npp, ho, nullptr, s);

@@ -38,6 +38,7 @@
 // same 4 outputs and writes z directly; h never reaches HBM.
 #include "common.h"
 #include "kernels.h"
+#include "layout.h"
 
 namespace {
 
@@ -45,34 +46,141 @@ namespace {
 template <bool PACKED>
 constexpr int kWavesPerWG = PACKED ? 8 : 4;
 
+// Routing layout of row block mb (16 rows), rebuilt in LDS from the routed ids by
+// the NT threads of a workgroup: the layout the align kernel writes ("fused_moe.py
+// analysis", moe_align_block_size; "DeepGEMM FusedMoE on Blackwell", 2.6.2), with
+// expert segments padded to 16 rows in expert order and items ascending inside a
+// segment. Returns the block's expert (-1 past the padded total), sets npp and
+// leaves the block's items in rows[0..15] (R for padding). The workgroup of column
+// tile 0 (writer) stores the block's part of the layout for the later stages, and
+// the one of block 0 also npp and inv_perm -1 for items no local expert takes.
+// The ids are read once (R <= kSelfAlignMaxR); the rest is an LDS histogram, a
+// one-wave DPP scan that also finds the block's expert, and a ballot rank over
+// that expert's items: five workgroup barriers ahead of the weight stream.
+template <int NT>
+__device__ int self_layout(const GemmArgs& p, int mb, bool writer, int32_t* rows, int& npp) {
+    static_assert(NT % MOE_WAVE == 0 && kSelfAlignMaxR % NT == 0, "whole waves, whole passes");
+    constexpr int kPasses = kSelfAlignMaxR / NT;
+    __shared__ int32_t count[kMaxE];
+    __shared__ int32_t wave_hits[NT / MOE_WAVE];
+    __shared__ int32_t blk[3];  // the block's expert, its first rank in that expert, npp
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int R = p.R, E = p.route_E;
+    const int m0 = mb * 16;
+
+    int el[kPasses];  // local expert of item tid + i * NT (-1: none)
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+        const int r = tid + i * NT;
+        el[i] = r < R ? local_expert(p.route_ids[r], p.route_emap, p.route_E_global) : -1;
+        if (static_cast<unsigned>(el[i]) >= static_cast<unsigned>(E)) el[i] = -1;
+    }
+    for (int i = tid; i < kMaxE; i += NT) count[i] = 0;
+    if (tid < 16) rows[tid] = R;
+    if (tid == 0) blk[0] = -1;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i)
+        if (el[i] >= 0) atomicAdd(&count[el[i]], 1);
+    __syncthreads();
+    if (wave == 0) {
+        // padded sizes -> segment starts; the lane holding the segment of row m0
+        // (a non-empty one) records the block's expert
+        int v[4], size[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ex = 4 * lane + i;
+            size[i] = ex < E ? (count[ex] + 15) / 16 * 16 : 0;
+            v[i] = size[i];
+        }
+        const int total = scan_padded(v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (v[i] <= m0 && m0 < v[i] + size[i]) {
+                blk[0] = 4 * lane + i;
+                blk[1] = m0 - v[i];
+            }
+        if (lane == 0) blk[2] = total;
+    }
+    __syncthreads();
+    const int e = blk[0];
+    npp = blk[2];
+    if (e >= 0) {
+        // the block holds ranks j0 .. j0 + 15 of expert e's items (in item order)
+        const int j0 = blk[1];
+        int base = 0;  // items of expert e in earlier passes (the same in every thread)
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+            if (i * NT >= R || base >= j0 + 16) break;
+            const bool hit = el[i] == e;
+            const uint64_t m = ballot64(hit);
+            if (lane == 0) wave_hits[wave] = __popcll(m);
+            __syncthreads();
+            int before = base;
+            for (int w = 0; w < NT / MOE_WAVE; ++w) {
+                const int c = wave_hits[w];
+                if (w < wave) before += c;
+                base += c;
+            }
+            const int j = before + __popcll(m & ((1ull << lane) - 1ull)) - j0;
+            if (hit && j >= 0 && j < 16) rows[j] = tid + i * NT;
+            __syncthreads();  // rows complete; wave_hits free for the next pass
+        }
+    }
+    if (writer) {
+        if (tid < 16) {
+            const int r = rows[tid];
+            p.out_sorted[m0 + tid] = r;
+            if (r < R) p.out_inv_perm[r] = m0 + tid;
+        }
+        if (tid == 0) p.out_expert_ids[mb] = e;
+        if (mb == 0) {
+            if (tid == 0) *p.out_npp = npp;
+#pragma unroll
+            for (int i = 0; i < kPasses; ++i)
+                if (tid + i * NT < R && el[i] < 0) p.out_inv_perm[tid + i * NT] = -1;
+        }
+    }
+    return e;
+}
+
 // TILES 16-row weight tiles per wave; per K chunk every row contributes S pieces of
 // 64 contiguous bytes (32 S bf16), and D chunks share the register ring (the host
 // picks D dividing K / (32 S)). ACT (GEMM1 with SiLU-and-mul, TILES = 2): tile 0
 // holds the 16 gate rows and tile 1 the 16 up rows of the wave's 16 output columns.
-template <bool GATHER, bool ACT, int TILES, int S, int D, bool PACKED>
+// SELF (with ACT): the workgroup rebuilds its block's routing layout (self_layout)
+// instead of reading it.
+template <bool GATHER, bool ACT, int TILES, int S, int D, bool PACKED, bool SELF>
 __global__ __launch_bounds__(kWavesPerWG<PACKED> * 64) void stream_gemm_bf16_kernel(GemmArgs p) {
     static_assert(!ACT || (GATHER && TILES == 2), "SiLU epilogue: GEMM1, one gate and one up tile");
+    static_assert(!SELF || ACT, "self-aligned: GEMM1 with the SiLU epilogue");
     constexpr int kColsPerWave = ACT ? 16 : 16 * TILES;  // output columns
     constexpr int kColsPerWG = kWavesPerWG<PACKED> * kColsPerWave;
     const int n_wg = (p.N + kColsPerWG - 1) / kColsPerWG;
     const int mb = blockIdx.x / n_wg, nb = blockIdx.x % n_wg;
-    const int npp = *p.npp;
     const int64_t m0 = static_cast<int64_t>(mb) * 16;
-    if (m0 >= npp) return;
-    const int e = p.expert_ids[mb];
-    if (e < 0) return;
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row16 = lane & 15, kq = lane >> 4;
+
+    int e, npp, r_item = 0;
+    if constexpr (SELF) {
+        __shared__ int32_t rows[16];
+        e = self_layout<kWavesPerWG<PACKED> * 64>(p, mb, nb == 0, rows, npp);
+        if (m0 >= npp || e < 0) return;
+        r_item = rows[row16];
+    } else {
+        npp = *p.npp;
+        if (m0 >= npp) return;
+        e = p.expert_ids[mb];
+        if (e < 0) return;
+        if constexpr (GATHER) r_item = p.sorted[m0 + row16];
+    }
+
     const int nw0 = nb * kColsPerWG + wave * kColsPerWave;
     if (nw0 >= p.N) return;
 
     int64_t src_row = m0 + row16;
-    int r_item = 0;
-    if constexpr (GATHER) {
-        r_item = p.sorted[m0 + row16];
-        src_row = r_item < p.R ? r_item / p.topk : 0;  // padding rows read token 0
-    }
+    if constexpr (GATHER) src_row = r_item < p.R ? r_item / p.topk : 0;  // padding rows read token 0
     const uint8_t* a_ptr = reinterpret_cast<const uint8_t*>(p.A) + src_row * p.lda_bytes + kq * 16;
     const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.W) + static_cast<int64_t>(e) * p.w_expert_bytes;
     // PS: bytes between consecutive 32-wide K pieces of one lane's weight row
@@ -178,29 +286,35 @@ __global__ __launch_bounds__(kWavesPerWG<PACKED> * 64) void stream_gemm_bf16_ker
     }
 }
 
-template <bool GATHER, bool ACT, int TILES, int S, int D, bool PACKED>
+template <bool GATHER, bool ACT, int TILES, int S, int D, bool PACKED, bool SELF>
 hipError_t launch_stream_as(const GemmArgs& a, hipStream_t stream) {
     constexpr int kColsPerWG = kWavesPerWG<PACKED> * (ACT ? 16 : 16 * TILES);
     const int n_wg = (a.N + kColsPerWG - 1) / kColsPerWG;
     const dim3 grid(static_cast<unsigned>(a.m_blocks * n_wg));
-    hipLaunchKernelGGL((stream_gemm_bf16_kernel<GATHER, ACT, TILES, S, D, PACKED>), grid,
+    hipLaunchKernelGGL((stream_gemm_bf16_kernel<GATHER, ACT, TILES, S, D, PACKED, SELF>), grid,
                        dim3(kWavesPerWG<PACKED> * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 // ring depth: 4 chunks for the SiLU form, 2 for the 64-row form (deeper rings
 // measured no faster there), or the largest smaller depth dividing the chunks
-template <bool GATHER, bool ACT, int TILES, int S, bool PACKED>
+template <bool GATHER, bool ACT, int TILES, int S, bool PACKED, bool SELF = false>
 hipError_t launch_stream_ring(const GemmArgs& a, hipStream_t stream) {
     const int kc = a.K / (32 * S);
-    if (ACT && kc % 4 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 4, PACKED>(a, stream);
-    if (kc % 2 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 2, PACKED>(a, stream);
-    return launch_stream_as<GATHER, ACT, TILES, S, 1, PACKED>(a, stream);
+    if (ACT && kc % 4 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 4, PACKED, SELF>(a, stream);
+    if (kc % 2 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 2, PACKED, SELF>(a, stream);
+    return launch_stream_as<GATHER, ACT, TILES, S, 1, PACKED, SELF>(a, stream);
 }
 
 template <bool PACKED>
 hipError_t launch_stream_layout(const GemmArgs& a, hipStream_t stream) {
     if (a.act) {
+        if (a.route_ids) {
+            if (a.R > kSelfAlignMaxR || a.route_E > kMaxE || !a.out_sorted || !a.out_expert_ids ||
+                !a.out_npp || !a.out_inv_perm)
+                return hipErrorInvalidValue;
+            return launch_stream_ring<true, true, 2, 4, PACKED, true>(a, stream);
+        }
         if (!a.sorted) return hipErrorInvalidValue;
         return launch_stream_ring<true, true, 2, 4, PACKED>(a, stream);
     }

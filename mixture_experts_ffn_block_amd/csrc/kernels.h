@@ -53,7 +53,23 @@ struct GemmArgs {
     // W tiled: 16-row x 32-column tiles of 1 KB, row-major inside, ordered by row
     // block then column block (bf16; block_m 16, 128 and 256)
     int w_packed;
+    // Self-aligned GEMM1 (block_m 16, SiLU epilogue): route_ids non-null. Each
+    // workgroup rebuilds its row block's expert and rows from the routed ids
+    // (R of them, E local experts, ids mapped through route_emap when non-null,
+    // as the align kernel does), instead of reading sorted / expert_ids / npp,
+    // and the workgroups of the first column tile write that layout to
+    // out_sorted, out_expert_ids, out_npp and out_inv_perm for the later stages
+    const int32_t* route_ids;
+    const int32_t* route_emap;
+    int route_E_global;
+    int route_E;
+    int32_t* out_sorted;
+    int32_t* out_expert_ids;
+    int32_t* out_npp;
+    int32_t* out_inv_perm;
 };
+
+constexpr int kSelfAlignMaxR = 1024;  // routed items up to which GEMM1 may align itself
 
 constexpr int kSplitSlots = 256;  // partial tiles of the split-K workspace
 
