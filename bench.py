@@ -556,18 +556,27 @@ def main():
     touched = int(np.unique(ids_host[held[ids_host]]).size)
     items = int(held[ids_host].sum())
 
-    # timed region: K steps through the product entry points (an event between steps
-    # gives each step's own duration; it does not synchronise)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # timed region: K steps through the product entry points, one event before and one
+    # after, between synchronisations
+    t0_ev, t1_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    t0_ev.record()
+    for _ in range(args.steps):
+        st.fused()
+    t1_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = t0_ev.elapsed_time(t1_ev) / args.steps
+    # each step's own duration: K more steps with an event between steps (not
+    # synchronising; a recorded event costs the stream a few microseconds, which
+    # these durations include and the timed region above does not)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     marks[0].record()
     for i in range(args.steps):
         st.fused()
         marks[i + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = marks[0].elapsed_time(marks[-1]) / args.steps
     per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     # fused_experts alone (the router's output already in place), K calls
     a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
