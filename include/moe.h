@@ -267,7 +267,9 @@ size_t moe_workspace_bytes(const moe_problem_t *p);
  *   y             [M, H] bf16 out; may be the same buffer as x (in place)
  *   workspace     device scratch of at least moe_workspace_bytes(p) bytes,
  *                 256-byte aligned; its contents on entry do not matter
- * M == 0 returns MOE_OK and launches nothing.
+ * M == 0 returns MOE_OK and launches nothing. For bf16 weights with block_m 16 and
+ * at most 1024 routed items (M * topk), GEMM1 builds the aligned layout itself, so
+ * no separate align kernel runs; the layout is moe_align_block_size's either way.
  */
 moe_status_t fused_experts(const moe_problem_t *p, const void *x, const void *w13,
                            const float *w13_scale, const void *w2, const float *w2_scale,
