@@ -7,8 +7,10 @@ column tile write the layout out for GEMM2 and the reduce. Here the layout left
 in the workspace must equal moe_align_block_size's bit for bit (sorted ids with
 their sentinels, expert ids, the padded total, inv_perm), and the layer must give
 the bits of the stage entry points, which align first. Both weight layouts (eight-
-and four-wave workgroups, so two and four passes over the ids), routings that put
-many blocks on one expert, the 1024/1025-item switch and expert maps are covered.
+and four-wave workgroups, so two and four passes over the ids), two hidden sizes,
+routings that put many blocks on one expert, the 1024/1025-item switch and expert
+maps (nothing local; a decode shard where most tokens have no local slot) are
+covered.
 """
 import numpy as np
 import pytest
@@ -71,6 +73,7 @@ CASES = [
     (40, 4, 8, 0, "random", True),        # router weight on the input
     (64, 4, 16, 32, "random", False),     # expert map: half the experts remote
     (100, 4, 4, 16, "random", False),     # expert map: nothing local (see NOTHING_LOCAL)
+    (48, 8, 64, 256, "random", False),    # expert map: a decode shard, most tokens with no local slot
 ]
 NOTHING_LOCAL = (100, 4, 4, 16)
 CASE_ID = lambda c: f"M{c[0]}-k{c[1]}-E{c[2]}-G{c[3]}-{c[4]}" + ("-oninput" if c[5] else "")
@@ -78,10 +81,11 @@ CASE_ID = lambda c: f"M{c[0]}-k{c[1]}-E{c[2]}-G{c[3]}-{c[4]}" + ("-oninput" if c
 
 @pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_TILED, moe.MOE_LAYOUT_ROWS], ids=["tiled", "rows"])
 @pytest.mark.parametrize("case", CASES, ids=CASE_ID)
-def test_self_aligned_layer_matches_the_aligned_stages(case, layout):
+@pytest.mark.parametrize("H", [512, 384], ids=["H512", "H384"])
+def test_self_aligned_layer_matches_the_aligned_stages(case, layout, H):
     M, k, E, G, kind, on_input = case
-    H, I = 256, 384
-    log(f"self-align M={M} k={k} E={E} G={G} {kind} on_input={on_input} layout={layout}")
+    I = 384
+    log(f"self-align M={M} k={k} E={E} G={G} {kind} on_input={on_input} layout={layout} H={H}")
     g = np.random.default_rng(M * 7 + k)
     p = synth.Problem(M=M, H=H, I=I, E=E, topk=k, block_m=B)
     d = synth.make_inputs(p, DEV)
