@@ -1168,21 +1168,26 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
                     f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0, bsc, 0, asc[tm]);
         }
     };
-    // scale of tile row arow + tm*32 + r32 times the wave's weight-block scale
-    // (ACT: column tile tn = 0 holds gate rows, tn = 1 up rows, each its own block)
-    auto fold = [&](int g) {
+    // scale of tile row arow + tm*32 + r32 times the wave's weight-block scale, from
+    // stage g's slot (ACT: column tile tn = 0 holds gate rows, tn = 1 up rows, each
+    // its own block), and the fold of a stage's sums into the accumulators
+    auto stage_scales = [&](int g, float (&sc)[TN][TM]) {
         const float* sx = reinterpret_cast<const float*>(stage_ptr(g) + C::SCALE_OFF / 16);
         const float* swb = reinterpret_cast<const float*>(stage_ptr(g) + C::WSCALE_OFF / 16);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
             const float x = sx[arow + tm * 32 + r32];
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const float sc = FMT == 2 ? x : x * swb[ACT ? tn : brow / 128];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[tn][tm][r] += part[tn][tm][r] * sc;
-            }
+            for (int tn = 0; tn < TN; ++tn) sc[tn][tm] = FMT == 2 ? x : x * swb[ACT ? tn : brow / 128];
         }
+    };
+    auto apply = [&](const float (&sc)[TN][TM]) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[tn][tm][r] += part[tn][tm][r] * sc[tn][tm];
     };
 
     // SiLU-and-mul epilogue of one tile (ACT): `ws` is a free ring slot, `ids`
@@ -1294,6 +1299,16 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
     }
     Frag f0, f1;
     int c_tile = 0, kt = 0;
+    // The waves of the upper half share each SIMD with one of the lower half. They
+    // fold a stage's sums into the accumulators at the start of the next stage
+    // (their scales read in its own stage, before its slot is refilled), so that
+    // one wave's multiply-adds run while the other's MFMAs do instead of both
+    // waves folding at once after their MFMAs. Each output still adds its stages in
+    // order, so the bits do not change; a tile's last stage is folded before its
+    // epilogue.
+    const bool late = wave >= C::NW / 2;
+    float held[TN][TM];
+    bool pending = false;
     for (int g = 0; g < G; ++g) {
         wait_barrier(min(STAGES - 2, G - 1 - g));
         const int gs = g + STAGES - 1;
@@ -1301,6 +1316,9 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
         read(g, 0, f0);
         if (more) issue_a(gs);
         read(g, 1, f1);
+        if constexpr (!MX) {
+            if (late && pending) apply(held);
+        }
         if constexpr (MX) {
             mma_mx(f0, g, 0);
             if (more) issue_rest(gs);
@@ -1309,14 +1327,29 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
             mma_w4(f0, g, 0, true);
             if (more) issue_rest(gs);
             mma_w4(f1, g, 1, false);
-            fold(g);
         } else {
             mma(f0, true);
             if (more) issue_rest(gs);
             mma(f1, false);
-            fold(g);
+        }
+        if constexpr (!MX) {
+            float sc[TN][TM];
+            stage_scales(g, sc);
+            if (late) {
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm) held[tn][tm] = sc[tn][tm];
+                pending = true;
+            } else {
+                apply(sc);
+            }
         }
         if (++kt == KT) {
+            if constexpr (!MX) {
+                if (late) apply(held);
+                pending = false;
+            }
             kt = 0;
             int mb, nb;
             tile_pos(c_tile, mb, nb);
