@@ -49,11 +49,17 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per GEMM1 launch from the committed counter profile of this workload
-    (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel of known size), or None if
-    there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(PROFILES, f"gemm1_{workload}_traffic.txt")
+def profile_block_m(kernel: str) -> int:
+    """Row-block size of a GEMM kernel from its name in a profile: the first template
+    argument of the tile configuration, or 16 for the weight-streaming kernel."""
+    if "Cfg<" in kernel:
+        return int(kernel.split("Cfg<", 1)[1].split(",", 1)[0])
+    return 16 if "stream_gemm" in kernel else -1
+
+
+def read_profile(path: str, block_m: int):
+    """key = value lines of a committed counter profile, or None if there is none, the
+    kernel sources changed since it was taken, or it was taken with another block_m."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -63,24 +69,26 @@ def measured_traffic(workload: str):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256") != kernel_source_digest():
         return None
-    return float(kv["hbm_bytes_per_launch"])
+    if profile_block_m(kv.get("kernel", "")) != block_m:
+        return None
+    return kv
 
 
-def measured_mfma(workload: str):
+def measured_traffic(workload: str, block_m: int):
+    """HBM bytes per GEMM1 launch from the committed counter profile of this workload
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel of known size), or None."""
+    kv = read_profile(os.path.join(PROFILES, f"gemm1_{workload}_traffic.txt"), block_m)
+    return None if kv is None else float(kv["hbm_bytes_per_launch"].split()[0])
+
+
+def measured_mfma(workload: str, block_m: int):
     """MFMA-busy fraction of the SIMDs and the clock during GEMM1 from the committed
-    counter profile of this workload (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE), or
-    None if there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(PROFILES, f"gemm1_{workload}_mfma.txt")
-    if not os.path.exists(path):
+    counter profile of this workload (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE), or None."""
+    kv = read_profile(os.path.join(PROFILES, f"gemm1_{workload}_mfma.txt"), block_m)
+    if kv is None:
         return None
-    kv = {}
-    for line in open(path):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.strip().split()[0]
-    if kv.get("kernel_source_sha256") != kernel_source_digest():
-        return None
-    return {"busy_fraction": float(kv["mfma_busy_fraction"]), "clock_ghz": float(kv["clock_ghz"])}
+    return {"busy_fraction": float(kv["mfma_busy_fraction"].split()[0]),
+            "clock_ghz": float(kv["clock_ghz"].split()[0])}
 
 
 def parse():
@@ -635,11 +643,11 @@ def main():
         roof = {"bound": "hbm", "achieved": round(alg_stage["bytes_g1"] / g1_s / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.workload)
+    roof["traffic"] = measured_traffic(args.workload, p.block_m)
     if roof["bound"] == "mfma":
         # counters: the share of SIMD cycles the matrix cores were busy, and the clock
         # (the chip is power-limited, so the spec peak at 2.4 GHz is not reached)
-        roof["mfma_counters"] = measured_mfma(args.workload)
+        roof["mfma_counters"] = measured_mfma(args.workload, p.block_m)
     roof["kernel"] = ("gemm1 + SiLU-and-mul epilogue (grouped expert GEMM, gathered token rows x w13, writes z)"
                       if st.act_fused else "gemm1 (grouped expert GEMM, gathered token rows x w13)")
     roof["avg_ms"] = round(stage_ms["gemm1"], 4)

@@ -59,8 +59,9 @@ import torch
 # shapes; block_m is the row-block size shared by the align step and the GEMMs.
 WORKLOADS = {
     "tiny": dict(M=64, H=256, I=512, E=8, topk=2, wdtype="bf16", block_m=16, bias_std=0.0),
+    # block_m 128: 3 % padded rows against 12 % with 256-row blocks (GEMM1 2 % faster)
     "mixtral_prefill_m4096": dict(M=4096, H=4096, I=14336, E=8, topk=2, wdtype="bf16",
-                                  block_m=256, bias_std=0.0),
+                                  block_m=128, bias_std=0.0),
     "dsv3_skewed_prefill_m8192": dict(M=8192, H=7168, I=2048, E=256, topk=8, wdtype="bf16",
                                       block_m=128, bias_std=1.5),
     "decode_m32": dict(M=32, H=2048, I=768, E=128, topk=8, wdtype="bf16", block_m=16,

@@ -72,25 +72,38 @@ def test_stage_roofline_classification():
     assert r["gemm"]["bound"] == "mfma" and abs(r["gemm"]["frac"] - 0.5) < 1e-9
 
 
+K128 = "kernel = void expert_gemm_dma_kernel<dma::Cfg<128, 512, 1, 4, 64, 8>, true, true>(GemmArgs)\n"
+
+
 def test_traffic_needs_a_profile_of_the_current_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    assert bench.measured_traffic("w") is None                      # no profile
+    assert bench.measured_traffic("w", 128) is None                 # no profile
     f = tmp_path / "gemm1_w_traffic.txt"
-    f.write_text("# header\nhbm_bytes_per_launch = 1234\nkernel_source_sha256 = 0\n")
-    assert bench.measured_traffic("w") is None                      # other sources
-    f.write_text(f"hbm_bytes_per_launch = 1234\nkernel_source_sha256 = {bench.kernel_source_digest()}\n")
-    assert bench.measured_traffic("w") == 1234.0
+    f.write_text("# header\n" + K128 + "hbm_bytes_per_launch = 1234\nkernel_source_sha256 = 0\n")
+    assert bench.measured_traffic("w", 128) is None                 # other sources
+    f.write_text(K128 + f"hbm_bytes_per_launch = 1234\nkernel_source_sha256 = {bench.kernel_source_digest()}\n")
+    assert bench.measured_traffic("w", 128) == 1234.0
+    assert bench.measured_traffic("w", 256) is None                 # taken with another block_m
 
 
 def test_mfma_counters_need_a_profile_of_the_current_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    assert bench.measured_mfma("w") is None
+    assert bench.measured_mfma("w", 128) is None
     f = tmp_path / "gemm1_w_mfma.txt"
-    body = "mfma_busy_fraction = 0.5   (note)\nclock_ghz = 1.8   (note)\n"
+    body = K128 + "mfma_busy_fraction = 0.5   (note)\nclock_ghz = 1.8   (note)\n"
     f.write_text(body + "kernel_source_sha256 = 0\n")
-    assert bench.measured_mfma("w") is None
+    assert bench.measured_mfma("w", 128) is None
     f.write_text(body + f"kernel_source_sha256 = {bench.kernel_source_digest()}\n")
-    assert bench.measured_mfma("w") == {"busy_fraction": 0.5, "clock_ghz": 1.8}
+    assert bench.measured_mfma("w", 128) == {"busy_fraction": 0.5, "clock_ghz": 1.8}
+    assert bench.measured_mfma("w", 256) is None
+
+
+def test_profile_block_m_from_the_kernel_name():
+    assert bench.profile_block_m(K128.split("=", 1)[1]) == 128
+    assert bench.profile_block_m("expert_gemm_dma_kernel<dma::Cfg<256, 256, 2, 5, 64, 8>, true, true>") == 256
+    assert bench.profile_block_m("expert_gemm_fp8_kernel<f8::Cfg<128, 256, 2, 4, 3, false>, true, true, 0>") == 128
+    assert bench.profile_block_m("stream_gemm_bf16_kernel<true, true, 2, 4, 4, true, true>") == 16
+    assert bench.profile_block_m("something else") == -1
 
 
 def test_committed_profiles_name_the_sources_they_were_taken_on():

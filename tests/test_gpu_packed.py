@@ -127,12 +127,15 @@ def test_stages_tiled_match_rows(cfg):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["decode_m32", "mixtral_prefill_m4096", "dsv3_skewed_prefill_m8192"])
-def test_full_size_tiled_matches_rows(name):
-    # the launch configuration bench.py times; row-major results are checked
-    # against the oracle on sampled tokens by the parity tests
-    p = synth.Problem.named(name)
-    log(f"full-size tiled {name}")
+@pytest.mark.parametrize("name,block_m", [("decode_m32", None), ("mixtral_prefill_m4096", None),
+                                          ("mixtral_prefill_m4096", 256),
+                                          ("dsv3_skewed_prefill_m8192", None)])
+def test_full_size_tiled_matches_rows(name, block_m):
+    # the launch configuration bench.py times (and the Mixtral shape in 256-row
+    # blocks); row-major results are checked against the oracle on sampled tokens
+    # by the parity tests
+    p = synth.Problem.named(name, **({} if block_m is None else {"block_m": block_m}))
+    log(f"full-size tiled {name} block_m {p.block_m}")
     d = synth.make_inputs(p, DEV)
     ids, w = moe.moe_topk(d.logits, p.topk)
     y_rows = moe.fused_experts(d.x, d.w13, d.w2, ids, w, p.block_m)

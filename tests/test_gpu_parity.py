@@ -522,9 +522,9 @@ def test_token_permutation_equivariance():
 
 # --------------------------------------------------- full-size, sampled ---
 
-def sampled_check(name):
-    p = synth.Problem.named(name)
-    log(f"full-size {name}: generating inputs on the device")
+def sampled_check(name, **overrides):
+    p = synth.Problem.named(name, **overrides)
+    log(f"full-size {name} {overrides}: generating inputs on the device")
     d = synth.make_inputs(p, DEV)
     ids, w = route_gpu(p, d.logits, d.score_bias)
     y = run_layer(p, d, ids, w)
@@ -556,6 +556,11 @@ def sampled_check(name):
                                   "mixtral_prefill_m32768_chunk16k"])
 def test_layer_full_size_sampled(name):
     sampled_check(name)
+
+
+def test_layer_full_size_sampled_mixtral_256_row_blocks():
+    # the Mixtral shape in 256-row blocks (256 x 256 tiles, split-K tail of GEMM2)
+    sampled_check("mixtral_prefill_m4096", block_m=256)
 
 
 # ------------------------------------------------------------- chunking ---
