@@ -31,6 +31,7 @@ int gemm_fmt(const moe_problem_t& p) { return is_mx(p) ? 1 : is_w4(p) ? 2 : 0; }
 constexpr int kMaxE = 256;
 constexpr int kMaxTopk = 32;
 constexpr int kGroupM = 32;  // blocks per tile-scheduling window (groups never span two experts)
+static_assert(kGroupM <= 64, "a window's expert ids fit one wavefront");
 
 int64_t up(int64_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 

@@ -136,16 +136,19 @@ __device__ __forceinline__ void store_block(const f32x16_t (&acc)[TN][TM], uint8
 struct TilePos {
     int mb, nb;
 };
+// Called by whole wavefronts (wave-uniform arguments): the window's expert ids
+// arrive in one vector load, one per lane (group_m <= 64), and a ballot marks the
+// blocks of the tile's expert; the group is the run of marked blocks around b0.
 __device__ __forceinline__ void tile_in_group(const GemmArgs& p, int tile, int n_tiles, int m_real,
                                               TilePos& t) {
-    using cint = __attribute__((address_space(4))) const int32_t;  // scalar loads
-    const cint* eids = (const cint*)(p.expert_ids);
     const int b0 = tile / n_tiles;
     const int w0 = b0 / p.group_m * p.group_m, w1 = min(w0 + p.group_m, m_real);
-    const int e0 = eids[b0];
-    int gs = b0, ge = b0 + 1;
-    while (gs > w0 && eids[gs - 1] == e0) --gs;
-    while (ge < w1 && eids[ge] == e0) ++ge;
+    const int lane = threadIdx.x & 63, i0 = b0 - w0;
+    const int eid = w0 + lane < w1 ? p.expert_ids[w0 + lane] : -2;  // real blocks hold ids >= 0
+    const uint64_t same = ballot64(eid == __shfl(eid, i0, 64));     // bit i0 is set
+    const uint64_t up = ~same >> i0, below = ~same & ((1ull << i0) - 1ull);
+    const int ge = up != 0 ? b0 + __builtin_ctzll(up) : w0 + 64;
+    const int gs = below != 0 ? w0 + 64 - __builtin_clzll(below) : w0;
     const int local = tile - gs * n_tiles, rows = ge - gs;
     t.mb = gs + local % rows;
     t.nb = local / rows;
@@ -621,12 +624,24 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
     // their accumulators stay 0 (the SiLU epilogue writes 0 to padding rows
     // anyway), and their LDS reads and MFMAs are left out. The copies and the
     // barriers are the same for every wave.
+    // ACT: the tile's sorted ids and on-input weights, loaded here so that their
+    // latency passes under the K loop instead of opening the epilogue
+    int rid[ACT ? TM : 1];
+    float ralpha[ACT ? TM : 1];
+    if constexpr (ACT) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) rid[i] = p.sorted[m0 + arow + i * 32 + r32];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) ralpha[i] = (rid[i] < p.R && p.act_on_input) ? p.act_weights[rid[i]] : 1.0f;
+    }
     int live = TM;
     if (p.live_ids != nullptr) {
         live = 0;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-            if (ballot64(p.live_ids[m0 + arow + i * 32 + r32] < p.R) != 0) live = i + 1;
+        for (int i = 0; i < TM; ++i) {
+            const int r = ACT ? rid[ACT ? i : 0] : p.live_ids[m0 + arow + i * 32 + r32];
+            if (ballot64(r < p.R) != 0) live = i + 1;
+        }
     }
     struct Frag {
         bf16x8_t a[TM], b[TN];
@@ -794,9 +809,8 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_dma_kernel(GemmArgs p)
         static_assert(TN % 2 == 0 && (BN / C::WN) % 64 == 0, "gate/up column tile pairs");
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-            const int r = p.sorted[m0 + arow + tm * 32 + r32];
-            const bool real = r < p.R;
-            const float alpha = (real && p.act_on_input) ? p.act_weights[r] : 1.0f;
+            const bool real = rid[tm] < p.R;
+            const float alpha = ralpha[tm];
 #pragma unroll
             for (int j = 0; j < TN / 2; ++j)
 #pragma unroll
