@@ -55,7 +55,13 @@ __global__ __launch_bounds__(256) void silu_mul_bf16_kernel(
 // ------------------------------------------------------ fp8 group quantiser --
 // Quantises 8 fp32 values per lane; the 16 lanes of a quarter-wave form one
 // 128-value group. Returns 8 e4m3 codes packed into 2 words and writes the
-// group scale from the group's first lane.
+// group scale from the group's first lane. EXACT: code = RNE(v / s) with the
+// correctly rounded quotient (the activation quantiser, whose codes match the
+// reference bit for bit); otherwise v times the rounded 1 / s (one division per
+// group instead of per value; groups with s below the smallest normal float keep
+// the quotient), the form the GEMM1 epilogue uses for z, so that the separate
+// pass and the fused epilogue agree bit for bit.
+template <bool EXACT>
 __device__ __forceinline__ u32x2_t quant_group8(const float (&v)[8], float* scale_out, bool writer) {
     float amax = 0.0f;
 #pragma unroll
@@ -65,8 +71,14 @@ __device__ __forceinline__ u32x2_t quant_group8(const float (&v)[8], float* scal
     const float s = amax / 448.0f;
     if (writer) *scale_out = s;
     float q[8];
+    if (EXACT || !(s >= 0x1p-126f)) {  // also groups so small that 1 / s would overflow
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = amax == 0.0f ? 0.0f : fminf(fmaxf(v[j] / s, -448.0f), 448.0f);
+        for (int j = 0; j < 8; ++j) q[j] = amax == 0.0f ? 0.0f : fminf(fmaxf(v[j] / s, -448.0f), 448.0f);
+    } else {
+        const float inv = 1.0f / s;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[j] = fminf(fmaxf(v[j] * inv, -448.0f), 448.0f);
+    }
     return u32x2_t{cvt_e4m3x4(q[0], q[1], q[2], q[3]), cvt_e4m3x4(q[4], q[5], q[6], q[7])};
 }
 
@@ -100,7 +112,7 @@ __global__ __launch_bounds__(256) void silu_mul_fp8_kernel(
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = 0.0f;
         }
-        const u32x2_t q = quant_group8(v, zs + (i0 / 128) * cap + pos, (lane & 15) == 0);
+        const u32x2_t q = quant_group8<false>(v, zs + (i0 / 128) * cap + pos, (lane & 15) == 0);
         *reinterpret_cast<u32x2_t*>(zq + pos * I + i0) = q;
     }
 }
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict
             v[2 * j] = __uint_as_float(xv[j] << 16);
             v[2 * j + 1] = __uint_as_float(xv[j] & 0xffff0000u);
         }
-        const u32x2_t qq = quant_group8(v, scale + row * (cols / 128) + c0 / 128, (lane & 15) == 0);
+        const u32x2_t qq = quant_group8<true>(v, scale + row * (cols / 128) + c0 / 128, (lane & 15) == 0);
         *reinterpret_cast<u32x2_t*>(q + row * cols + c0) = qq;
     }
 }

@@ -1273,15 +1273,22 @@ __global__ __launch_bounds__(C::NW * 64) void expert_gemm_fp8_kernel(GemmArgs p)
                                       fmaxf(amax_part[2 * BM + rl], amax_part[3 * BM + rl]));
                 const float s = m / 448.0f;
                 if (wn == 0 && half == 0) p.z_scale[nb * p.z_scale_ld + m0 + rl] = s;
+                // codes: v times the rounded 1 / s, or the quotient where s is below the
+                // smallest normal float (as the separate activation pass does)
+                float c16[16];
+                if (!(s >= 0x1p-126f)) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float c4[4];
+                    for (int j = 0; j < 16; ++j)
+                        c16[j] = m == 0.0f ? 0.0f : fminf(fmaxf(v[tm][j] / s, -448.0f), 448.0f);
+                } else {
+                    const float inv = 1.0f / s;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        c4[j] = m == 0.0f ? 0.0f : fminf(fmaxf(v[tm][4 * q + j] / s, -448.0f), 448.0f);
-                    *reinterpret_cast<uint32_t*>(ws + rl * ZP + wn * 32 + 8 * q + 4 * half) =
-                        cvt_e4m3x4(c4[0], c4[1], c4[2], c4[3]);
+                    for (int j = 0; j < 16; ++j) c16[j] = fminf(fmaxf(v[tm][j] * inv, -448.0f), 448.0f);
                 }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint32_t*>(ws + rl * ZP + wn * 32 + 8 * q + 4 * half) =
+                        cvt_e4m3x4(c16[4 * q], c16[4 * q + 1], c16[4 * q + 2], c16[4 * q + 3]);
             }
             lds_barrier();
             // 128 rows x 128 bytes: 8 lanes per row, 8 rows per wave per pass
