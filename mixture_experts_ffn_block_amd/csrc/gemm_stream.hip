@@ -301,7 +301,9 @@ hipError_t launch_stream_as(const GemmArgs& a, hipStream_t stream) {
 template <bool GATHER, bool ACT, int TILES, int S, bool PACKED, bool SELF = false>
 hipError_t launch_stream_ring(const GemmArgs& a, hipStream_t stream) {
     const int kc = a.K / (32 * S);
-    if (ACT && kc % 4 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 4, PACKED, SELF>(a, stream);
+    if constexpr (ACT) {  // (the 4-deep ring is instantiated for the SiLU form only)
+        if (kc % 4 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 4, PACKED, SELF>(a, stream);
+    }
     if (kc % 2 == 0) return launch_stream_as<GATHER, ACT, TILES, S, 2, PACKED, SELF>(a, stream);
     return launch_stream_as<GATHER, ACT, TILES, S, 1, PACKED, SELF>(a, stream);
 }
