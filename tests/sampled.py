@@ -2,13 +2,15 @@
 
 At full size the oracle cannot compute every token in test time, so the checked
 tokens are chosen from the aligned layout (which the align tests show is the
-GPU's, bit for bit): one real row from every block of block_m rows, so that
-every tile of both GEMMs (every column tile of every block, hence the first and
+GPU's, bit for bit) so that every block of block_m rows holds a checked row,
+hence every tile of both GEMMs (every column tile of every block, the first and
 last tiles of every XCD's range, the split-K tail tiles and the last rounds of
-the persistent kernels) holds a checked row; the row's position inside its
-block cycles through the 32-row groups from block to block. Added to those: the
-first and last tokens, a token of every expert that received exactly one item,
-and random tokens up to `at_least`.
+the persistent kernels). A token holds topk rows in different blocks, so the
+tokens are picked greedily, each covering the most blocks not yet covered (ties
+broken at random, which spreads the checked rows over the 32-row groups of the
+blocks): a fraction of one token per block. Added to those: the first and last
+tokens, a token of every expert that received exactly one item, and random
+tokens up to `at_least`.
 """
 from __future__ import annotations
 
@@ -17,25 +19,33 @@ import numpy as np
 import oracle
 
 
-def block_rows(ids: np.ndarray, E: int, block_m: int, expert_map=None) -> list[int]:
-    """Tokens holding one real row of each block of the layout of `ids` [M, k]."""
+def block_rows(ids: np.ndarray, E: int, block_m: int, expert_map=None, seed: int = 0) -> list[int]:
+    """Tokens that together hold a real row of every block of the layout of `ids` [M, k]."""
     M, k = ids.shape
     sorted_ids, _, npp, _ = oracle.align(ids, E, block_m, expert_map=expert_map)
     R = M * k
-    groups = max(block_m // 32, 1)
+    item = np.asarray(sorted_ids[:npp], np.int64)
+    real = item < R
+    blk = np.nonzero(real)[0] // block_m
+    tok = item[real] // k
+    if blk.size == 0:
+        return []
+    covered = np.zeros(int(blk.max()) + 1, bool)
+    covered[np.setdiff1d(np.arange(covered.size), blk)] = True   # padding-only blocks
+    jitter = np.random.default_rng(seed).random(M) * 0.5       # breaks ties only
     toks = []
-    for b in range(npp // block_m):
-        rows = sorted_ids[b * block_m:(b + 1) * block_m]
-        real = int(np.count_nonzero(rows < R))
-        if real == 0:
-            continue
-        want = (b % groups) * 32 + (7 * b) % min(32, block_m)
-        toks.append(int(rows[min(want, real - 1)]) // k)
+    while not covered.all():
+        open_rows = ~covered[blk]
+        gain = np.bincount(tok[open_rows], minlength=M) + jitter
+        gain[np.bincount(tok[open_rows], minlength=M) == 0] = -1.0
+        t = int(np.argmax(gain))
+        toks.append(t)
+        covered[blk[tok == t]] = True
     return toks
 
 
 def pick_tokens(ids: np.ndarray, E: int, block_m: int, expert_map=None, chunk: int = 0,
-                at_least: int = 128, at_most: int = 720, seed: int = 0) -> list[int]:
+                at_least: int = 192, at_most: int = 720, seed: int = 0) -> list[int]:
     """Sorted token indices to check. chunk > 0: the layer runs on chunks of that many
     tokens, each with its own layout."""
     M = ids.shape[0]
