@@ -403,10 +403,22 @@ def stage_roofline(work: dict, stage_ms: dict, dt: str) -> dict:
 
 
 def cpu_model() -> str:
-    """The host CPU's model name and logical CPU count (from /proc/cpuinfo)."""
+    """The host CPU's model name, its family / model numbers (a virtualised host may
+    report only a generic name) and the logical CPU count, from /proc/cpuinfo."""
     try:
-        names = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")]
-        return f"{names[0]} ({len(names)} logical CPUs)" if names else "unknown"
+        fields: dict = {}
+        names = 0
+        for l in open("/proc/cpuinfo"):
+            key, _, val = l.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "model name":
+                names += 1
+            if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                fields[key] = val
+        if not names:
+            return "unknown"
+        ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+        return f"{fields['model name']} ({ids + '; ' if ids else ''}{names} logical CPUs)"
     except OSError:
         return "unknown"
 

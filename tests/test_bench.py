@@ -116,3 +116,12 @@ def test_committed_profiles_name_the_sources_they_were_taken_on():
     for n in files:
         text = open(os.path.join(ROOT, "profiles", n)).read()
         assert re.search(r"^kernel_source_sha256 = [0-9a-f]{64}$", text, re.M), n
+
+
+def test_cpu_model_names_the_host():
+    # the model name, its family / model numbers where /proc/cpuinfo has them, and
+    # the logical CPU count
+    s = bench.cpu_model()
+    assert s == "unknown" or s.endswith("logical CPUs)")
+    if os.path.exists("/proc/cpuinfo") and "cpu family" in open("/proc/cpuinfo").read():
+        assert "cpu family" in s
